@@ -1,0 +1,173 @@
+/*
+ * i4s.h -- C ABI of libi4s: packed INT4 SparseGEMV over the 2-bit CSR format,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed follows "Efficient LLM-based Advertising via Model
+ * Compression and Parallel Verification" (arXiv 2605.11582):
+ *   - section 3.2, "Sparsification", Eq. (3): N:M pruning by element
+ *     importance; with a constant activation norm and no gradient term the
+ *     importance is |W_ij|, so each aligned group of 4 columns keeps its
+ *     n_keep largest-magnitude weights (2 for 2:4, 1 for 1:4, 4 = dense);
+ *   - section 3.1 and 3.2, "Adaptive Group-Wise Quantization": symmetric INT4
+ *     weight-only quantization with a group size chosen per layer;
+ *   - section 3.3, "Sparse Index Structure": CSR rows whose column index is a
+ *     2-bit position inside the group of 4, eight indices per uint16 word,
+ *     filled from the least significant bits;
+ *   - section 3.3, "Computational Acceleration" and section 1 (the SparseGemv
+ *     kernel): y = W x with INT4 weights widened to fp16 in registers and the
+ *     activations staged in on-chip shared memory (LDS on this GPU).
+ *
+ * FORMAT (version 1).  W is R x K (rows = output features), K % 64 == 0.
+ *   nnz_row = K * n_keep / 4; nnz = R * nnz_row.  Element e of a row lies in
+ *   4-column group t = e / n_keep and column 4*t + code_e; the kept columns of
+ *   a group are listed in ascending order.
+ *   row_ptr : int32[R+1], row_ptr[i] = i * nnz_row (in elements).
+ *   vals    : uint8[nnz/2].  Row i starts at byte row_ptr[i]/2.  Each
+ *             little-endian 32-bit word holds 8 consecutive elements
+ *             e0..e7; nibble slot k (bits 4k..4k+3) holds element
+ *             (0,2,4,6,1,3,5,7)[k].  Nibble u = q + 8, q in [-8, 7].
+ *   codes   : uint16[nnz/8] (absent when n_keep == 4).  Element e's code is
+ *             at bits 2*(e % 8) of word e / 8 of the row (row i starts at
+ *             word row_ptr[i]/8).  For 2:4, bits 4p..4p+3 of a word are
+ *             group p's pair (first | second << 2).
+ *   scales  : fp16 bits [R][K/G], s = round_to_nearest_even_fp16(amax / 7)
+ *             over the kept elements whose column lies in [gG, (g+1)G); an
+ *             all-zero group has s = +0 and q = 0.
+ *   q       : clamp(round_half_even(w / s), -8, 7), computed with a correctly
+ *             rounded division.
+ *   W_hat[i][4t + code_e] = s[i][(4t)/G] * q_e; all other entries are 0.
+ *   Adaptive group size (group_size == 0): each G in {64, 128, 256} is tried
+ *   and the one with the smallest exact sum over kept elements of
+ *   (w - s*q)^2 wins, ties going to the larger G.
+ *
+ * CONVENTIONS.  Every pointer to tensor data is a DEVICE pointer unless
+ * marked "host".  The caller owns all memory: the library never allocates or
+ * frees device memory.  `stream` is a hipStream_t passed as void* (NULL is
+ * the null stream).  All argument checks run before anything is enqueued; a
+ * failed check returns I4S_ERR_INVALID_ARGUMENT (or another status) and
+ * leaves every buffer untouched.  Errors raised by the HIP runtime come back
+ * as I4S_ERR_DEVICE; the message of the last failing call on the calling
+ * thread is available from i4s_last_error().  Faults inside a kernel surface
+ * at the caller's next synchronisation.  No call aborts or throws.
+ */
+#ifndef I4S_H
+#define I4S_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define I4S_FORMAT_VERSION 1
+#define I4S_MAX_BATCH 16
+
+typedef enum i4s_status {
+  I4S_OK = 0,
+  I4S_ERR_INVALID_ARGUMENT = 1,  /* a shape, pattern, pointer or size is invalid      */
+  I4S_ERR_UNSUPPORTED = 2,       /* the current device is not gfx950                  */
+  I4S_ERR_NONFINITE_WEIGHT = 3,  /* W holds an Inf or NaN                             */
+  I4S_ERR_WORKSPACE_TOO_SMALL = 4,
+  I4S_ERR_DEVICE = 5             /* a HIP runtime call failed                         */
+} i4s_status;
+
+/* A packed layer.  Plain data: every buffer is owned by the caller, the
+ * struct can be copied freely and holds no hidden state. */
+typedef struct i4s_packed {
+  int32_t rows;        /* R                                                   */
+  int32_t cols;        /* K, a multiple of 64                                 */
+  int32_t n_keep;      /* 1, 2 or 4 kept per group of 4 (4 = dense INT4)      */
+  int32_t group_size;  /* G in use: 64, 128 or 256                            */
+  int64_t nnz;         /* R * K * n_keep / 4                                  */
+  int32_t *row_ptr;    /* [R+1]                                               */
+  uint8_t *vals;       /* [nnz/2]                                             */
+  uint16_t *codes;     /* [nnz/8]; NULL when n_keep == 4                      */
+  uint16_t *scales;    /* [R*K/G] fp16 bits                                   */
+} i4s_packed;
+
+/* Buffer sizes in bytes. */
+typedef struct i4s_sizes {
+  uint64_t row_ptr;
+  uint64_t vals;
+  uint64_t codes;      /* 0 when n_keep == 4                                  */
+  uint64_t scales;     /* for adaptive G, sized for the smallest candidate (64) */
+  uint64_t workspace;  /* scratch i4s_pack needs                              */
+} i4s_sizes;
+
+/* What i4s_pack decided.  SSE values are exact integers in units of 2^-48,
+ * split into high and low 64-bit halves. */
+typedef struct i4s_pack_report {
+  int32_t group_size;      /* G chosen (or the fixed G)                       */
+  int32_t n_candidates;    /* 3 when chosen adaptively, else 0                */
+  int32_t candidates[3];   /* 64, 128, 256                                    */
+  int32_t reserved;
+  uint64_t sse_hi[3];
+  uint64_t sse_lo[3];
+} i4s_pack_report;
+
+/* Sizes of the packed buffers and of the pack workspace for an R x K weight.
+ * Host-only and pure: touches no device.  group_size 0 means adaptive.
+ * Errors: I4S_ERR_INVALID_ARGUMENT for rows < 1, cols not a positive multiple
+ * of 64 (or of every G in use), n_keep not in {1,2,4}, G not in
+ * {0,64,128,256}, nnz >= 2^31, or out == NULL. */
+i4s_status i4s_pack_sizes(int32_t rows, int32_t cols, int32_t n_keep,
+                          int32_t group_size, i4s_sizes *out /* host */);
+
+/* Prune, quantize and encode a dense fp16 weight (section 3.2 and 3.3 of the
+ * page; see FORMAT above).
+ *   w_fp16     : [rows][cols] fp16 bits, row-major, 16-byte aligned.
+ *   group_size : 64, 128, 256, or 0 to choose per matrix by minimum SSE.
+ *   workspace  : device scratch of at least i4s_pack_sizes().workspace bytes,
+ *                16-byte aligned; its contents on entry do not matter.
+ *   inout      : host struct whose row_ptr, vals, codes (unless n_keep == 4)
+ *                and scales point at caller-owned device buffers of the sizes
+ *                i4s_pack_sizes() reports, each 16-byte aligned.  On success
+ *                rows, cols, n_keep, group_size and nnz are filled in.
+ *   report     : optional host struct receiving the chosen G and the SSEs.
+ * Enqueues its kernels on `stream` and synchronises that stream once to read
+ * back the non-finite flag and, when adaptive, the SSE totals.
+ * Errors: I4S_ERR_INVALID_ARGUMENT (checks as in i4s_pack_sizes, null or
+ * misaligned pointers), I4S_ERR_WORKSPACE_TOO_SMALL,
+ * I4S_ERR_NONFINITE_WEIGHT (the output buffers are then unspecified),
+ * I4S_ERR_UNSUPPORTED (device is not gfx950), I4S_ERR_DEVICE. */
+i4s_status i4s_pack(const uint16_t *w_fp16, int32_t rows, int32_t cols,
+                    int32_t n_keep, int32_t group_size, void *workspace,
+                    uint64_t workspace_bytes, i4s_packed *inout /* host */,
+                    i4s_pack_report *report /* host, may be NULL */,
+                    void *stream);
+
+/* y = W_hat x for `batch` activation vectors (section 3.3 of the page: the
+ * SparseGemv kernel over the 2-bit CSR format).
+ *   w      : host descriptor filled by i4s_pack (or an equivalent layout);
+ *            group_size must be 64, 128 or 256; vals 16-byte, codes 8-byte,
+ *            row_ptr 4-byte and scales 2-byte aligned.  row_ptr is read.
+ *   x_fp16 : [batch][cols] fp16 bits, contiguous, 16-byte aligned.
+ *   batch  : 1 .. I4S_MAX_BATCH.
+ *   y_fp16 : [batch][rows] fp16 bits, contiguous, 2-byte aligned; fully
+ *            overwritten.  Must not overlap x or any packed buffer.
+ * Accumulates in fp32 and rounds y to fp16 (nearest even).  One kernel
+ * launch on `stream`; asynchronous; allocates nothing; never synchronises.
+ * Errors: I4S_ERR_INVALID_ARGUMENT (descriptor inconsistent, null or
+ * misaligned pointers, batch out of range, x/y overlap),
+ * I4S_ERR_UNSUPPORTED, I4S_ERR_DEVICE. */
+i4s_status i4s_run(const i4s_packed *w /* host */, const uint16_t *x_fp16,
+                   int32_t batch, uint16_t *y_fp16, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *i4s_status_string(i4s_status s);
+
+/* Message of the last failing call on the calling thread ("" if none). */
+const char *i4s_last_error(void);
+
+/* Library version: 10000 * major + 100 * minor + patch. */
+int32_t i4s_version(void);
+
+/* FORMAT version this library reads and writes (I4S_FORMAT_VERSION). */
+int32_t i4s_format_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I4S_H */

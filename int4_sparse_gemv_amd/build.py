@@ -1,0 +1,72 @@
+"""Build libi4s.so in-tree with hipcc for gfx950.
+
+``python -m int4_sparse_gemv_amd.build`` (or ``build()``) compiles every HIP
+and C++ source under ``csrc/`` into ``int4_sparse_gemv_amd/libi4s.so``.  It
+always recompiles.  hipcc cross-compiles for gfx950 without a GPU present.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libi4s.so")
+
+SOURCES = ("i4s_api.cpp", "i4s_pack.hip", "i4s_gemv.hip")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    # IEEE-correct fp32 division (the packer's scale and quantizer rely on it)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # keep packed-fp32 VALU forms out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libi4s)")
+
+
+def _run(cmd):
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in proc.stdout.splitlines()
+                    if "is not a recognized feature for this target" not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"command failed ({proc.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libi4s.so; returns its path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="i4s_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+            out = _run(cmd)
+            if verbose and out.strip():
+                print(out)
+            objs.append(obj)
+        tmp_lib = LIB + ".tmp"
+        _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib])
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

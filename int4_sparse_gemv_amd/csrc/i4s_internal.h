@@ -1,0 +1,50 @@
+// Internal declarations shared by the host layer and the kernel launchers of
+// libi4s.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "i4s.h"
+
+namespace i4s {
+
+// Columns covered by one "segment": the unit of work of a pack thread and of
+// a GEMV lane.  Every supported group size (64, 128, 256) is a multiple of it,
+// so a segment never straddles two quantization groups.
+constexpr int kSegCols = 64;
+
+// Pack workspace layout (bytes from the workspace base):
+//   [0, 4)     uint32 non-finite flag
+//   [16, 64)   three 128-bit SSE totals (lo, hi) for G = 64, 128, 256
+//   [64, ...)  per-block 128-bit partials, 3 per analyze block
+constexpr size_t kWsFlagOffset = 0;
+constexpr size_t kWsTotalsOffset = 16;
+constexpr size_t kWsPartialsOffset = 64;
+constexpr int kPackThreads = 256;
+
+inline int64_t pack_threads_total(int32_t rows, int32_t cols) {
+  return (int64_t)rows * (cols / kSegCols);
+}
+inline int64_t pack_blocks(int32_t rows, int32_t cols) {
+  return (pack_threads_total(rows, cols) + kPackThreads - 1) / kPackThreads;
+}
+inline size_t pack_workspace_bytes(int32_t rows, int32_t cols) {
+  return kWsPartialsOffset + (size_t)pack_blocks(rows, cols) * 3 * 16;
+}
+
+// Pack kernels (i4s_pack.hip).  `adaptive` selects whether the analyze pass
+// also accumulates the exact SSE of every candidate group size; it always
+// raises the non-finite flag.
+hipError_t launch_pack_analyze(const uint16_t *w, int32_t rows, int32_t cols,
+                               int32_t n_keep, bool adaptive, void *ws,
+                               hipStream_t stream);
+hipError_t launch_pack_emit(const uint16_t *w, int32_t rows, int32_t cols,
+                            int32_t n_keep, int32_t group_size,
+                            const i4s_packed &out, hipStream_t stream);
+
+// GEMV kernels (i4s_gemv.hip).
+hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch,
+                       uint16_t *y, hipStream_t stream);
+
+}  // namespace i4s

@@ -1,0 +1,164 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+its structs match the header's layout, and host-side validation returns the
+documented status before touching a device.  No compute call runs here."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from int4_sparse_gemv_amd import _binding as B
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "i4s.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from int4_sparse_gemv_amd import build
+        build.build()
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(i4s_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["i4s_pack_sizes", "i4s_pack", "i4s_run", "i4s_status_string", "i4s_last_error",
+         "i4s_version", "i4s_format_version"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (i4s_[a-z_]+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert set(B.SIGNATURES) == set(declared_functions())
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "i4s.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu\n", sizeof(i4s_packed), offsetof(i4s_packed, nnz),
+         offsetof(i4s_packed, row_ptr), offsetof(i4s_packed, codes), offsetof(i4s_packed, scales));
+  printf("%zu %zu\n", sizeof(i4s_sizes), offsetof(i4s_sizes, workspace));
+  printf("%zu %zu %zu\n", sizeof(i4s_pack_report), offsetof(i4s_pack_report, sse_hi),
+         offsetof(i4s_pack_report, sse_lo));
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    P, S, R = B.i4s_packed, B.i4s_sizes, B.i4s_pack_report
+    assert lines[0].split() == [str(v) for v in (ctypes.sizeof(P), P.nnz.offset, P.row_ptr.offset,
+                                                 P.codes.offset, P.scales.offset)]
+    assert lines[1].split() == [str(v) for v in (ctypes.sizeof(S), S.workspace.offset)]
+    assert lines[2].split() == [str(v) for v in (ctypes.sizeof(R), R.sse_hi.offset, R.sse_lo.offset)]
+
+
+def test_version_and_status_strings(lib):
+    assert B.i4s_version() >= 100
+    assert B.i4s_format_version() == B.I4S_FORMAT_VERSION == 1
+    for st in range(6):
+        assert B.i4s_status_string(st)
+    assert B.i4s_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("rows,cols,n_keep,g", [
+    (512, 512, 2, 128), (4096, 4096, 2, 128), (11008, 4096, 2, 0), (4096, 11008, 2, 64),
+    (4096, 4096, 4, 64), (13824, 5120, 2, 128), (3, 192, 1, 64), (1, 64, 4, 64)])
+def test_pack_sizes_match_closed_form(lib, rows, cols, n_keep, g):
+    sz = B.i4s_sizes()
+    assert B.i4s_pack_sizes(rows, cols, n_keep, g, sz) == B.I4S_OK
+    want = oracle.packed_nbytes(rows, cols, n_keep, g or 64)
+    assert (sz.row_ptr, sz.vals, sz.codes, sz.scales) == (want["row_ptr"], want["vals"], want["codes"],
+                                                          want["scales"])
+    assert sz.workspace >= 64
+
+
+@pytest.mark.parametrize("rows,cols,n_keep,g", [
+    (0, 512, 2, 128), (4, 96, 2, 64), (4, 512, 3, 128), (4, 512, 2, 32), (4, 192, 2, 128),
+    (4, 320, 2, 0), (4, 576, 2, 256), (1 << 20, 1 << 12, 4, 64), (-1, 64, 2, 64)])
+def test_pack_sizes_rejects(lib, rows, cols, n_keep, g):
+    sz = B.i4s_sizes()
+    assert B.i4s_pack_sizes(rows, cols, n_keep, g, sz) == B.I4S_ERR_INVALID_ARGUMENT
+    assert B.i4s_last_error()
+
+
+def test_pack_sizes_null_out(lib):
+    assert lib.i4s_pack_sizes(64, 64, 2, 64, None) == B.I4S_ERR_INVALID_ARGUMENT
+
+
+def _desc(rows=64, cols=256, n_keep=2, g=128, base=1 << 20):
+    d = B.i4s_packed()
+    d.rows, d.cols, d.n_keep, d.group_size = rows, cols, n_keep, g
+    d.nnz = rows * cols * n_keep // 4
+    d.row_ptr, d.vals, d.codes, d.scales = base, base + (1 << 16), base + (2 << 16), base + (3 << 16)
+    return d
+
+
+@pytest.mark.parametrize("mutate,batch", [
+    (lambda d: setattr(d, "group_size", 0), 1),
+    (lambda d: setattr(d, "group_size", 96), 1),
+    (lambda d: setattr(d, "nnz", 5), 1),
+    (lambda d: setattr(d, "vals", (1 << 20) + 8), 1),
+    (lambda d: setattr(d, "codes", None), 1),
+    (lambda d: setattr(d, "n_keep", 3), 1),
+    (lambda d: None, 0),
+    (lambda d: None, 17),
+])
+def test_run_validation_fails_before_any_device_call(lib, mutate, batch):
+    d = _desc()
+    mutate(d)
+    x, y = 1 << 30, 1 << 31
+    assert B.i4s_run(d, x, batch, y, None) == B.I4S_ERR_INVALID_ARGUMENT
+    assert B.i4s_last_error()
+
+
+def test_run_rejects_overlap_and_misalignment(lib):
+    d = _desc()
+    assert B.i4s_run(d, 1 << 30, 1, (1 << 30) + 64, None) == B.I4S_ERR_INVALID_ARGUMENT  # x/y overlap
+    assert B.i4s_run(d, (1 << 30) + 2, 1, 1 << 31, None) == B.I4S_ERR_INVALID_ARGUMENT   # x misaligned
+    assert B.i4s_run(d, 1 << 30, 1, (1 << 20) + (1 << 16), None) == B.I4S_ERR_INVALID_ARGUMENT  # y on vals
+    assert lib.i4s_run(None, 1 << 30, 1, 1 << 31, None) == B.I4S_ERR_INVALID_ARGUMENT
+
+
+def test_pack_validation_fails_before_any_device_call(lib):
+    sz = B.i4s_sizes()
+    assert B.i4s_pack_sizes(64, 256, 2, 0, sz) == B.I4S_OK
+    d = _desc()
+    rep = B.i4s_pack_report()
+    w, ws = 1 << 30, 1 << 31
+    # workspace too small
+    assert B.i4s_pack(w, 64, 256, 2, 0, ws, sz.workspace - 1, d, rep, None) == B.I4S_ERR_WORKSPACE_TOO_SMALL
+    # misaligned weight, null workspace, bad shape
+    assert B.i4s_pack(w + 2, 64, 256, 2, 0, ws, sz.workspace, d, rep, None) == B.I4S_ERR_INVALID_ARGUMENT
+    assert B.i4s_pack(w, 64, 256, 2, 0, None, sz.workspace, d, rep, None) == B.I4S_ERR_INVALID_ARGUMENT
+    assert B.i4s_pack(w, 64, 250, 2, 0, ws, sz.workspace, d, rep, None) == B.I4S_ERR_INVALID_ARGUMENT
+    d.codes = None
+    assert B.i4s_pack(w, 64, 256, 2, 0, ws, sz.workspace, d, rep, None) == B.I4S_ERR_INVALID_ARGUMENT
+
+
+def test_binding_without_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError):
+        B._lib_saved = B._lib
+        try:
+            B._lib = None
+            B.load(str(tmp_path / "missing.so"))
+        finally:
+            B._lib = B._lib_saved

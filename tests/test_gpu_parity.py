@@ -1,0 +1,250 @@
+"""GPU parity of libi4s against the CPU oracle (needs an MI355X).
+
+Packed buffers must be bit-identical to the oracle's; GEMV outputs must
+satisfy |y_gpu - y_ref| <= 1e-3 * sum_j |w_hat_ij x_j| + 1e-5 per element,
+where y_ref and the sum come from the oracle in float64.  Every input is
+seeded and synthetic (``workloads``).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_lib():
+    _require_gpu()
+    import int4_sparse_gemv_amd as I
+    I._binding.load()  # raises if the library is not built
+    return I
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_pack(w16, n_keep, g):
+    import int4_sparse_gemv_amd as I
+    w = torch.from_numpy(w16.view(np.int16)).cuda().view(torch.float16)
+    p = I.pack(w, n_keep, g)
+    torch.cuda.synchronize()
+    return p
+
+
+def host_bytes(p):
+    return {
+        "row_ptr": p.row_ptr.cpu().numpy().astype(np.int32),
+        "vals": p.vals.cpu().numpy().astype(np.uint8),
+        "codes": (p.codes.cpu().numpy().view(np.uint16) if p.codes is not None else np.zeros(0, np.uint16)),
+        "scales": p.scales.cpu().numpy().view(np.uint16),
+    }
+
+
+def assert_pack_equal(p, ref, label):
+    got = host_bytes(p)
+    assert p.group_size == ref["group_size"], f"{label}: G {p.group_size} != {ref['group_size']}"
+    for k in ("row_ptr", "vals", "codes", "scales"):
+        a, b = got[k], np.asarray(ref[k])
+        assert a.shape == b.shape, f"{label}: {k} shape {a.shape} != {b.shape}"
+        bad = np.flatnonzero(a != b)
+        assert bad.size == 0, f"{label}: {k} differs at {bad.size} positions, first {bad[:5]}"
+    if ref["sse"]:
+        assert p.sse == ref["sse"], f"{label}: SSE {p.sse} != {ref['sse']}"
+
+
+def gpu_run(p, x16):
+    import int4_sparse_gemv_amd as I
+    x = torch.from_numpy(np.ascontiguousarray(x16).view(np.int16)).cuda().view(torch.float16)
+    y = I.run(p, x)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def assert_gemv_close(y_gpu, y_ref, a_ref, label):
+    err = np.abs(y_gpu - y_ref)
+    tol = 1e-3 * a_ref + 1e-5
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, (f"{label}: {len(bad)} outputs outside tolerance, first {bad[:3].tolist()}, "
+                           f"max err/tol {float((err / tol).max()):.3g}")
+
+
+def rand16(rng, shape, scale=0.02):
+    return (scale * rng.standard_normal(shape)).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# packer
+
+def test_scale_every_fp16_amax():
+    """One row per finite fp16 magnitude: the row's only non-zero is that value."""
+    bits = np.arange(0, 0x7C00, dtype=np.uint16)
+    w = np.zeros((len(bits), 64), dtype=np.uint16)
+    w[:, 5] = bits
+    w[1::2, 5] |= 0x8000  # half of them negative
+    w16 = w.view(np.float16)
+    say(f"case scale-exhaustive rows={len(bits)}")
+    ref = O.pack(w16, 4, 64)
+    assert_pack_equal(gpu_pack(w16, 4, 64), ref, "scale-exhaustive")
+
+
+SMALL_CASES = [
+    (1, 64, 2, 64), (3, 192, 2, 64), (17, 256, 2, 128), (5, 512, 2, 256), (33, 256, 2, 0),
+    (4, 64, 4, 64), (9, 384, 4, 128), (7, 768, 4, 0), (2, 64, 1, 64), (6, 512, 1, 0),
+    (11, 1024, 1, 256), (64, 4160, 2, 64),
+]
+
+
+@pytest.mark.parametrize("rows,cols,n_keep,g", SMALL_CASES)
+def test_pack_small_with_special_values(rows, cols, n_keep, g):
+    rng = np.random.default_rng(rows * 1000 + cols + n_keep)
+    w = rand16(rng, (rows, cols))
+    # ties, signed zeros, subnormals, extremes and an all-zero row
+    w[0, :8] = np.float16([0.5, -0.5, 0.5, -0.5, -0.0, 0.0, 0.0, -0.0])
+    if cols >= 32:
+        w[0, 8:16] = np.float16([6e-8, -6e-8, 1.2e-7, 0, 65504, -65504, 1, -1])
+        w[0, 16:32] = np.float16(rng.integers(-2, 3, 16))
+    if rows > 2:
+        w[rows // 2] = 0
+    say(f"case pack-small {rows}x{cols} n={n_keep} g={g}")
+    ref = O.pack(w, n_keep, g)
+    assert_pack_equal(gpu_pack(w, n_keep, g), ref, f"{rows}x{cols} n{n_keep} g{g}")
+
+
+def test_pack_rejects_nonfinite():
+    import int4_sparse_gemv_amd as I
+    w = np.zeros((4, 256), np.float16)
+    w[2, 100] = np.inf
+    say("case pack-nonfinite")
+    with pytest.raises(I.I4SError) as e:
+        gpu_pack(w, 2, 0)
+    assert e.value.status == I._binding.I4S_ERR_NONFINITE_WEIGHT
+    w[2, 100] = np.nan
+    with pytest.raises(I.I4SError):
+        gpu_pack(w, 4, 64)
+
+
+def config_matrices():
+    out = []
+    for name in ("c1_512", "c2_4096", "c3_mlp7b", "c5_verify13b"):
+        for m in WL.WORKLOADS[name].matrices:
+            out.append((name, m))
+    # a sample of the 32-layer stack: a dense and a 2:4 layer, all projections
+    for m in WL.WORKLOADS["c4_stack7b"].matrices:
+        if m.name.startswith(("L0.", "L4.")):
+            out.append(("c4_stack7b", m))
+    return out
+
+
+_REF_CACHE = {}
+
+
+def reference(name, m):
+    key = (name, m.name)
+    if key not in _REF_CACHE:
+        batch = max(WL.WORKLOADS[name].batches)
+        w, x = WL.make_weight_and_x(m, batch)
+        _REF_CACHE.clear()
+        _REF_CACHE[key] = (w, x, O.pack(w, m.n_keep, m.group_size))
+    return _REF_CACHE[key]
+
+
+@pytest.mark.parametrize("name,m", config_matrices(), ids=lambda v: v if isinstance(v, str) else v.name)
+def test_config_pack_and_gemv(name, m):
+    say(f"case config {name}/{m.name} {m.rows}x{m.cols} n={m.n_keep} g={m.group_size}")
+    w, x, ref = reference(name, m)
+    p = gpu_pack(w, m.n_keep, m.group_size)
+    assert_pack_equal(p, ref, f"{name}/{m.name}")
+    w_hat = O.reconstruct(ref)
+    for batch in WL.WORKLOADS[name].batches:
+        say(f"  gemv batch={batch}")
+        y_ref, a_ref = O.gemv(w_hat, x[:batch])
+        assert_gemv_close(gpu_run(p, x[:batch]), y_ref, a_ref, f"{name}/{m.name} b{batch}")
+
+
+# ---------------------------------------------------------------------------
+# GEMV edge cases
+
+@pytest.mark.parametrize("rows,cols,n_keep,g", [
+    (1, 64, 2, 64), (17, 192, 2, 64), (33, 4160, 2, 64), (100, 8192, 2, 128), (5, 64, 4, 64),
+    (19, 320, 4, 64), (21, 4224, 4, 128), (3, 128, 1, 64), (13, 4352, 1, 256), (16, 16384, 2, 256)])
+def test_gemv_shapes_and_all_batches(rows, cols, n_keep, g):
+    rng = np.random.default_rng(rows + cols)
+    w = rand16(rng, (rows, cols))
+    w[rows // 2] = 0  # an all-pruned row
+    say(f"case gemv-shape {rows}x{cols} n={n_keep} g={g}")
+    ref = O.pack(w, n_keep, g)
+    p = gpu_pack(w, n_keep, g)
+    assert_pack_equal(p, ref, "shape")
+    w_hat = O.reconstruct(ref)
+    x = rng.standard_normal((16, cols)).astype(np.float16)
+    for batch in range(1, 17):
+        y_gpu = gpu_run(p, x[:batch])
+        y_ref, a_ref = O.gemv(w_hat, x[:batch])
+        assert_gemv_close(y_gpu, y_ref, a_ref, f"b{batch}")
+        assert (y_gpu[:, rows // 2] == 0).all()
+
+
+def test_gemv_zero_x_and_unit_vectors():
+    rng = np.random.default_rng(77)
+    rows, cols = 40, 512
+    w = rand16(rng, (rows, cols))
+    say("case gemv-unit-vectors")
+    ref = O.pack(w, 2, 128)
+    p = gpu_pack(w, 2, 128)
+    w_hat = O.reconstruct(ref)
+    assert (gpu_run(p, np.zeros((3, cols), np.float16)) == 0).all()
+    cols_to_try = [0, 1, 2, 3, 63, 64, 255, 256, 511]
+    for j0 in range(0, len(cols_to_try), 16):
+        js = cols_to_try[j0:j0 + 16]
+        x = np.zeros((len(js), cols), np.float16)
+        for b, j in enumerate(js):
+            x[b, j] = 1.0
+        y = gpu_run(p, x)
+        for b, j in enumerate(js):
+            # a single product s*q is exact in fp32 and rounds once to fp16
+            np.testing.assert_array_equal(y[b], w_hat[:, j].astype(np.float16).astype(np.float64))
+
+
+def test_batch_rows_match_single_calls():
+    rng = np.random.default_rng(78)
+    rows, cols = 64, 2048
+    w = rand16(rng, (rows, cols))
+    say("case gemv-batch-consistency")
+    p = gpu_pack(w, 2, 64)
+    x = rng.standard_normal((16, cols)).astype(np.float16)
+    yb = gpu_run(p, x)
+    for b in range(16):
+        np.testing.assert_array_equal(yb[b], gpu_run(p, x[b:b + 1])[0])
+
+
+def test_run_on_side_stream():
+    import int4_sparse_gemv_amd as I
+    rng = np.random.default_rng(79)
+    rows, cols = 256, 1024
+    w = rand16(rng, (rows, cols))
+    say("case gemv-side-stream")
+    ref = O.pack(w, 2, 128)
+    x16 = rng.standard_normal((4, cols)).astype(np.float16)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        wt = torch.from_numpy(w.view(np.int16)).cuda().view(torch.float16)
+        p = I.pack(wt, 2, 128)
+        x = torch.from_numpy(x16.view(np.int16)).cuda().view(torch.float16)
+        y = I.run(p, x)
+    s.synchronize()
+    y_ref, a_ref = O.gemv(O.reconstruct(ref), x16)
+    assert_gemv_close(y.cpu().numpy().astype(np.float64), y_ref, a_ref, "side-stream")
