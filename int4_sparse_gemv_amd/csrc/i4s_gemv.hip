@@ -5,28 +5,44 @@
 // staged in on-chip shared memory (LDS here) by the whole block, INT4 weights
 // are widened to fp16 with a few bit operations, and the 2-bit indices packed
 // in uint16 words are decoded with shifts and masks.  The design below is
-// written for CDNA4 (wave64, v_perm_b32, v_dot2_f32_f16, 64 KB+ LDS), not
-// taken from the page's NVIDIA kernel.
+// written for CDNA4 (wave64, v_perm_b32, v_dot2_f32_f16, DPP, 64 KB+ LDS),
+// not taken from the page's NVIDIA kernel.
 //
-// Mapping.  A block is 4 waves; each wave owns RPW consecutive rows.  A row
+// Mapping.  A block is 8 waves (batch-1 kernel) or 4 waves (batch kernel);
+// each wave owns RPW consecutive rows.  A row
 // is cut into 64-column "units" (16 groups of 4 columns: 8*NK bytes of vals,
 // 4*NK bytes of codes, one scale); lane l takes units l, l+64, ...  Adjacent
 // lanes therefore read adjacent 16-byte pieces of a row (dwordx4 for 2:4),
 // and one unit never straddles a quantization group.  The RPW rows of a wave
 // share the same columns, so each activation fetch from LDS feeds RPW rows.
 //
+// Row starts: the kernel reads row_ptr, but it issues the weight loads of a
+// row at the offset the format prescribes (row * K * N / 4) without waiting
+// for that read; when row_ptr disagrees, the row is re-fetched from
+// row_ptr's offset.  A dependent round trip to memory is thus kept off the
+// common path.
+//
 // Per 8 stored elements (one 32-bit vals word) the decode is one shift, four
 // v_and_or_b32 that drop nibble pairs into the mantissa of 1024.0 (fp16
 // 0x6400) and four packed fp16 adds/fmas that remove the bias exactly; the
 // nibble interleave of the format puts elements (2p, 2p+1) in bits 4p and
-// 16+4p so one mask yields one pair.  For 2:4, a group's 4-bit code builds a
-// v_perm_b32 selector that picks the two kept activations out of the group's
-// four, and v_dot2_f32_f16 multiplies and accumulates in fp32.  The group
-// scale is applied once per unit.
+// 16+4p so one mask yields one pair.  For 2:4, a group's 4-bit code picks a
+// v_perm_b32 selector (from a 16-entry table in LDS) that moves the two kept
+// activations out of the group's four into one fp16 pair, and
+// v_dot2_f32_f16 multiplies and accumulates in fp32.  The group scale is
+// applied once per unit.  Row sums across lanes use DPP row rotations and
+// four lane reads (no LDS traffic).
 //
-// Batch: BT activation vectors (BT >= batch, rounded up to 1, 2, 4, 8, 16;
-// the extra vectors are zero in LDS and never stored).  When BT*K*2 bytes do
-// not fit the LDS budget the K axis is processed in chunks, re-staging x.
+// LDS layout of x: each 64-column unit occupies 72 (batch-1 kernel) or 68
+// (batch kernel) halfs, so the 16-byte or 8-byte reads that 64 lanes issue
+// for 64 different units fall in distinct banks.
+//
+// Batch kernel: BT activation vectors (BT >= batch, rounded up to 1, 2, 4,
+// 8, 16; the extra vectors are zero in LDS and never stored).  When the
+// staged activations exceed the LDS budget the K axis is processed in
+// chunks, re-staging x.
+
+#include <stdlib.h>
 
 #include "i4s_internal.h"
 
@@ -38,8 +54,17 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLdsBudget = 64 * 1024;  // bytes of LDS for staged activations
+constexpr int kStrideB1 = 72;          // halfs per unit, batch-1 kernel (16-byte reads)
+constexpr int kStrideBT = 68;          // halfs per unit, batch kernel (8-byte reads)
 
 __device__ inline h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+
+// (a & m) | c in one VALU op; GFX9 VOP3 takes no literal, so m comes in an SGPR.
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
+  return d;
+}
 
 // Four exact fp16 pairs (q_{2p}, q_{2p+1}), p = 0..3, of one vals word.
 __device__ inline void dequant_word(uint32_t w, h2_t q[4]) {
@@ -49,18 +74,19 @@ __device__ inline void dequant_word(uint32_t w, h2_t q[4]) {
   const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const h2_t bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
   // slots 0/4 and 2/6: nibble in mantissa bits 0..3 -> 1024 + u
-  q[0] = as_h2((w & 0x000F000Fu) | magic) + bias;
-  q[2] = as_h2((t & 0x000F000Fu) | magic) + bias;
+  q[0] = as_h2(and_or(w, 0x000F000Fu, magic)) + bias;
+  q[2] = as_h2(and_or(t, 0x000F000Fu, magic)) + bias;
   // slots 1/5 and 3/7: nibble in mantissa bits 4..7 -> 1024 + 16u
-  q[1] = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | magic), sixteenth, bias16);
-  q[3] = __builtin_elementwise_fma(as_h2((t & 0x00F000F0u) | magic), sixteenth, bias16);
+  q[1] = __builtin_elementwise_fma(as_h2(and_or(w, 0x00F000F0u, magic)), sixteenth, bias16);
+  q[3] = __builtin_elementwise_fma(as_h2(and_or(t, 0x00F000F0u, magic)), sixteenth, bias16);
 }
 
 // v_perm_b32 selector taking fp16 lanes cf and cs of a group's four
 // activations (held as two dwords {x0|x1<<16, x2|x3<<16}) into (lo, hi):
-// bytes [2cf, 2cf+1, 2cs, 2cs+1].  h = cf | cs << 2.  The multiply spreads
-// the two 2-bit fields into four byte lanes without carries between them.
-__device__ inline uint32_t pair_selector(uint32_t h) {
+// bytes [2cf, 2cf+1, 2cs, 2cs+1], for the code nibble h = cf | cs << 2.
+// The multiply spreads the two 2-bit fields into four byte lanes without
+// carries between them.
+__host__ __device__ constexpr uint32_t pair_selector(uint32_t h) {
   return ((h * 0x808202u) & 0x06060606u) | 0x01000100u;
 }
 
@@ -73,10 +99,25 @@ __device__ inline uint32_t float_to_fp16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+template <int CTRL>
+__device__ inline float dpp_rot_add(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+  return v + __builtin_bit_cast(float, s);
+}
+
+// Sum over the 64 lanes; every lane gets the result.  Rotations by 8, 4, 2,
+// 1 inside each 16-lane row (DPP row_ror), then the four row sums.
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v = dpp_rot_add<0x128>(v);
+  v = dpp_rot_add<0x124>(v);
+  v = dpp_rot_add<0x122>(v);
+  v = dpp_rot_add<0x121>(v);
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 template <int NK>
@@ -86,12 +127,13 @@ struct UnitRegs {
   uint32_t s;                         // scale bits
 };
 
+// Loads one unit: elem0 is the unit's first element (row start + 16*NK*u).
 template <int NK>
 __device__ inline void load_unit(UnitRegs<NK> &r, const uint8_t *__restrict__ vals,
                                  const uint16_t *__restrict__ codes,
-                                 const uint16_t *__restrict__ scales, int64_t elem0,
-                                 int64_t scale_idx) {
-  const uint32_t *vp = reinterpret_cast<const uint32_t *>(vals + elem0 / 2);
+                                 const uint16_t *__restrict__ scales, uint32_t elem0,
+                                 uint32_t scale_idx) {
+  const uint32_t *vp = reinterpret_cast<const uint32_t *>(vals + (elem0 >> 1));
   if constexpr (NK == 1) {
     const uint2 a = *reinterpret_cast<const uint2 *>(vp);
     r.v[0] = a.x; r.v[1] = a.y;
@@ -105,28 +147,182 @@ __device__ inline void load_unit(UnitRegs<NK> &r, const uint8_t *__restrict__ va
     r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
   }
   if constexpr (NK == 1) {
-    r.c[0] = *reinterpret_cast<const uint32_t *>(codes + elem0 / 8);
+    r.c[0] = *reinterpret_cast<const uint32_t *>(codes + (elem0 >> 3));
   } else if constexpr (NK == 2) {
-    const uint2 c = *reinterpret_cast<const uint2 *>(codes + elem0 / 8);
+    const uint2 c = *reinterpret_cast<const uint2 *>(codes + (elem0 >> 3));
     r.c[0] = c.x; r.c[1] = c.y;
   }
   r.s = scales[scale_idx];
 }
 
-template <int NK>
-__device__ inline void zero_unit(UnitRegs<NK> &r) {
-#pragma unroll
-  for (int i = 0; i < 2 * NK; ++i) r.v[i] = 0x88888888u;  // q = 0
-#pragma unroll
-  for (int i = 0; i < (NK < 4 ? NK : 1); ++i) r.c[i] = 0x44444444u;  // valid codes
-  r.s = 0u;
+// Fill the 16-entry selector table (2:4 only); call with threadIdx.x < 16.
+__device__ inline void init_selector_table(uint32_t *lut) {
+  lut[threadIdx.x] = pair_selector(threadIdx.x);
 }
+
+__device__ inline uint32_t lut_read(const uint32_t *lut, uint32_t byte_off) {
+  return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lut) + byte_off);
+}
+
+// ---------------------------------------------------------------------------
+// batch-1 kernel (2:4 and dense): the lane's 64 activations live in registers
+
+template <int NK>
+__device__ inline float unit_dot_b1(const UnitRegs<NK> &u, const uint32_t (&xr)[32], const uint32_t *lut) {
+  float g = 0.0f;
+  if constexpr (NK == 2) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {  // code dword c: groups 8c..8c+7
+      const uint32_t me = (u.c[c] << 2) & 0x3C3C3C3Cu;  // byte k: 4 * code nibble of group 8c+2k
+      const uint32_t mo = (u.c[c] >> 2) & 0x3C3C3C3Cu;  // byte k: 4 * code nibble of group 8c+2k+1
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {  // vals word j = 2c + half: groups 8c+4half .. +3
+        h2_t q[4];
+        dequant_word(u.v[2 * c + half], q);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int gi = 4 * half + p;  // group within the code dword
+          const uint32_t m = (gi & 1) ? mo : me;
+          const uint32_t sel = lut_read(lut, (m >> (8 * (gi >> 1))) & 0xFFu);
+          const int grp = 8 * c + gi;
+          const uint32_t xp = __builtin_amdgcn_perm(xr[2 * grp + 1], xr[2 * grp], sel);
+          g = __builtin_amdgcn_fdot2(q[p], as_h2(xp), g, false);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // vals word j: columns 8j..8j+7
+      h2_t q[4];
+      dequant_word(u.v[j], q);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) g = __builtin_amdgcn_fdot2(q[p], as_h2(xr[4 * j + p]), g, false);
+    }
+  }
+  return g;
+}
+
+template <int NK, int RPW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
+    int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
+    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
+    uint16_t *__restrict__ y, int kc_units) {
+  extern __shared__ __align__(16) uint16_t xs[];  // [kc_units][kStrideB1]
+  __shared__ uint32_t lut[16];
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  const int row0 = (blockIdx.x * WAVES + wave) * RPW;
+  const int units = cols / kSegCols;
+  const uint32_t nnz_row = (uint32_t)cols / 4 * NK;
+  const int sg_shift = group_size == 64 ? 0 : (group_size == 128 ? 1 : 2);  // log2(G / 64)
+  const uint32_t ngroups = (uint32_t)(cols / group_size);
+
+  // Rows past the end re-read the last row (their sums are never stored),
+  // so every load and every decode below works on real data.
+  uint32_t rstart[RPW], srow[RPW];
+  bool rvalid[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    rvalid[r] = row0 + r < rows;
+    const int rr = min(row0 + r, rows - 1);
+    rstart[r] = (uint32_t)rr * nnz_row;  // the format's offset
+    srow[r] = (uint32_t)rr * ngroups;    // first scale of the row
+  }
+
+  float acc[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+
+  for (int ub = 0; ub < units; ub += kc_units) {
+    const int ue = min(units, ub + kc_units);
+    int u = ub + lane;
+    bool has = u < ue;
+    UnitRegs<NK> cur[RPW];
+    if (has) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                      srow[r] + ((uint32_t)u >> sg_shift));
+    }
+    int32_t rp[RPW];
+    if (ub == 0) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) rp[r] = row_ptr[min(row0 + r, rows - 1)];
+    }
+
+    if (ub > 0) __syncthreads();  // the previous chunk is fully consumed
+    {
+      const int nvec = (ue - ub) * (kSegCols / 8);  // uint4 = 8 halfs
+      for (int i = threadIdx.x; i < nvec; i += 64 * WAVES) {
+        const int un = i >> 3, part = i & 7;
+        *reinterpret_cast<uint4 *>(xs + un * kStrideB1 + 8 * part) =
+            *reinterpret_cast<const uint4 *>(x + (int64_t)ub * kSegCols + 8 * i);
+      }
+      if (NK == 2 && ub == 0 && threadIdx.x < 16) init_selector_table(lut);
+    }
+    __syncthreads();
+
+    if (ub == 0) {
+      // row_ptr check (wave-uniform): re-fetch rows stored elsewhere
+      bool moved = false;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) moved |= (uint32_t)rp[r] != rstart[r];
+      if (moved) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          rstart[r] = (uint32_t)rp[r];
+          if (has)
+            load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                          srow[r] + ((uint32_t)u >> sg_shift));
+        }
+      }
+    }
+
+    while (has) {
+      const int un = u + 64;
+      const bool hn = un < ue;
+      UnitRegs<NK> nxt[RPW];
+      if (hn) {  // prefetch the lane's next unit
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+          load_unit<NK>(nxt[r], vals, codes, scales, rstart[r] + (uint32_t)un * 16 * NK,
+                        srow[r] + ((uint32_t)un >> sg_shift));
+      }
+      uint32_t xr[32];
+      const uint4 *xv = reinterpret_cast<const uint4 *>(xs + (u - ub) * kStrideB1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 t = xv[i];
+        xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float gsum = unit_dot_b1<NK>(cur[r], xr, lut);
+        acc[r] = fmaf(fp16_bits_to_float(cur[r].s), gsum, acc[r]);
+      }
+      if (!hn) break;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) cur[r] = nxt[r];
+      u = un;
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float t = wave_sum(acc[r]);
+    if (lane == 0 && rvalid[r]) y[row0 + r] = (uint16_t)float_to_fp16_bits(t);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// batch kernel (any N, 1 <= batch <= 16)
 
 // Accumulate one unit of RPW rows into acc[r][b].  xs points at the LDS copy
 // of the unit's 64 columns for batch vector 0; vector b is xstride halfs on.
 template <int NK, int BT, int RPW>
 __device__ inline void compute_unit(const UnitRegs<NK> (&u)[RPW], const uint16_t *xs, int xstride,
-                                    float (&acc)[RPW][BT]) {
+                                    const uint32_t *lut, float (&acc)[RPW][BT]) {
   float g[RPW][BT];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
@@ -148,7 +344,7 @@ __device__ inline void compute_unit(const UnitRegs<NK> (&u)[RPW], const uint16_t
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
           const uint32_t cw = u[r].c[j >> 1] >> (16 * (j & 1));
-          const uint32_t sel = pair_selector((cw >> (4 * p)) & 0xFu);
+          const uint32_t sel = lut_read(lut, ((cw >> (4 * p)) & 0xFu) << 2);
 #pragma unroll
           for (int b = 0; b < BT; ++b) {
             const uint32_t xp = __builtin_amdgcn_perm(xg[b].y, xg[b].x, sel);
@@ -163,18 +359,19 @@ __device__ inline void compute_unit(const UnitRegs<NK> (&u)[RPW], const uint16_t
       h2_t q[RPW][4];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) dequant_word(u[r].v[j], q[r]);
-      uint4 xg[BT];
 #pragma unroll
-      for (int b = 0; b < BT; ++b) xg[b] = *reinterpret_cast<const uint4 *>(xs + b * xstride + 8 * j);
+      for (int h = 0; h < 2; ++h) {
+        uint2 xg[BT];
 #pragma unroll
-      for (int r = 0; r < RPW; ++r)
+        for (int b = 0; b < BT; ++b) xg[b] = *reinterpret_cast<const uint2 *>(xs + b * xstride + 8 * j + 4 * h);
 #pragma unroll
-        for (int b = 0; b < BT; ++b) {
-          g[r][b] = __builtin_amdgcn_fdot2(q[r][0], as_h2(xg[b].x), g[r][b], false);
-          g[r][b] = __builtin_amdgcn_fdot2(q[r][1], as_h2(xg[b].y), g[r][b], false);
-          g[r][b] = __builtin_amdgcn_fdot2(q[r][2], as_h2(xg[b].z), g[r][b], false);
-          g[r][b] = __builtin_amdgcn_fdot2(q[r][3], as_h2(xg[b].w), g[r][b], false);
-        }
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+          for (int b = 0; b < BT; ++b) {
+            g[r][b] = __builtin_amdgcn_fdot2(q[r][2 * h], as_h2(xg[b].x), g[r][b], false);
+            g[r][b] = __builtin_amdgcn_fdot2(q[r][2 * h + 1], as_h2(xg[b].y), g[r][b], false);
+          }
+      }
     }
   } else {  // NK == 1: element e of the unit is group e, column 4e + code
 #pragma unroll
@@ -212,21 +409,28 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
-    uint16_t *__restrict__ y, int kc_cols) {
-  extern __shared__ uint16_t xs[];  // [BT][kc_cols]
+    uint16_t *__restrict__ y, int kc_units) {
+  extern __shared__ __align__(16) uint16_t xs[];  // [BT][kc_units][kStrideBT]
+  __shared__ uint32_t lut[16];
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
   const int row0 = (blockIdx.x * kWaves + wave) * RPW;
-  const int sg = group_size / kSegCols;  // units per quantization group
-  const int ngroups = cols / group_size;
+  const int units = cols / kSegCols;
+  const uint32_t nnz_row = (uint32_t)cols / 4 * NK;
+  const int sg_shift = group_size == 64 ? 0 : (group_size == 128 ? 1 : 2);  // log2(G / 64)
+  const uint32_t ngroups = (uint32_t)(cols / group_size);
+  const int xstride = kc_units * kStrideBT;  // halfs between batch vectors in LDS
 
-  // Row starts come from row_ptr (CSR); every row holds cols*NK/4 elements.
-  int64_t rstart[RPW];
+  // Rows past the end re-read the last row (their sums are never stored),
+  // so every load and every decode below works on real data.
+  uint32_t rstart[RPW], srow[RPW];
   bool rvalid[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     rvalid[r] = row0 + r < rows;
-    rstart[r] = rvalid[r] ? (int64_t)row_ptr[row0 + r] : 0;
+    const int rr = min(row0 + r, rows - 1);
+    rstart[r] = (uint32_t)rr * nnz_row;  // the format's offset
+    srow[r] = (uint32_t)rr * ngroups;    // first scale of the row
   }
 
   float acc[RPW][BT];
@@ -235,53 +439,73 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
     for (int b = 0; b < BT; ++b) acc[r][b] = 0.0f;
 
-  for (int k0 = 0; k0 < cols; k0 += kc_cols) {
-    const int kcn = min(kc_cols, cols - k0);
-    const int ub = k0 / kSegCols, ue = (k0 + kcn) / kSegCols;
-
-    // issue the first weight loads of this chunk before staging x
+  for (int ub = 0; ub < units; ub += kc_units) {
+    const int ue = min(units, ub + kc_units);
     int u = ub + lane;
     bool has = u < ue;
     UnitRegs<NK> cur[RPW];
+    if (has) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      if (has && rvalid[r])
-        load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (int64_t)u * 16 * NK,
-                      (int64_t)(row0 + r) * ngroups + u / sg);
-      else
-        zero_unit<NK>(cur[r]);
+      for (int r = 0; r < RPW; ++r)
+        load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                      srow[r] + ((uint32_t)u >> sg_shift));
+    }
+    int32_t rp[RPW];
+    if (ub == 0) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) rp[r] = row_ptr[min(row0 + r, rows - 1)];
     }
 
-    if (k0 > 0) __syncthreads();  // previous chunk fully consumed
+    if (ub > 0) __syncthreads();  // the previous chunk is fully consumed
     {
-      const int vec_per_row = kcn / 8;  // uint4 = 8 halfs
-      const int total = BT * vec_per_row;
-      for (int i = threadIdx.x; i < total; i += kThreads) {
-        const int b = i / vec_per_row, c = i % vec_per_row;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (b < batch) v = *reinterpret_cast<const uint4 *>(x + (int64_t)b * cols + k0 + 8 * c);
-        *reinterpret_cast<uint4 *>(xs + b * kc_cols + 8 * c) = v;
+      const int vpb = (ue - ub) * (kSegCols / 8);  // uint4 per batch vector
+      for (int i = threadIdx.x; i < BT * vpb; i += kThreads) {
+        const int b = i / vpb, c = i % vpb;
+        const int un = c >> 3, part = c & 7;
+        uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+        if (b < batch) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(x + (int64_t)b * cols + (int64_t)ub * kSegCols + 8 * c);
+          lo = make_uint2(v.x, v.y);
+          hi = make_uint2(v.z, v.w);
+        }
+        uint16_t *dst = xs + b * xstride + un * kStrideBT + 8 * part;  // 8-byte aligned
+        reinterpret_cast<uint2 *>(dst)[0] = lo;
+        reinterpret_cast<uint2 *>(dst)[1] = hi;
       }
+      if (NK == 2 && ub == 0 && threadIdx.x < 16) init_selector_table(lut);
     }
     __syncthreads();
+
+    if (ub == 0) {
+      bool moved = false;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) moved |= (uint32_t)rp[r] != rstart[r];
+      if (moved) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          rstart[r] = (uint32_t)rp[r];
+          if (has)
+            load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                          srow[r] + ((uint32_t)u >> sg_shift));
+        }
+      }
+    }
 
     while (has) {
       const int un = u + 64;
       const bool hn = un < ue;
       UnitRegs<NK> nxt[RPW];
+      if (hn) {  // prefetch the lane's next unit
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        if (hn && rvalid[r])
-          load_unit<NK>(nxt[r], vals, codes, scales, rstart[r] + (int64_t)un * 16 * NK,
-                        (int64_t)(row0 + r) * ngroups + un / sg);
-        else
-          zero_unit<NK>(nxt[r]);
+        for (int r = 0; r < RPW; ++r)
+          load_unit<NK>(nxt[r], vals, codes, scales, rstart[r] + (uint32_t)un * 16 * NK,
+                        srow[r] + ((uint32_t)un >> sg_shift));
       }
-      compute_unit<NK, BT, RPW>(cur, xs + (u - ub) * kSegCols, kc_cols, acc);
+      compute_unit<NK, BT, RPW>(cur, xs + (u - ub) * kStrideBT, xstride, lut, acc);
+      if (!hn) break;
 #pragma unroll
       for (int r = 0; r < RPW; ++r) cur[r] = nxt[r];
       u = un;
-      has = hn;
     }
   }
 
@@ -295,12 +519,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// dispatch
+
 template <int NK, int BT, int RPW>
 hipError_t launch_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                     hipStream_t stream) {
-  int kc = (kLdsBudget / (BT * 2)) / kSegCols * kSegCols;
-  if (kc > w.cols) kc = w.cols;
-  const size_t lds = (size_t)BT * kc * 2;
+  const int units = w.cols / kSegCols;
+  int kc = kLdsBudget / (BT * kStrideBT * 2);
+  if (kc > units) kc = units;
+  const size_t lds = (size_t)BT * kc * kStrideBT * 2;
   const int rows_per_block = kWaves * RPW;
   const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(kThreads);
   hipLaunchKernelGGL((gemv_kernel<NK, BT, RPW>), grid, block, lds, stream, w.rows, w.cols,
@@ -308,10 +536,50 @@ hipError_t launch_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint1
   return hipGetLastError();
 }
 
+// Batch-1 kernel: 8 waves per block (512 threads), RPW rows per wave.
+constexpr int kB1Waves = 8;
+
+template <int NK, int RPW>
+hipError_t launch_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  const int units = w.cols / kSegCols;
+  int kc = kLdsBudget / (kStrideB1 * 2);
+  if (kc > units) kc = units;
+  const size_t lds = (size_t)kc * kStrideB1 * 2;
+  const int rows_per_block = kB1Waves * RPW;
+  const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kB1Waves);
+  hipLaunchKernelGGL((gemv_b1_kernel<NK, RPW, kB1Waves>), grid, block, lds, stream, w.rows, w.cols,
+                     w.group_size, w.row_ptr, w.vals, w.codes, w.scales, x, y, kc);
+  return hipGetLastError();
+}
+
+// Rows per wave of the batch-1 kernel.  One row per wave keeps 2+ blocks on
+// every CU up to ~8k rows; taller matrices take two rows per wave so each
+// block's staged activations feed more rows.  I4S_B1_RPW (1, 2 or 4)
+// overrides the choice for tuning; it is read once.
+int b1_rows_per_wave(int rows) {
+  static const int forced = [] {
+    const char *e = getenv("I4S_B1_RPW");
+    const int r = e ? atoi(e) : 0;
+    return (r == 1 || r == 2 || r == 4) ? r : 0;
+  }();
+  if (forced) return forced;
+  return rows > 8192 ? 2 : 1;
+}
+
 template <int NK>
 hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                      hipStream_t stream) {
-  if (batch <= 1) return launch_t<NK, 1, 4>(w, x, batch, y, stream);
+  if (batch <= 1) {
+    if constexpr (NK == 2 || NK == 4) {
+      switch (b1_rows_per_wave(w.rows)) {
+        case 1: return launch_b1<NK, 1>(w, x, y, stream);
+        case 4: return launch_b1<NK, 4>(w, x, y, stream);
+        case 2: return launch_b1<NK, 2>(w, x, y, stream);
+        default: return launch_b1<NK, 1>(w, x, y, stream);
+      }
+    }
+    return launch_t<NK, 1, 4>(w, x, batch, y, stream);
+  }
   if (batch <= 2) return launch_t<NK, 2, 4>(w, x, batch, y, stream);
   if (batch <= 4) return launch_t<NK, 4, 2>(w, x, batch, y, stream);
   if (batch <= 8) return launch_t<NK, 8, 2>(w, x, batch, y, stream);

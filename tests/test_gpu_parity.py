@@ -248,3 +248,26 @@ def test_run_on_side_stream():
     s.synchronize()
     y_ref, a_ref = O.gemv(O.reconstruct(ref), x16)
     assert_gemv_close(y.cpu().numpy().astype(np.float64), y_ref, a_ref, "side-stream")
+
+
+@pytest.mark.parametrize("n_keep,batch", [(2, 1), (4, 1), (2, 3), (1, 1), (4, 8)])
+def test_row_ptr_is_honoured(n_keep, batch):
+    """Rows stored in reverse order, described only by row_ptr, give the same y."""
+    import int4_sparse_gemv_amd as I
+    rng = np.random.default_rng(80 + n_keep)
+    rows, cols, g = 37, 4096 + 1024, 128
+    w = rand16(rng, (rows, cols))
+    say(f"case row-ptr-reversed n={n_keep} b={batch}")
+    p = gpu_pack(w, n_keep, g)
+    x16 = rng.standard_normal((batch, cols)).astype(np.float16)
+    y0 = gpu_run(p, x16)
+    nnz_row = cols * n_keep // 4
+    vb, cb = nnz_row // 2, nnz_row // 8
+    perm = torch.arange(rows - 1, -1, -1, device=p.vals.device)
+    vals = p.vals.view(rows, vb)[perm].reshape(-1).contiguous()
+    codes = p.codes.view(rows, cb)[perm].reshape(-1).contiguous() if p.codes is not None else None
+    row_ptr = torch.tensor([(rows - 1 - i) * nnz_row for i in range(rows)] + [rows * nnz_row],
+                           dtype=torch.int32, device=p.vals.device)
+    q = I.PackedWeight(rows, cols, n_keep, p.group_size, row_ptr, vals, codes, p.scales)
+    y1 = gpu_run(q, x16)
+    np.testing.assert_array_equal(y0, y1)
