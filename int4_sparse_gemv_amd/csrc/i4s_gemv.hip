@@ -520,6 +520,235 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// batch kernel on the sparse matrix cores (2:4, 2 <= batch <= 16)
+//
+// v_smfmac_f32_16x16x64_f16 multiplies a 16x64 2:4-sparse A (8 kept fp16
+// values per lane plus their 2-bit in-group positions) by a dense 64x16 B
+// and accumulates a 16x16 fp32 tile.  Here A is 16 weight rows and B is 64
+// columns of the 16 activation vectors (vectors past `batch` are zero).  On
+// gfx950 lane l = i + 16*kq of A holds row i's kept elements 8kq..8kq+7 of the
+// tile's 64 columns, and its index VGPR holds their 2-bit positions at bits
+// 2e (low half; abid 1 selects the high half) -- exactly one 32-bit vals word
+// and one uint16 code word of the 2-bit CSR format, so the codes go to the
+// matrix core untouched.  B lane j + 16*bq holds vector j's columns
+// 8bq..8bq+7 and 32+8bq..32+8bq+7; the accumulator lane j + 16*q holds rows
+// 4q..4q+3 of vector j.
+//
+// A lane loads one whole 64-column unit of its row (16-byte vals, 8-byte
+// codes) for each block of 4 units; a 4x4 transpose across the 4 lanes of a
+// row (v_permlane32_swap + v_permlane16_swap) then hands lane kq word kq of
+// each unit, so one matrix instruction covers exactly one unit, which lies in
+// one quantization group: the group scale multiplies the fp32 tile after the
+// group's last unit (exact, as in the other kernels).
+//
+// The block's 4 waves share its row tiles and split K (each takes every 4th
+// block of 4 units); x is staged in LDS in chunks of 28 units for all 16
+// vectors, and the 4 partial tiles are summed in LDS at the end.
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h16_t __attribute__((ext_vector_type(16)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kMWaves = 4;
+constexpr int kMChunkUnits = 28;                      // units of x staged per chunk
+constexpr int kMXStride = kMChunkUnits * kSegCols + 8;  // halfs per vector in LDS (16-byte pad)
+constexpr int kMXBytes = 16 * kMXStride * 2;
+
+// Transpose a 4x4 block of dwords held by the 4 lanes i, i+16, i+32, i+48:
+// on return lane-row q holds in v_s what lane-row s held in v_q.
+__device__ inline void transpose4(uint32_t &v0, uint32_t &v1, uint32_t &v2, uint32_t &v3) {
+  auto a = __builtin_amdgcn_permlane32_swap(v0, v2, false, false);
+  v0 = a[0]; v2 = a[1];
+  auto b = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
+  v1 = b[0]; v3 = b[1];
+  auto c = __builtin_amdgcn_permlane16_swap(v0, v1, false, false);
+  v0 = c[0]; v1 = c[1];
+  auto d = __builtin_amdgcn_permlane16_swap(v2, v3, false, false);
+  v2 = d[0]; v3 = d[1];
+}
+
+// Codes of one unit per lane-row (c0 = halfwords 0,1; c1 = halfwords 2,3) ->
+// p = (halfword q of unit 0, of unit 2), r = (halfword q of unit 1, of unit 3)
+// for lane-row q.
+__device__ inline void transpose_codes(uint32_t c0, uint32_t c1, uint32_t &p, uint32_t &r) {
+  auto a = __builtin_amdgcn_permlane32_swap(c0, c1, false, false);
+  const uint32_t lo = __builtin_amdgcn_perm(a[1], a[0], 0x05040100u);
+  const uint32_t hi = __builtin_amdgcn_perm(a[1], a[0], 0x07060302u);
+  auto b = __builtin_amdgcn_permlane16_swap(lo, hi, false, false);
+  p = b[0];
+  r = b[1];
+}
+
+template <int S>
+__device__ inline f4_t smfmac_step(const uint32_t w, const h16_t &bx, const f4_t &c, uint32_t p, uint32_t r) {
+  h2_t q[4];
+  dequant_word(w, q);
+  u4_t qa = {__builtin_bit_cast(uint32_t, q[0]), __builtin_bit_cast(uint32_t, q[1]),
+             __builtin_bit_cast(uint32_t, q[2]), __builtin_bit_cast(uint32_t, q[3])};
+  const h8_t a = __builtin_bit_cast(h8_t, qa);
+  const int idx = (int)((S & 1) ? r : p);
+  return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, bx, c, idx, 0, S >> 1);
+}
+
+template <int RT>
+__global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
+    int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
+    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
+    uint16_t *__restrict__ y) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint16_t *xs = lds;                                                  // [16][kMXStride]
+  uint16_t *sc = lds + kMXBytes / 2;                                   // [RT][kMChunkUnits][16]
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  const int li = lane % 16, lq = lane / 16;
+  const int row_base = blockIdx.x * 16 * RT;
+  const int units = cols / kSegCols;
+  const uint32_t nnz_row = (uint32_t)cols / 2;
+  const int sg = group_size / kSegCols;
+  const int sg_shift = sg == 1 ? 0 : (sg == 2 ? 1 : 2);
+  const uint32_t ngroups = (uint32_t)(cols / group_size);
+
+  // A rows of this lane (clamped: rows past the end re-read the last row)
+  uint32_t rstart[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) rstart[t] = (uint32_t)min(row_base + 16 * t + li, rows - 1) * nnz_row;
+
+  // vectors past `batch` stay zero for the whole kernel
+  for (int i = threadIdx.x; i < (16 - batch) * (kMXStride / 8); i += 64 * kMWaves)
+    reinterpret_cast<uint4 *>(xs + batch * kMXStride)[i] = make_uint4(0u, 0u, 0u, 0u);
+
+  f4_t acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  bool first = true;
+  for (int ub = 0; ub < units; ub += kMChunkUnits) {
+    const int ue = min(units, ub + kMChunkUnits);
+    const int nblk = (ue - ub + 3) / 4;
+
+    // first block of this wave in the chunk: issue its weight loads early
+    int blk = wave;
+    uint32_t V[RT][4], C[RT][2];
+    auto load_block = [&](int b) {
+      const int u = ub + 4 * b + lq;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        if (u < ue) {
+          const uint32_t e0 = rstart[t] + (uint32_t)u * 32;
+          const uint4 v = *reinterpret_cast<const uint4 *>(vals + (e0 >> 1));
+          const uint2 c = *reinterpret_cast<const uint2 *>(codes + (e0 >> 3));
+          V[t][0] = v.x; V[t][1] = v.y; V[t][2] = v.z; V[t][3] = v.w;
+          C[t][0] = c.x; C[t][1] = c.y;
+        } else {
+          V[t][0] = V[t][1] = V[t][2] = V[t][3] = 0x88888888u;  // q = 0
+          C[t][0] = C[t][1] = 0x44444444u;
+        }
+      }
+    };
+    if (blk < nblk) load_block(blk);
+    int32_t rp[RT];
+    if (first) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) rp[t] = row_ptr[min(row_base + 16 * t + li, rows - 1)];
+    }
+
+    __syncthreads();  // the previous chunk is consumed
+    {
+      const int vpb = (ue - ub) * (kSegCols / 8);
+      for (int i = threadIdx.x; i < batch * vpb; i += 64 * kMWaves) {
+        const int b = i / vpb, c = i % vpb;
+        *reinterpret_cast<uint4 *>(xs + b * kMXStride + 8 * c) =
+            *reinterpret_cast<const uint4 *>(x + (int64_t)b * cols + (int64_t)ub * kSegCols + 8 * c);
+      }
+      const int ng = (ue - ub) >> sg_shift, g0 = ub >> sg_shift;
+      for (int i = threadIdx.x; i < RT * 16 * ng; i += 64 * kMWaves) {
+        const int g = i % ng, r = (i / ng) % 16, t = i / (ng * 16);
+        const int row = min(row_base + 16 * t + r, rows - 1);
+        sc[(t * kMChunkUnits + g) * 16 + r] = scales[(uint32_t)row * ngroups + g0 + g];
+      }
+    }
+    __syncthreads();
+
+    if (first) {
+      first = false;
+      // row_ptr check: a row stored elsewhere is re-fetched from there
+      bool moved = false;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        if ((uint32_t)rp[t] != rstart[t]) { rstart[t] = (uint32_t)rp[t]; moved = true; }
+      }
+      if (moved && blk < nblk) load_block(blk);
+    }
+
+    for (; blk < nblk; blk += kMWaves) {
+      // this block's words and codes, transposed so lane-row q holds word q of each unit
+      uint32_t W[RT][4], P[RT], Q[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        W[t][0] = V[t][0]; W[t][1] = V[t][1]; W[t][2] = V[t][2]; W[t][3] = V[t][3];
+        transpose4(W[t][0], W[t][1], W[t][2], W[t][3]);
+        transpose_codes(C[t][0], C[t][1], P[t], Q[t]);
+      }
+      const int u4 = ub + 4 * blk;
+      if (blk + kMWaves < nblk) load_block(blk + kMWaves);  // prefetch
+
+      f4_t cg[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) cg[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int u = u4 + s;
+        if (u >= ue) break;
+        const uint16_t *xb = xs + li * kMXStride + (u - ub) * kSegCols + 8 * lq;
+        const uint4 xa = *reinterpret_cast<const uint4 *>(xb);
+        const uint4 xc = *reinterpret_cast<const uint4 *>(xb + 32);
+        const u8_t xv = {xa.x, xa.y, xa.z, xa.w, xc.x, xc.y, xc.z, xc.w};
+        const h16_t bx = __builtin_bit_cast(h16_t, xv);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          if (s == 0) cg[t] = smfmac_step<0>(W[t][0], bx, cg[t], P[t], Q[t]);
+          if (s == 1) cg[t] = smfmac_step<1>(W[t][1], bx, cg[t], P[t], Q[t]);
+          if (s == 2) cg[t] = smfmac_step<2>(W[t][2], bx, cg[t], P[t], Q[t]);
+          if (s == 3) cg[t] = smfmac_step<3>(W[t][3], bx, cg[t], P[t], Q[t]);
+        }
+        if (((u + 1) & (sg - 1)) == 0) {  // the group ends with this unit
+          const int g = (u >> sg_shift) - (ub >> sg_shift);
+#pragma unroll
+          for (int t = 0; t < RT; ++t) {
+            const uint2 sv = *reinterpret_cast<const uint2 *>(sc + (t * kMChunkUnits + g) * 16 + 4 * lq);
+            acc[t][0] = fmaf(fp16_bits_to_float(sv.x & 0xFFFFu), cg[t][0], acc[t][0]);
+            acc[t][1] = fmaf(fp16_bits_to_float(sv.x >> 16), cg[t][1], acc[t][1]);
+            acc[t][2] = fmaf(fp16_bits_to_float(sv.y & 0xFFFFu), cg[t][2], acc[t][2]);
+            acc[t][3] = fmaf(fp16_bits_to_float(sv.y >> 16), cg[t][3], acc[t][3]);
+            cg[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+        }
+      }
+    }
+  }
+
+  // sum the 4 waves' partial tiles (LDS reused) and store
+  __syncthreads();
+  float *red = reinterpret_cast<float *>(lds);  // [wave][t][4][64]
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((wave * RT + t) * 4 + r) * 64 + lane] = acc[t][r];
+  __syncthreads();
+  for (int o = threadIdx.x; o < RT * 4 * 64; o += 64 * kMWaves) {
+    const int l = o % 64, r = (o / 64) % 4, t = o / 256;
+    float v = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kMWaves; ++wv) v += red[((wv * RT + t) * 4 + r) * 64 + l];
+    const int j = l % 16, row = row_base + 16 * t + 4 * (l / 16) + r;
+    if (j < batch && row < rows) y[(int64_t)j * rows + row] = (uint16_t)float_to_fp16_bits(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 
 template <int NK, int BT, int RPW>
@@ -566,9 +795,34 @@ int b1_rows_per_wave(int rows) {
   return rows > 8192 ? 2 : 1;
 }
 
+template <int RT>
+hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+                         hipStream_t stream) {
+  const size_t lds = (size_t)kMXBytes + (size_t)RT * kMChunkUnits * 16 * 2;
+  const int rows_per_block = 16 * RT;
+  const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kMWaves);
+  hipLaunchKernelGGL((gemv_smfmac_kernel<RT>), grid, block, lds, stream, w.rows, w.cols, w.group_size,
+                     w.row_ptr, w.vals, w.codes, w.scales, x, batch, y);
+  return hipGetLastError();
+}
+
+// I4S_BATCH_PATH=valu forces the VALU batch kernel for 2:4 (tuning and
+// cross-checks); read once.
+bool smfmac_enabled() {
+  static const bool v = [] {
+    const char *e = getenv("I4S_BATCH_PATH");
+    return !(e && e[0] == 'v');
+  }();
+  return v;
+}
+
 template <int NK>
 hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                      hipStream_t stream) {
+  if (NK == 2 && batch >= 2 && smfmac_enabled()) {
+    const int tiles = (w.rows + 15) / 16;
+    return tiles >= 512 ? launch_smfmac<2>(w, x, batch, y, stream) : launch_smfmac<1>(w, x, batch, y, stream);
+  }
   if (batch <= 1) {
     if constexpr (NK == 2 || NK == 4) {
       switch (b1_rows_per_wave(w.rows)) {

@@ -219,16 +219,28 @@ def test_gemv_zero_x_and_unit_vectors():
             np.testing.assert_array_equal(y[b], w_hat[:, j].astype(np.float16).astype(np.float64))
 
 
-def test_batch_rows_match_single_calls():
+@pytest.mark.parametrize("n_keep", [1, 2, 4])
+def test_batch_rows_match_single_calls(n_keep):
+    """Row b of a batch call matches the batch-1 call on x_b (within the
+    tolerance: batch 1 and batch >= 2 run different kernels), and is
+    bit-identical across every batch size >= 2 (one kernel, no mixing of
+    vectors)."""
     rng = np.random.default_rng(78)
     rows, cols = 64, 2048
     w = rand16(rng, (rows, cols))
-    say("case gemv-batch-consistency")
-    p = gpu_pack(w, 2, 64)
+    say(f"case gemv-batch-consistency n={n_keep}")
+    ref = O.pack(w, n_keep, 64)
+    p = gpu_pack(w, n_keep, 64)
+    w_hat = O.reconstruct(ref)
     x = rng.standard_normal((16, cols)).astype(np.float16)
-    yb = gpu_run(p, x)
+    y16 = gpu_run(p, x)
     for b in range(16):
-        np.testing.assert_array_equal(yb[b], gpu_run(p, x[b:b + 1])[0])
+        y1 = gpu_run(p, x[b:b + 1])[0]
+        y_ref, a_ref = O.gemv(w_hat, x[b:b + 1])
+        assert_gemv_close(y1[None], y_ref, a_ref, f"single {b}")
+        assert_gemv_close(y16[b][None], y_ref, a_ref, f"batch row {b}")
+    for nb in range(2, 16):
+        np.testing.assert_array_equal(gpu_run(p, x[:nb]), y16[:nb])
 
 
 def test_run_on_side_stream():
