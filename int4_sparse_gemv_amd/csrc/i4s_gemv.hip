@@ -535,15 +535,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 // 4q..4q+3 of vector j.
 //
 // A lane loads one whole 64-column unit of its row (16-byte vals, 8-byte
-// codes) for each block of 4 units; a 4x4 transpose across the 4 lanes of a
-// row (v_permlane32_swap + v_permlane16_swap) then hands lane kq word kq of
-// each unit, so one matrix instruction covers exactly one unit, which lies in
-// one quantization group: the group scale multiplies the fp32 tile after the
-// group's last unit (exact, as in the other kernels).
+// codes, its scale) for each block of 4 units; a 4x4 transpose across the 4
+// lanes of a row (v_permlane32_swap + v_permlane16_swap) then hands lane kq
+// word kq of each unit, so one matrix instruction covers exactly one unit,
+// which lies in one quantization group: the group scale multiplies the fp32
+// tile after the group's last unit (exact, as in the other kernels).  Scales
+// move from the loading lanes to the accumulator lanes through a small
+// wave-private LDS slot.
 //
-// The block's 4 waves share its row tiles and split K (each takes every 4th
-// block of 4 units); x is staged in LDS in chunks of 28 units for all 16
-// vectors, and the 4 partial tiles are summed in LDS at the end.
+// A block is one 16-row tile and 8 waves; wave w takes blocks of 4 units
+// w, w+8, ... (a K split inside the block) and reads its B fragments straight
+// from global memory (x is small and stays in L2), so there is no block-wide
+// staging and no barrier until the 8 partial tiles are summed in LDS at the
+// end.  The next block's weights and activations are loaded while the
+// current one runs on the matrix core.
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 h16_t __attribute__((ext_vector_type(16)));
@@ -551,10 +556,7 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kMWaves = 4;
-constexpr int kMChunkUnits = 28;                      // units of x staged per chunk
-constexpr int kMXStride = kMChunkUnits * kSegCols + 8;  // halfs per vector in LDS (16-byte pad)
-constexpr int kMXBytes = 16 * kMXStride * 2;
+constexpr int kMWaves = 8;
 
 // Transpose a 4x4 block of dwords held by the 4 lanes i, i+16, i+32, i+48:
 // on return lane-row q holds in v_s what lane-row s held in v_q.
@@ -592,158 +594,120 @@ __device__ inline f4_t smfmac_step(const uint32_t w, const h16_t &bx, const f4_t
   return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, bx, c, idx, 0, S >> 1);
 }
 
-template <int RT>
+// Registers of one block of 4 units for one lane.
+struct MBlock {
+  uint32_t v[4];   // vals words of the lane's unit
+  uint32_t c[2];   // its code words
+  uint32_t s;      // its scale
+  uint4 x[8];      // B fragments of the 4 units (2 x 16 bytes each)
+};
+
+
 __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
     int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
     uint16_t *__restrict__ y) {
-  extern __shared__ __align__(16) uint16_t lds[];
-  uint16_t *xs = lds;                                                  // [16][kMXStride]
-  uint16_t *sc = lds + kMXBytes / 2;                                   // [RT][kMChunkUnits][16]
+  __shared__ __align__(16) uint16_t scs[kMWaves][4][16];   // per wave: scales of 4 units x 16 rows
+  __shared__ __align__(16) float red[kMWaves][4][64];      // partial tiles
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
   const int li = lane % 16, lq = lane / 16;
-  const int row_base = blockIdx.x * 16 * RT;
+  const int row0 = blockIdx.x * 16;
   const int units = cols / kSegCols;
+  const int nblk = (units + 3) / 4;
   const uint32_t nnz_row = (uint32_t)cols / 2;
   const int sg = group_size / kSegCols;
   const int sg_shift = sg == 1 ? 0 : (sg == 2 ? 1 : 2);
   const uint32_t ngroups = (uint32_t)(cols / group_size);
 
-  // A rows of this lane (clamped: rows past the end re-read the last row)
-  uint32_t rstart[RT];
-#pragma unroll
-  for (int t = 0; t < RT; ++t) rstart[t] = (uint32_t)min(row_base + 16 * t + li, rows - 1) * nnz_row;
+  // this lane's weight row (clamped: rows past the end re-read the last row)
+  const int arow = min(row0 + li, rows - 1);
+  uint32_t rstart = (uint32_t)arow * nnz_row;  // the format's offset; checked against row_ptr below
+  // B lane (vector li, column quarter lq).  Lanes of vectors past `batch`
+  // read the last real vector: B column j only feeds output column j, and
+  // those columns are never stored.
+  const uint16_t *xrow = x + (int64_t)min(li, batch - 1) * cols + 8 * lq;
 
-  // vectors past `batch` stay zero for the whole kernel
-  for (int i = threadIdx.x; i < (16 - batch) * (kMXStride / 8); i += 64 * kMWaves)
-    reinterpret_cast<uint4 *>(xs + batch * kMXStride)[i] = make_uint4(0u, 0u, 0u, 0u);
-
-  f4_t acc[RT];
+  // Loads block b (units 4b..4b+3).  Units past the end re-read the last
+  // unit; the matrix steps of those units are skipped, and the transposes
+  // only move a unit's data into that unit's own step.
+  auto load = [&](MBlock &m, int b) {
+    const int u = min(4 * b + lq, units - 1);
+    const uint32_t e0 = rstart + (uint32_t)u * 32;
+    const uint4 v = *reinterpret_cast<const uint4 *>(vals + (e0 >> 1));
+    const uint2 c = *reinterpret_cast<const uint2 *>(codes + (e0 >> 3));
+    m.v[0] = v.x; m.v[1] = v.y; m.v[2] = v.z; m.v[3] = v.w;
+    m.c[0] = c.x; m.c[1] = c.y;
+    m.s = scales[(uint32_t)arow * ngroups + ((uint32_t)u >> sg_shift)];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  bool first = true;
-  for (int ub = 0; ub < units; ub += kMChunkUnits) {
-    const int ue = min(units, ub + kMChunkUnits);
-    const int nblk = (ue - ub + 3) / 4;
-
-    // first block of this wave in the chunk: issue its weight loads early
-    int blk = wave;
-    uint32_t V[RT][4], C[RT][2];
-    auto load_block = [&](int b) {
-      const int u = ub + 4 * b + lq;
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        if (u < ue) {
-          const uint32_t e0 = rstart[t] + (uint32_t)u * 32;
-          const uint4 v = *reinterpret_cast<const uint4 *>(vals + (e0 >> 1));
-          const uint2 c = *reinterpret_cast<const uint2 *>(codes + (e0 >> 3));
-          V[t][0] = v.x; V[t][1] = v.y; V[t][2] = v.z; V[t][3] = v.w;
-          C[t][0] = c.x; C[t][1] = c.y;
-        } else {
-          V[t][0] = V[t][1] = V[t][2] = V[t][3] = 0x88888888u;  // q = 0
-          C[t][0] = C[t][1] = 0x44444444u;
-        }
-      }
-    };
-    if (blk < nblk) load_block(blk);
-    int32_t rp[RT];
-    if (first) {
-#pragma unroll
-      for (int t = 0; t < RT; ++t) rp[t] = row_ptr[min(row_base + 16 * t + li, rows - 1)];
+    for (int s = 0; s < 4; ++s) {
+      const int uu = min(4 * b + s, units - 1);
+      m.x[2 * s] = *reinterpret_cast<const uint4 *>(xrow + uu * kSegCols);
+      m.x[2 * s + 1] = *reinterpret_cast<const uint4 *>(xrow + uu * kSegCols + 32);
     }
+  };
 
-    __syncthreads();  // the previous chunk is consumed
-    {
-      const int vpb = (ue - ub) * (kSegCols / 8);
-      for (int i = threadIdx.x; i < batch * vpb; i += 64 * kMWaves) {
-        const int b = i / vpb, c = i % vpb;
-        *reinterpret_cast<uint4 *>(xs + b * kMXStride + 8 * c) =
-            *reinterpret_cast<const uint4 *>(x + (int64_t)b * cols + (int64_t)ub * kSegCols + 8 * c);
-      }
-      const int ng = (ue - ub) >> sg_shift, g0 = ub >> sg_shift;
-      for (int i = threadIdx.x; i < RT * 16 * ng; i += 64 * kMWaves) {
-        const int g = i % ng, r = (i / ng) % 16, t = i / (ng * 16);
-        const int row = min(row_base + 16 * t + r, rows - 1);
-        sc[(t * kMChunkUnits + g) * 16 + r] = scales[(uint32_t)row * ngroups + g0 + g];
+  f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto process = [&](const MBlock &m, int b) {
+    uint32_t W0 = m.v[0], W1 = m.v[1], W2 = m.v[2], W3 = m.v[3], P, Q;
+    transpose4(W0, W1, W2, W3);
+    transpose_codes(m.c[0], m.c[1], P, Q);
+    scs[wave][lq][li] = (uint16_t)m.s;  // scale of (row li, unit 4b+lq)
+    f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int u = 4 * b + s;
+      if (u >= units) break;
+      const u8_t xv = {m.x[2 * s].x, m.x[2 * s].y, m.x[2 * s].z, m.x[2 * s].w,
+                       m.x[2 * s + 1].x, m.x[2 * s + 1].y, m.x[2 * s + 1].z, m.x[2 * s + 1].w};
+      const h16_t bx = __builtin_bit_cast(h16_t, xv);
+      if (s == 0) cg = smfmac_step<0>(W0, bx, cg, P, Q);
+      if (s == 1) cg = smfmac_step<1>(W1, bx, cg, P, Q);
+      if (s == 2) cg = smfmac_step<2>(W2, bx, cg, P, Q);
+      if (s == 3) cg = smfmac_step<3>(W3, bx, cg, P, Q);
+      if (((u + 1) & (sg - 1)) == 0) {  // the group ends with this unit
+        const uint2 sv = *reinterpret_cast<const uint2 *>(&scs[wave][s][4 * lq]);
+        acc[0] = fmaf(fp16_bits_to_float(sv.x & 0xFFFFu), cg[0], acc[0]);
+        acc[1] = fmaf(fp16_bits_to_float(sv.x >> 16), cg[1], acc[1]);
+        acc[2] = fmaf(fp16_bits_to_float(sv.y & 0xFFFFu), cg[2], acc[2]);
+        acc[3] = fmaf(fp16_bits_to_float(sv.y >> 16), cg[3], acc[3]);
+        cg = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
-    __syncthreads();
+  };
 
-    if (first) {
-      first = false;
-      // row_ptr check: a row stored elsewhere is re-fetched from there
-      bool moved = false;
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        if ((uint32_t)rp[t] != rstart[t]) { rstart[t] = (uint32_t)rp[t]; moved = true; }
-      }
-      if (moved && blk < nblk) load_block(blk);
-    }
-
-    for (; blk < nblk; blk += kMWaves) {
-      // this block's words and codes, transposed so lane-row q holds word q of each unit
-      uint32_t W[RT][4], P[RT], Q[RT];
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        W[t][0] = V[t][0]; W[t][1] = V[t][1]; W[t][2] = V[t][2]; W[t][3] = V[t][3];
-        transpose4(W[t][0], W[t][1], W[t][2], W[t][3]);
-        transpose_codes(C[t][0], C[t][1], P[t], Q[t]);
-      }
-      const int u4 = ub + 4 * blk;
-      if (blk + kMWaves < nblk) load_block(blk + kMWaves);  // prefetch
-
-      f4_t cg[RT];
-#pragma unroll
-      for (int t = 0; t < RT; ++t) cg[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int u = u4 + s;
-        if (u >= ue) break;
-        const uint16_t *xb = xs + li * kMXStride + (u - ub) * kSegCols + 8 * lq;
-        const uint4 xa = *reinterpret_cast<const uint4 *>(xb);
-        const uint4 xc = *reinterpret_cast<const uint4 *>(xb + 32);
-        const u8_t xv = {xa.x, xa.y, xa.z, xa.w, xc.x, xc.y, xc.z, xc.w};
-        const h16_t bx = __builtin_bit_cast(h16_t, xv);
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          if (s == 0) cg[t] = smfmac_step<0>(W[t][0], bx, cg[t], P[t], Q[t]);
-          if (s == 1) cg[t] = smfmac_step<1>(W[t][1], bx, cg[t], P[t], Q[t]);
-          if (s == 2) cg[t] = smfmac_step<2>(W[t][2], bx, cg[t], P[t], Q[t]);
-          if (s == 3) cg[t] = smfmac_step<3>(W[t][3], bx, cg[t], P[t], Q[t]);
-        }
-        if (((u + 1) & (sg - 1)) == 0) {  // the group ends with this unit
-          const int g = (u >> sg_shift) - (ub >> sg_shift);
-#pragma unroll
-          for (int t = 0; t < RT; ++t) {
-            const uint2 sv = *reinterpret_cast<const uint2 *>(sc + (t * kMChunkUnits + g) * 16 + 4 * lq);
-            acc[t][0] = fmaf(fp16_bits_to_float(sv.x & 0xFFFFu), cg[t][0], acc[t][0]);
-            acc[t][1] = fmaf(fp16_bits_to_float(sv.x >> 16), cg[t][1], acc[t][1]);
-            acc[t][2] = fmaf(fp16_bits_to_float(sv.y & 0xFFFFu), cg[t][2], acc[t][2]);
-            acc[t][3] = fmaf(fp16_bits_to_float(sv.y >> 16), cg[t][3], acc[t][3]);
-            cg[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          }
-        }
-      }
+  int b = wave;
+  MBlock ma, mb;
+  if (b < nblk) {
+    load(ma, b);
+    const int32_t rp = row_ptr[arow];
+    if ((uint32_t)rp != rstart) {  // a row stored elsewhere: re-fetch from row_ptr's offset
+      rstart = (uint32_t)rp;
+      load(ma, b);
     }
   }
+  // two register sets in turn: the next block loads while the current runs
+  while (b < nblk) {
+    if (b + kMWaves < nblk) load(mb, b + kMWaves);
+    process(ma, b);
+    b += kMWaves;
+    if (b >= nblk) break;
+    if (b + kMWaves < nblk) load(ma, b + kMWaves);
+    process(mb, b);
+    b += kMWaves;
+  }
 
-  // sum the 4 waves' partial tiles (LDS reused) and store
-  __syncthreads();
-  float *red = reinterpret_cast<float *>(lds);  // [wave][t][4][64]
+  // sum the partial tiles of the 8 waves and store
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[((wave * RT + t) * 4 + r) * 64 + lane] = acc[t][r];
+  for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
   __syncthreads();
-  for (int o = threadIdx.x; o < RT * 4 * 64; o += 64 * kMWaves) {
-    const int l = o % 64, r = (o / 64) % 4, t = o / 256;
+  if (threadIdx.x < 256) {
+    const int l = threadIdx.x % 64, r = threadIdx.x / 64;
     float v = 0.0f;
 #pragma unroll
-    for (int wv = 0; wv < kMWaves; ++wv) v += red[((wv * RT + t) * 4 + r) * 64 + l];
-    const int j = l % 16, row = row_base + 16 * t + 4 * (l / 16) + r;
+    for (int wv = 0; wv < kMWaves; ++wv) v += red[wv][r][l];
+    const int j = l % 16, row = row0 + 4 * (l / 16) + r;
     if (j < batch && row < rows) y[(int64_t)j * rows + row] = (uint16_t)float_to_fp16_bits(v);
   }
 }
@@ -795,14 +759,11 @@ int b1_rows_per_wave(int rows) {
   return rows > 8192 ? 2 : 1;
 }
 
-template <int RT>
 hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                          hipStream_t stream) {
-  const size_t lds = (size_t)kMXBytes + (size_t)RT * kMChunkUnits * 16 * 2;
-  const int rows_per_block = 16 * RT;
-  const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kMWaves);
-  hipLaunchKernelGGL((gemv_smfmac_kernel<RT>), grid, block, lds, stream, w.rows, w.cols, w.group_size,
-                     w.row_ptr, w.vals, w.codes, w.scales, x, batch, y);
+  const dim3 grid((unsigned)((w.rows + 15) / 16)), block(64 * kMWaves);
+  hipLaunchKernelGGL(gemv_smfmac_kernel, grid, block, 0, stream, w.rows, w.cols, w.group_size, w.row_ptr,
+                     w.vals, w.codes, w.scales, x, batch, y);
   return hipGetLastError();
 }
 
@@ -820,8 +781,7 @@ template <int NK>
 hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                      hipStream_t stream) {
   if (NK == 2 && batch >= 2 && smfmac_enabled()) {
-    const int tiles = (w.rows + 15) / 16;
-    return tiles >= 512 ? launch_smfmac<2>(w, x, batch, y, stream) : launch_smfmac<1>(w, x, batch, y, stream);
+    return launch_smfmac(w, x, batch, y, stream);
   }
   if (batch <= 1) {
     if constexpr (NK == 2 || NK == 4) {
