@@ -1,6 +1,6 @@
 """Benchmark of the packed INT4 2-bit-CSR SparseGEMV on one MI355X.
 
-One step = one ``i4s_run`` call (the whole per-call hot path: stage x, stream
+One step = one ``i4s_run_ws`` call (the whole per-call hot path: stage x, stream
 the packed weights, decode, multiply-accumulate, reduce, store y) over one
 batch of synthetic input.  The layer is packed once beforehand (packing is
 offline work); its time is reported separately as ``pack_ms``.
@@ -97,32 +97,40 @@ class Runner:
                                    p.codes.clone() if p.codes is not None else None, p.scales.clone())
 
     def calls(self, items):
-        """items: list of (packed, x tensor, y tensor, batch) -> list of ctypes call argument tuples."""
-        out = []
+        """items: list of (packed, x tensor, y tensor, batch) -> list of i4s_run_ws argument tuples.
+
+        Calls that can use a workspace share one zero-filled buffer (they run
+        in order on one stream, and each leaves it zero-filled)."""
+        out, need = [], 0
         for p, x, y, b in items:
             d = p.descriptor()
             self.keep.append(d)
-            out.append((ctypes.byref(d), x.data_ptr(), b, y.data_ptr()))
-        return out
+            n = ctypes.c_uint64()
+            self.B.check(self.B.i4s_run_workspace_size(d, b, n), "i4s_run_workspace_size")
+            need = max(need, n.value)
+            out.append([ctypes.byref(d), x.data_ptr(), b, y.data_ptr(), n.value])
+        ws = self.torch.zeros(max(need, 256), dtype=self.torch.uint8, device=self.dev)
+        self.keep.append(ws)
+        return [(d, xp, b, yp, ws.data_ptr() if n else None, ws.numel()) for d, xp, b, yp, n in out]
 
     def timed(self, seq, steps, warmup, trials):
         """Median (wall ms per step, event ms per step) over trials; seq is visited round-robin."""
         import numpy as np
-        torch, run = self.torch, self.lib.i4s_run
+        torch, run = self.torch, self.lib.i4s_run_ws
         walls, evs = [], []
         if self.args.eager:
             sh = self.stream.cuda_stream
             for i in range(warmup):
-                d, xp, b, yp = seq[i % len(seq)]
-                assert run(d, xp, b, yp, sh) == 0
+                d, xp, b, yp, wp, wn = seq[i % len(seq)]
+                assert run(d, xp, b, yp, wp, wn, sh) == 0
             for _ in range(trials):
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 t = time.perf_counter()
                 e0.record(self.stream)
                 for i in range(steps):
-                    d, xp, b, yp = seq[i % len(seq)]
-                    run(d, xp, b, yp, sh)
+                    d, xp, b, yp, wp, wn = seq[i % len(seq)]
+                    run(d, xp, b, yp, wp, wn, sh)
                 e1.record(self.stream)
                 torch.cuda.synchronize()
                 walls.append((time.perf_counter() - t) * 1e3 / steps)
@@ -135,8 +143,8 @@ class Runner:
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=cap):
                 for i in range(n):
-                    d, xp, b, yp = seq[i % len(seq)]
-                    st = run(d, xp, b, yp, cap.cuda_stream)
+                    d, xp, b, yp, wp, wn = seq[i % len(seq)]
+                    st = run(d, xp, b, yp, wp, wn, cap.cuda_stream)
                     if st != 0:
                         raise self.B.I4SError(st, "i4s_run")
             graphs.append(g)

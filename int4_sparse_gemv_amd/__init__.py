@@ -14,14 +14,17 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 from typing import Dict, Optional
 
+import ctypes
+
 from . import _binding as B
 from ._binding import (  # noqa: F401  (the C names)
     I4SError, i4s_format_version, i4s_last_error, i4s_pack, i4s_pack_sizes, i4s_run,
-    i4s_status_string, i4s_version,
+    i4s_run_workspace_size, i4s_run_ws, i4s_status_string, i4s_version,
 )
 
-__all__ = ["PackedWeight", "pack", "run", "pack_sizes", "I4SError", "i4s_pack_sizes", "i4s_pack",
-           "i4s_run", "i4s_status_string", "i4s_last_error", "i4s_version", "i4s_format_version"]
+__all__ = ["PackedWeight", "pack", "run", "pack_sizes", "run_workspace_size", "I4SError",
+           "i4s_pack_sizes", "i4s_pack", "i4s_run", "i4s_run_workspace_size", "i4s_run_ws",
+           "i4s_status_string", "i4s_last_error", "i4s_version", "i4s_format_version"]
 
 
 def _torch():
@@ -109,8 +112,36 @@ def pack(w, n_keep: int = 2, group_size: int = 128) -> PackedWeight:
     return PackedWeight(rows, cols, n_keep, g, row_ptr, vals, codes, scales, sse)
 
 
-def run(p: PackedWeight, x, out=None, descriptor: Optional[B.i4s_packed] = None):
-    """y = W_hat x for x of shape [batch][cols] (or [cols]) fp16 on the GPU."""
+def run_workspace_size(p: PackedWeight, batch: int) -> int:
+    n = ctypes.c_uint64()
+    B.check(B.i4s_run_workspace_size(p.descriptor(), batch, n), "i4s_run_workspace_size")
+    return n.value
+
+
+# One zero-filled workspace per (device, stream), grown on demand.  Calls on
+# one stream are ordered, and every completed call leaves the workspace
+# zero-filled again, so it can be reused by the next call on that stream.
+_WORKSPACES: Dict[tuple, object] = {}
+
+
+def _workspace(device, stream_handle: int, nbytes: int):
+    torch = _torch()
+    key = (device.index, stream_handle)
+    t = _WORKSPACES.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = t
+    return t
+
+
+def run(p: PackedWeight, x, out=None, descriptor: Optional[B.i4s_packed] = None, workspace=None,
+        use_workspace: bool = True):
+    """y = W_hat x for x of shape [batch][cols] (or [cols]) fp16 on the GPU.
+
+    With ``use_workspace`` (the default) calls that can use one go through
+    ``i4s_run_ws`` with ``workspace`` (a zero-filled uint8 tensor) or a
+    cached per-stream workspace; otherwise through ``i4s_run``.
+    """
     torch = _torch()
     squeeze = x.dim() == 1
     if squeeze:
@@ -122,5 +153,16 @@ def run(p: PackedWeight, x, out=None, descriptor: Optional[B.i4s_packed] = None)
     if out is None:
         out = torch.empty(batch, p.rows, dtype=torch.float16, device=x.device)
     d = descriptor if descriptor is not None else p.descriptor()
-    B.check(B.i4s_run(d, x.data_ptr(), batch, out.data_ptr(), _stream_handle(x.device)), "i4s_run")
+    stream = _stream_handle(x.device)
+    nbytes = 0
+    if use_workspace:
+        n = ctypes.c_uint64()
+        B.check(B.i4s_run_workspace_size(d, batch, n), "i4s_run_workspace_size")
+        nbytes = n.value
+    if nbytes:
+        ws = workspace if workspace is not None else _workspace(x.device, stream, nbytes)
+        B.check(B.i4s_run_ws(d, x.data_ptr(), batch, out.data_ptr(), ws.data_ptr(), ws.numel(), stream),
+                "i4s_run_ws")
+    else:
+        B.check(B.i4s_run(d, x.data_ptr(), batch, out.data_ptr(), stream), "i4s_run")
     return out[0] if squeeze else out

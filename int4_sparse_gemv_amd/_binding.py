@@ -69,6 +69,10 @@ SIGNATURES = {
                                 ctypes.c_void_p]),
     "i4s_run": (ctypes.c_int, [ctypes.POINTER(i4s_packed), ctypes.c_void_p, ctypes.c_int32,
                                ctypes.c_void_p, ctypes.c_void_p]),
+    "i4s_run_workspace_size": (ctypes.c_int, [ctypes.POINTER(i4s_packed), ctypes.c_int32,
+                                              ctypes.POINTER(ctypes.c_uint64)]),
+    "i4s_run_ws": (ctypes.c_int, [ctypes.POINTER(i4s_packed), ctypes.c_void_p, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
     "i4s_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "i4s_last_error": (ctypes.c_char_p, []),
     "i4s_version": (ctypes.c_int32, []),
@@ -121,6 +125,14 @@ def i4s_pack(w_ptr, rows, cols, n_keep, group_size, ws_ptr, ws_bytes, inout, rep
 
 def i4s_run(packed, x_ptr, batch, y_ptr, stream):
     return load().i4s_run(ctypes.byref(packed), x_ptr, batch, y_ptr, stream)
+
+
+def i4s_run_workspace_size(packed, batch, out):
+    return load().i4s_run_workspace_size(ctypes.byref(packed), batch, ctypes.byref(out))
+
+
+def i4s_run_ws(packed, x_ptr, batch, y_ptr, ws_ptr, ws_bytes, stream):
+    return load().i4s_run_ws(ctypes.byref(packed), x_ptr, batch, y_ptr, ws_ptr, ws_bytes, stream)
 
 
 def i4s_status_string(status):

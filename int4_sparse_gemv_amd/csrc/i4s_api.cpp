@@ -176,8 +176,12 @@ i4s_status i4s_pack(const uint16_t *w_fp16, int32_t rows, int32_t cols, int32_t 
   return I4S_OK;
 }
 
-i4s_status i4s_run(const i4s_packed *w, const uint16_t *x_fp16, int32_t batch, uint16_t *y_fp16,
-                   void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by i4s_run, i4s_run_ws and i4s_run_workspace_size.
+i4s_status validate_layer(const i4s_packed *w, int32_t batch) {
   if (!w) return fail(I4S_ERR_INVALID_ARGUMENT, "w is NULL");
   i4s_status st = check_shape(w->rows, w->cols, w->n_keep, w->group_size, false);
   if (st != I4S_OK) return st;
@@ -185,13 +189,20 @@ i4s_status i4s_run(const i4s_packed *w, const uint16_t *x_fp16, int32_t batch, u
   if (w->nnz != nnz)
     return fail(I4S_ERR_INVALID_ARGUMENT, "nnz=%lld does not match rows*cols*n_keep/4=%lld",
                 (long long)w->nnz, (long long)nnz);
+  if (batch < 1 || batch > I4S_MAX_BATCH)
+    return fail(I4S_ERR_INVALID_ARGUMENT, "batch=%d must be in [1, %d]", batch, I4S_MAX_BATCH);
+  return I4S_OK;
+}
+
+i4s_status validate_run(const i4s_packed *w, const uint16_t *x_fp16, int32_t batch, const uint16_t *y_fp16) {
+  i4s_status st = validate_layer(w, batch);
+  if (st != I4S_OK) return st;
+  const int64_t nnz = w->nnz;
   if (!w->row_ptr || !aligned(w->row_ptr, 4) || !w->vals || !aligned(w->vals, 16) || !w->scales ||
       !aligned(w->scales, 2))
     return fail(I4S_ERR_INVALID_ARGUMENT, "row_ptr/vals/scales NULL or misaligned (need 4/16/2 bytes)");
   if (w->n_keep < 4 && (!w->codes || !aligned(w->codes, 8)))
     return fail(I4S_ERR_INVALID_ARGUMENT, "codes NULL or not 8-byte aligned");
-  if (batch < 1 || batch > I4S_MAX_BATCH)
-    return fail(I4S_ERR_INVALID_ARGUMENT, "batch=%d must be in [1, %d]", batch, I4S_MAX_BATCH);
   if (!x_fp16 || !aligned(x_fp16, 16)) return fail(I4S_ERR_INVALID_ARGUMENT, "x is NULL or not 16-byte aligned");
   if (!y_fp16 || !aligned(y_fp16, 2)) return fail(I4S_ERR_INVALID_ARGUMENT, "y is NULL or not 2-byte aligned");
   const uint64_t xb = 2ull * batch * w->cols, yb = 2ull * batch * w->rows;
@@ -201,9 +212,51 @@ i4s_status i4s_run(const i4s_packed *w, const uint16_t *x_fp16, int32_t batch, u
       overlap(y_fp16, yb, w->row_ptr, 4ull * (w->rows + 1)) ||
       (w->n_keep < 4 && overlap(y_fp16, yb, w->codes, (uint64_t)nnz / 4)))
     return fail(I4S_ERR_INVALID_ARGUMENT, "y overlaps a packed weight buffer");
+  return I4S_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+i4s_status i4s_run(const i4s_packed *w, const uint16_t *x_fp16, int32_t batch, uint16_t *y_fp16,
+                   void *stream) {
+  i4s_status st = validate_run(w, x_fp16, batch, y_fp16);
+  if (st != I4S_OK) return st;
   st = check_device();
   if (st != I4S_OK) return st;
   const hipError_t e = i4s::launch_gemv(*w, x_fp16, batch, y_fp16, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "gemv launch");
+  return I4S_OK;
+}
+
+i4s_status i4s_run_workspace_size(const i4s_packed *w, int32_t batch, uint64_t *bytes) {
+  if (!bytes) return fail(I4S_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  const i4s_status st = validate_layer(w, batch);
+  if (st != I4S_OK) return st;
+  *bytes = i4s::split_plan(*w, batch).workspace_bytes;
+  return I4S_OK;
+}
+
+i4s_status i4s_run_ws(const i4s_packed *w, const uint16_t *x_fp16, int32_t batch, uint16_t *y_fp16,
+                      void *workspace, uint64_t workspace_bytes, void *stream) {
+  i4s_status st = validate_run(w, x_fp16, batch, y_fp16);
+  if (st != I4S_OK) return st;
+  const i4s::SplitPlan plan = i4s::split_plan(*w, batch);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || !aligned(workspace, 16))
+      return fail(I4S_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
+    if (workspace_bytes < plan.workspace_bytes)
+      return fail(I4S_ERR_WORKSPACE_TOO_SMALL, "workspace has %llu bytes, %llu needed",
+                  (unsigned long long)workspace_bytes, (unsigned long long)plan.workspace_bytes);
+    const uint64_t xb = 2ull * batch * w->cols, yb = 2ull * batch * w->rows;
+    if (overlap(workspace, workspace_bytes, x_fp16, xb) || overlap(workspace, workspace_bytes, y_fp16, yb))
+      return fail(I4S_ERR_INVALID_ARGUMENT, "workspace overlaps x or y");
+  }
+  st = check_device();
+  if (st != I4S_OK) return st;
+  const hipError_t e = i4s::launch_gemv_ws(*w, x_fp16, batch, y_fp16, plan, workspace,
+                                           reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "gemv launch");
   return I4S_OK;
 }

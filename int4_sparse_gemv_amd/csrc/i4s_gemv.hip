@@ -713,6 +713,167 @@ __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// batch kernel on the sparse matrix cores with a K split across blocks
+//
+// Same matrix-core step as above, but a block owns 128 rows (8 waves x one
+// 16-row tile) and one slice of K.  The slice of x (batch vectors x the
+// slice's columns) is staged once in LDS and shared by the 8 tiles, so the
+// activations cross from L2 once per 128 rows instead of once per 16.  Each
+// block writes its 8 partial fp32 tiles to the caller's workspace; the block
+// that finishes a row group last (a per-group counter in the workspace) sums
+// the slices in slice order -- the result does not depend on which block is
+// last -- stores y and resets the counter to zero for the next call.
+
+constexpr int kSWaves = 8;              // tiles (waves) per block
+constexpr int kSRows = 16 * kSWaves;    // rows per block
+constexpr int kSMaxBlocks = 8;          // blocks of 4 units per slice (all loaded up front)
+
+// Weight registers of one block of 4 units for one lane.
+struct WBlock {
+  uint32_t v[4];
+  uint32_t c[2];
+  uint32_t s;
+};
+
+__global__ __launch_bounds__(64 * kSWaves) void gemv_smfmac_split_kernel(
+    int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
+    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
+    uint16_t *__restrict__ y, uint32_t *__restrict__ counters, f4_t *__restrict__ partial,
+    int ksplit, int ups) {
+  extern __shared__ __align__(16) uint16_t xs[];          // [batch][ups * 64 + 8]
+  __shared__ __align__(16) uint16_t scs[kSWaves][4][16];
+  __shared__ int last_block;
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  const int li = lane % 16, lq = lane / 16;
+  const int rg = blockIdx.x, ks = blockIdx.y, ngrp = gridDim.x;
+  const int row0 = rg * kSRows + 16 * wave;
+  const int units = cols / kSegCols;
+  const int u0 = ks * ups, u1 = min(units, u0 + ups);
+  const int xst = ups * kSegCols + 8;  // halfs per vector in LDS (16-byte pad)
+  const uint32_t nnz_row = (uint32_t)cols / 2;
+  const int sg = group_size / kSegCols;
+  const int sg_shift = sg == 1 ? 0 : (sg == 2 ? 1 : 2);
+  const uint32_t ngroups = (uint32_t)(cols / group_size);
+
+  const int arow = min(row0 + li, rows - 1);
+  uint32_t rstart = (uint32_t)arow * nnz_row;
+  // B lane (vector li, column quarter lq); lanes past `batch` read the last
+  // real vector (their output columns are never stored)
+  const uint16_t *xl = xs + min(li, batch - 1) * xst + 8 * lq;
+
+  auto load = [&](WBlock &m, int b) {  // weights of block b (units 4b..4b+3) of this tile
+    const int u = min(4 * b + lq, u1 - 1);
+    const uint32_t e0 = rstart + (uint32_t)u * 32;
+    const uint4 v = *reinterpret_cast<const uint4 *>(vals + (e0 >> 1));
+    const uint2 c = *reinterpret_cast<const uint2 *>(codes + (e0 >> 3));
+    m.v[0] = v.x; m.v[1] = v.y; m.v[2] = v.z; m.v[3] = v.w;
+    m.c[0] = c.x; m.c[1] = c.y;
+    m.s = scales[(uint32_t)arow * ngroups + ((uint32_t)u >> sg_shift)];
+  };
+
+  f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto process = [&](const WBlock &m, int b) {
+    uint32_t W0 = m.v[0], W1 = m.v[1], W2 = m.v[2], W3 = m.v[3], P, Q;
+    transpose4(W0, W1, W2, W3);
+    transpose_codes(m.c[0], m.c[1], P, Q);
+    scs[wave][lq][li] = (uint16_t)m.s;
+    f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int u = 4 * b + s;
+      if (u >= u1) break;
+      const uint4 xa = *reinterpret_cast<const uint4 *>(xl + (u - u0) * kSegCols);
+      const uint4 xc = *reinterpret_cast<const uint4 *>(xl + (u - u0) * kSegCols + 32);
+      const u8_t xv = {xa.x, xa.y, xa.z, xa.w, xc.x, xc.y, xc.z, xc.w};
+      const h16_t bx = __builtin_bit_cast(h16_t, xv);
+      if (s == 0) cg = smfmac_step<0>(W0, bx, cg, P, Q);
+      if (s == 1) cg = smfmac_step<1>(W1, bx, cg, P, Q);
+      if (s == 2) cg = smfmac_step<2>(W2, bx, cg, P, Q);
+      if (s == 3) cg = smfmac_step<3>(W3, bx, cg, P, Q);
+      if (((u + 1) & (sg - 1)) == 0) {
+        const uint2 sv = *reinterpret_cast<const uint2 *>(&scs[wave][s][4 * lq]);
+        acc[0] = fmaf(fp16_bits_to_float(sv.x & 0xFFFFu), cg[0], acc[0]);
+        acc[1] = fmaf(fp16_bits_to_float(sv.x >> 16), cg[1], acc[1]);
+        acc[2] = fmaf(fp16_bits_to_float(sv.y & 0xFFFFu), cg[2], acc[2]);
+        acc[3] = fmaf(fp16_bits_to_float(sv.y >> 16), cg[3], acc[3]);
+        cg = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+  };
+
+  // All of this tile's weights for the slice are requested at once, before
+  // the activations are staged, so the memory latency is paid once.
+  const int b0 = u0 / 4, nb = (u1 + 3) / 4 - b0;  // nb <= kSMaxBlocks
+  WBlock mw[kSMaxBlocks];
+#pragma unroll
+  for (int i = 0; i < kSMaxBlocks; ++i)
+    if (i < nb) load(mw[i], b0 + i);
+  const int32_t rp = row_ptr[arow];
+  {
+    const int vpb = (u1 - u0) * (kSegCols / 8);  // uint4 per vector
+    for (int i = threadIdx.x; i < batch * vpb; i += 64 * kSWaves) {
+      const int bv = i / vpb, c = i % vpb;
+      *reinterpret_cast<uint4 *>(xs + bv * xst + 8 * c) =
+          *reinterpret_cast<const uint4 *>(x + (int64_t)bv * cols + (int64_t)u0 * kSegCols + 8 * c);
+    }
+  }
+  if ((uint32_t)rp != rstart) {  // a row stored elsewhere: re-fetch from row_ptr's offset
+    rstart = (uint32_t)rp;
+#pragma unroll
+    for (int i = 0; i < kSMaxBlocks; ++i)
+      if (i < nb) load(mw[i], b0 + i);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSMaxBlocks; ++i)
+    if (i < nb) process(mw[i], b0 + i);
+
+  if (ksplit == 1) {  // no split: store directly
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 4 * lq + r;
+      if (li < batch && row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(acc[r]);
+    }
+    return;
+  }
+  // Partial tile -> workspace, then the last block of the row group sums.
+  // The 8 XCDs' L2 caches are not coherent with each other, and a device-
+  // scope fence would write back and invalidate the whole L2; instead every
+  // access to the workspace is a device-scope atomic, performed at the
+  // memory-side coherence point, and the counter is bumped only after this
+  // block's partial stores have completed (s_waitcnt on outstanding stores,
+  // then the block barrier).
+  {
+    float *dst = reinterpret_cast<float *>(partial + ((size_t)(ks * ngrp + rg) * kSWaves + wave) * 64 + lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // all of this wave's stores acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_block = old == (uint32_t)(ksplit - 1);
+  }
+  __syncthreads();
+  if (!last_block) return;
+  f4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < ksplit; ++k) {
+    const float *src = reinterpret_cast<const float *>(partial + ((size_t)(k * ngrp + rg) * kSWaves + wave) * 64 + lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sum[r] += __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = row0 + 4 * lq + r;
+    if (li < batch && row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(sum[r]);
+  }
+  if (threadIdx.x == 0)  // ready for the next call
+    __hip_atomic_store(&counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 
 template <int NK, int BT, int RPW>
@@ -767,6 +928,18 @@ hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, 
   return hipGetLastError();
 }
 
+hipError_t launch_smfmac_split(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+                               const SplitPlan &pl, void *workspace, hipStream_t stream) {
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  uint32_t *counters = reinterpret_cast<uint32_t *>(ws);
+  f4_t *partial = reinterpret_cast<f4_t *>(ws + pl.counter_bytes);
+  const size_t lds = (size_t)batch * (pl.ups * kSegCols + 8) * 2;
+  const dim3 grid((unsigned)pl.row_groups, (unsigned)pl.ksplit), block(64 * kSWaves);
+  hipLaunchKernelGGL(gemv_smfmac_split_kernel, grid, block, lds, stream, w.rows, w.cols, w.group_size,
+                     w.row_ptr, w.vals, w.codes, w.scales, x, batch, y, counters, partial, pl.ksplit, pl.ups);
+  return hipGetLastError();
+}
+
 // I4S_BATCH_PATH=valu forces the VALU batch kernel for 2:4 (tuning and
 // cross-checks); read once.
 bool smfmac_enabled() {
@@ -801,6 +974,49 @@ hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint
 }
 
 }  // namespace
+
+SplitPlan split_plan(const i4s_packed &w, int32_t batch) {
+  SplitPlan pl{};
+  if (w.n_keep != 2 || batch < 2) return pl;  // no workspace: the other kernels need none
+  const int units = w.cols / kSegCols;
+  pl.row_groups = (w.rows + kSRows - 1) / kSRows;
+  // activations of one slice must fit the LDS budget (60 KB, leaving room
+  // for the kernel's static LDS under the 64 KB per-block default)
+  int max_ups = ((60 * 1024 / 2) / batch - 8) / kSegCols / 4 * 4;
+  if (max_ups > 4 * kSMaxBlocks) max_ups = 4 * kSMaxBlocks;  // every block's weights in registers
+  if (max_ups < 4) max_ups = 4;
+  // about one block per CU: 256 / row groups slices, at least 4 units each
+  int ks = (256 + pl.row_groups - 1) / pl.row_groups;
+  if (ks > (units + 3) / 4) ks = (units + 3) / 4;
+  if (ks < 1) ks = 1;
+  int ups = ((units + ks - 1) / ks + 3) / 4 * 4;
+  if (ups > max_ups) ups = max_ups;
+  pl.ups = ups;
+  pl.ksplit = (units + ups - 1) / ups;
+  // The split pays for its cross-block reduction (three dependent trips to
+  // the memory-side coherence point, several microseconds) only when the
+  // activations would otherwise cross from L2 once per 16 rows for many rows
+  // or many columns: tall matrices, or wide ones at batch >= 8 (measured on
+  // the 13B-shaped layers).  Otherwise the barrier-free kernel runs and no
+  // workspace is needed.
+  const bool worth_it = pl.row_groups >= 64 || (units >= 128 && batch >= 8);
+  if (!worth_it || pl.row_groups > kSplitMaxRowGroups) return SplitPlan{};
+  if (pl.ksplit > 1) {
+    // The counters sit in a fixed region at the start of every workspace, so
+    // layers of any shape that share a workspace never see each other's
+    // partial tiles as counters; every completed call leaves that region zero.
+    pl.counter_bytes = kSplitCounterBytes;
+    pl.partial_bytes = (size_t)pl.ksplit * pl.row_groups * kSWaves * 64 * sizeof(float) * 4;
+  }
+  pl.workspace_bytes = pl.counter_bytes + pl.partial_bytes;
+  return pl;
+}
+
+hipError_t launch_gemv_ws(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+                          const SplitPlan &pl, void *workspace, hipStream_t stream) {
+  if (pl.ksplit >= 1 && smfmac_enabled()) return launch_smfmac_split(w, x, batch, y, pl, workspace, stream);
+  return launch_gemv(w, x, batch, y, stream);
+}
 
 hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                        hipStream_t stream) {

@@ -33,8 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["i4s_pack_sizes", "i4s_pack", "i4s_run", "i4s_status_string", "i4s_last_error",
-         "i4s_version", "i4s_format_version"])
+        ["i4s_pack_sizes", "i4s_pack", "i4s_run", "i4s_run_workspace_size", "i4s_run_ws",
+         "i4s_status_string", "i4s_last_error", "i4s_version", "i4s_format_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -162,3 +162,29 @@ def test_binding_without_library_fails_loudly(tmp_path):
             B.load(str(tmp_path / "missing.so"))
         finally:
             B._lib = B._lib_saved
+
+
+def test_run_workspace_size_is_host_only_and_planned(lib):
+    n = ctypes.c_uint64()
+    # batch 1 and non-2:4 patterns need no workspace
+    assert B.i4s_run_workspace_size(_desc(4096, 4096, 2, 128), 1, n) == B.I4S_OK and n.value == 0
+    assert B.i4s_run_workspace_size(_desc(4096, 4096, 4, 128), 8, n) == B.I4S_OK and n.value == 0
+    # 2:4 batch: counters (one per 128-row group, 256-byte padded) + fp32 partial tiles
+    assert B.i4s_run_workspace_size(_desc(5120, 13824, 2, 128), 16, n) == B.I4S_OK
+    assert n.value > 16384 and n.value % 256 == 0
+    for batch in (2, 4, 8, 16):
+        assert B.i4s_run_workspace_size(_desc(13824, 5120, 2, 128), batch, n) == B.I4S_OK
+    assert B.i4s_run_workspace_size(_desc(), 0, n) == B.I4S_ERR_INVALID_ARGUMENT
+    assert lib.i4s_run_workspace_size(ctypes.byref(_desc()), 2, None) == B.I4S_ERR_INVALID_ARGUMENT
+
+
+def test_run_ws_validation_fails_before_any_device_call(lib):
+    d = _desc(5120, 13824, 2, 128)
+    n = ctypes.c_uint64()
+    assert B.i4s_run_workspace_size(d, 16, n) == B.I4S_OK
+    x, y, ws = 1 << 34, 1 << 35, 1 << 36
+    assert B.i4s_run_ws(d, x, 16, y, ws, n.value - 1, None) == B.I4S_ERR_WORKSPACE_TOO_SMALL
+    assert B.i4s_run_ws(d, x, 16, y, None, n.value, None) == B.I4S_ERR_INVALID_ARGUMENT
+    assert B.i4s_run_ws(d, x, 16, y, ws + 8, n.value, None) == B.I4S_ERR_INVALID_ARGUMENT
+    assert B.i4s_run_ws(d, x, 16, y, x, n.value, None) == B.I4S_ERR_INVALID_ARGUMENT  # overlaps x
+    assert B.i4s_run_ws(d, x, 17, y, ws, n.value, None) == B.I4S_ERR_INVALID_ARGUMENT

@@ -283,3 +283,71 @@ def test_row_ptr_is_honoured(n_keep, batch):
     q = I.PackedWeight(rows, cols, n_keep, p.group_size, row_ptr, vals, codes, p.scales)
     y1 = gpu_run(q, x16)
     np.testing.assert_array_equal(y0, y1)
+
+
+@pytest.mark.parametrize("rows,cols,batch", [(200, 2048, 3), (5120, 1024, 16), (128, 13824, 16), (777, 4352, 8),
+                                              (8200, 1024, 4), (300, 8192, 8), (8193, 2048, 16)])
+def test_batch_paths_with_and_without_workspace(rows, cols, batch):
+    """i4s_run (no workspace) and i4s_run_ws (K split across blocks where the
+    layer's plan uses it) both meet the tolerance; the workspace path is
+    deterministic across repeated calls."""
+    import int4_sparse_gemv_amd as I
+    rng = np.random.default_rng(rows + batch)
+    w = rand16(rng, (rows, cols))
+    say(f"case batch-paths {rows}x{cols} b{batch}")
+    ref = O.pack(w, 2, 64)
+    p = gpu_pack(w, 2, 64)
+    w_hat = O.reconstruct(ref)
+    x16 = rng.standard_normal((batch, cols)).astype(np.float16)
+    y_ref, a_ref = O.gemv(w_hat, x16)
+    x = torch.from_numpy(x16.view(np.int16)).cuda().view(torch.float16)
+    y_plain = I.run(p, x, use_workspace=False)
+    y_ws1 = I.run(p, x)
+    y_ws2 = I.run(p, x)
+    torch.cuda.synchronize()
+    for y in (y_plain, y_ws1):
+        assert_gemv_close(y.cpu().numpy().astype(np.float64), y_ref, a_ref, f"{rows}x{cols} b{batch}")
+    assert torch.equal(y_ws1, y_ws2)
+
+
+def test_shared_workspace_across_layers_and_graph_replay():
+    """One workspace serves different layers in turn (its counters return to
+    zero after each call), also when the calls are replayed from a graph."""
+    import int4_sparse_gemv_amd as I
+    rng = np.random.default_rng(91)
+    shapes = [(640, 8192), (1536, 1024), (96, 8192), (8320, 512)]
+    packs, xs, refs = [], [], []
+    for r, c in shapes:
+        w = rand16(rng, (r, c))
+        ref = O.pack(w, 2, 128)
+        packs.append(gpu_pack(w, 2, 128))
+        x16 = rng.standard_normal((16, c)).astype(np.float16)
+        xs.append(torch.from_numpy(x16.view(np.int16)).cuda().view(torch.float16))
+        refs.append(O.gemv(O.reconstruct(ref), x16))
+    say("case shared-workspace")
+    need = max(I.run_workspace_size(p, 16) for p in packs)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    outs = [torch.empty(16, r, dtype=torch.float16, device="cuda") for r, _ in shapes]
+    for _ in range(2):
+        for p, x, o in zip(packs, xs, outs):
+            I.run(p, x, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for o, (y_ref, a_ref) in zip(eager, refs):
+        assert_gemv_close(o.cpu().numpy().astype(np.float64), y_ref, a_ref, "shared workspace")
+    assert int(ws[:16384].view(torch.int32).abs().sum()) == 0  # counters back to zero
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        descs = [p.descriptor() for p in packs]
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for p, x, o, d in zip(packs, xs, outs, descs):
+                I.run(p, x, out=o, descriptor=d, workspace=ws)
+    for _ in range(3):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e)
