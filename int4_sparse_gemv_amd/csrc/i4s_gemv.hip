@@ -316,6 +316,164 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// batch-1 kernel for rows of at most 64 * UPL units: every load up front.
+//
+// A wave issues the block's share of the activation loads first, then all of
+// its lanes' weight loads (UPL units per lane, nontemporal: the weights are
+// read once), then the row_ptr reads.  Vector loads retire in issue order, so
+// the LDS write of x -- and the block barrier after it -- waits for the
+// activations only, not for the weight stream; each wave starts computing as
+// soon as its own weights are in, which overlaps the decode with the stream.
+
+// Block barrier that orders LDS only: the fences are restricted to the local
+// address space, so no wave waits here for its outstanding global loads.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int NK>
+__device__ inline void load_unit_nt(UnitRegs<NK> &r, const uint8_t *__restrict__ vals,
+                                    const uint16_t *__restrict__ codes,
+                                    const uint16_t *__restrict__ scales, uint32_t elem0,
+                                    uint32_t scale_idx) {
+  const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(vals + (elem0 >> 1));
+  if constexpr (NK == 1) {
+    const u32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(vp));
+    r.v[0] = a.x; r.v[1] = a.y;
+  } else if constexpr (NK == 2) {
+    const u32x4_t a = __builtin_nontemporal_load(vp);
+    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+  } else {
+    const u32x4_t a = __builtin_nontemporal_load(vp);
+    const u32x4_t b = __builtin_nontemporal_load(vp + 1);
+    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+    r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
+  }
+  if constexpr (NK == 1) {
+    r.c[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + (elem0 >> 3)));
+  } else if constexpr (NK == 2) {
+    const u32x2_t c = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(codes + (elem0 >> 3)));
+    r.c[0] = c.x; r.c[1] = c.y;
+  }
+  r.s = __builtin_nontemporal_load(scales + scale_idx);
+}
+
+template <int NK, int RPW, int UPL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
+    int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
+    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
+    uint16_t *__restrict__ y) {
+  extern __shared__ __align__(16) uint16_t xs[];  // [units][kStrideB1]
+  __shared__ uint32_t lut[16];
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  const int row0 = (blockIdx.x * WAVES + wave) * RPW;
+  const int units = cols / kSegCols;
+  const int nvec = units * (kSegCols / 8);  // uint4 pieces of x
+  const uint32_t nnz_row = (uint32_t)cols / 4 * NK;
+  const int sg_shift = group_size == 64 ? 0 : (group_size == 128 ? 1 : 2);  // log2(G / 64)
+  const uint32_t ngroups = (uint32_t)(cols / group_size);
+
+  // 1. activations (nvec <= 64 * WAVES * UPL, so UPL pieces per thread cover
+  // them).  Every load below is unconditional, at a clamped index, so the
+  // wait before the LDS write counts exactly the loads issued after it.
+  uint4 xg[UPL];
+  int xi[UPL];
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    xi[j] = min((int)threadIdx.x + j * 64 * WAVES, nvec - 1);
+    xg[j] = reinterpret_cast<const uint4 *>(x)[xi[j]];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. weights: rows past the end re-read the last row (never stored)
+  uint32_t rstart[RPW], srow[RPW];
+  bool rvalid[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    rvalid[r] = row0 + r < rows;
+    const int rr = min(row0 + r, rows - 1);
+    rstart[r] = (uint32_t)rr * nnz_row;
+    srow[r] = (uint32_t)rr * ngroups;
+  }
+  UnitRegs<NK> wr[UPL][RPW];
+#pragma unroll
+  for (int k = 0; k < UPL; ++k) {
+    const int u = min(lane + 64 * k, units - 1);  // lanes past the row re-read its last unit
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      load_unit_nt<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                       srow[r] + ((uint32_t)u >> sg_shift));
+  }
+  int32_t rp[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) rp[r] = row_ptr[min(row0 + r, rows - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. stage x in LDS (threads with a clamped index write the same piece
+  // to the same place again)
+#pragma unroll
+  for (int j = 0; j < UPL; ++j)
+    *reinterpret_cast<uint4 *>(xs + (xi[j] >> 3) * kStrideB1 + 8 * (xi[j] & 7)) = xg[j];
+  if (NK == 2 && threadIdx.x < 16) init_selector_table(lut);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 4. row_ptr check (wave-uniform): re-fetch rows stored elsewhere
+  bool moved = false;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) moved |= (uint32_t)rp[r] != rstart[r];
+  if (moved) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      rstart[r] = (uint32_t)rp[r];
+#pragma unroll
+      for (int k = 0; k < UPL; ++k) {
+        const int u = min(lane + 64 * k, units - 1);
+        load_unit<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                      srow[r] + ((uint32_t)u >> sg_shift));
+      }
+    }
+  }
+
+  // 5. decode and accumulate
+  float acc[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < UPL; ++k) {
+    const int u = lane + 64 * k;
+    if (u < units) {
+      uint32_t xr[32];
+      const uint4 *xv = reinterpret_cast<const uint4 *>(xs + u * kStrideB1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 t = xv[i];
+        xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float gsum = unit_dot_b1<NK>(wr[k][r], xr, lut);
+        acc[r] = fmaf(fp16_bits_to_float(wr[k][r].s), gsum, acc[r]);
+      }
+    }
+  }
+
+  // 6. reduce and store
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float t = wave_sum(acc[r]);
+    if (lane == 0 && rvalid[r]) y[row0 + r] = (uint16_t)float_to_fp16_bits(t);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // batch kernel (any N, 1 <= batch <= 16)
 
 // Accumulate one unit of RPW rows into acc[r][b].  xs points at the LDS copy
@@ -893,9 +1051,38 @@ hipError_t launch_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint1
 // Batch-1 kernel: 8 waves per block (512 threads), RPW rows per wave.
 constexpr int kB1Waves = 8;
 
+template <int NK, int RPW, int UPL>
+hipError_t launch_b1_direct(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  const int units = w.cols / kSegCols;
+  const size_t lds = (size_t)units * kStrideB1 * 2;
+  const int rows_per_block = kB1Waves * RPW;
+  const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kB1Waves);
+  hipLaunchKernelGGL((gemv_b1_direct_kernel<NK, RPW, UPL, kB1Waves>), grid, block, lds, stream, w.rows,
+                     w.cols, w.group_size, w.row_ptr, w.vals, w.codes, w.scales, x, y);
+  return hipGetLastError();
+}
+
+// I4S_B1_KERNEL=stream forces the pipelined batch-1 kernel (tuning); read once.
+bool b1_direct_enabled() {
+  static const bool v = [] {
+    const char *e = getenv("I4S_B1_KERNEL");
+    return !(e && e[0] == 's');
+  }();
+  return v;
+}
+
 template <int NK, int RPW>
 hipError_t launch_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
   const int units = w.cols / kSegCols;
+  if (b1_direct_enabled()) {
+    switch ((units + 63) / 64) {
+      case 1: return launch_b1_direct<NK, RPW, 1>(w, x, y, stream);
+      case 2: return launch_b1_direct<NK, RPW, 2>(w, x, y, stream);
+      case 3: return launch_b1_direct<NK, RPW, 3>(w, x, y, stream);
+      case 4: return launch_b1_direct<NK, RPW, 4>(w, x, y, stream);
+      default: break;  // longer rows: the pipelined kernel
+    }
+  }
   int kc = kLdsBudget / (kStrideB1 * 2);
   if (kc > units) kc = units;
   const size_t lds = (size_t)kc * kStrideB1 * 2;
