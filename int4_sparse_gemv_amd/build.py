@@ -30,6 +30,10 @@ HIPCC_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # keep packed-fp32 VALU forms out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 16 kernel-argument dwords arrive in SGPRs at wave start, so
+    # the GEMV's first loads do not wait for a scalar memory round trip (the
+    # code object keeps a fallback that loads them itself)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
 ]
 

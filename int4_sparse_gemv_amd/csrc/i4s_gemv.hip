@@ -320,10 +320,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
 //
 // A wave issues the block's share of the activation loads first, then all of
 // its lanes' weight loads (UPL units per lane, nontemporal: the weights are
-// read once), then the row_ptr reads.  Vector loads retire in issue order, so
-// the LDS write of x -- and the block barrier after it -- waits for the
-// activations only, not for the weight stream; each wave starts computing as
-// soon as its own weights are in, which overlaps the decode with the stream.
+// read once).  Vector loads retire in issue order, so the LDS write of x --
+// and the block barrier after it -- waits for the activations only, not for
+// the weight stream; each wave starts computing as soon as its own weights
+// are in, which overlaps the decode with the stream.
 
 // Block barrier that orders LDS only: the fences are restricted to the local
 // address space, so no wave waits here for its outstanding global loads.
@@ -363,9 +363,11 @@ __device__ inline void load_unit_nt(UnitRegs<NK> &r, const uint8_t *__restrict__
   r.s = __builtin_nontemporal_load(scales + scale_idx);
 }
 
+// units = K / 64; sg_shift = log2(G / 64).  Shapes arrive pre-divided so the
+// prologue before the first load is a handful of scalar shifts.
 template <int NK, int RPW, int UPL, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
-    int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
+    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
     uint16_t *__restrict__ y) {
@@ -374,11 +376,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
   const int row0 = (blockIdx.x * WAVES + wave) * RPW;
-  const int units = cols / kSegCols;
   const int nvec = units * (kSegCols / 8);  // uint4 pieces of x
-  const uint32_t nnz_row = (uint32_t)cols / 4 * NK;
-  const int sg_shift = group_size == 64 ? 0 : (group_size == 128 ? 1 : 2);  // log2(G / 64)
-  const uint32_t ngroups = (uint32_t)(cols / group_size);
+  const uint32_t nnz_row = (uint32_t)units * 16 * NK;
+  const uint32_t ngroups = (uint32_t)units >> sg_shift;
 
   // 1. activations (nvec <= 64 * WAVES * UPL, so UPL pieces per thread cover
   // them).  Every load below is unconditional, at a clamped index, so the
@@ -411,6 +411,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
       load_unit_nt<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
                        srow[r] + ((uint32_t)u >> sg_shift));
   }
+  // row_ptr: a vector load, issued last and needed only after decoding.  (A
+  // scalar load would share its counter with LDS and, returning out of
+  // order, hold up the block barrier and the first LDS reads.)
   int32_t rp[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) rp[r] = row_ptr[min(row0 + r, rows - 1)];
@@ -425,11 +428,36 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
-  // 4. row_ptr check (wave-uniform): re-fetch rows stored elsewhere
-  bool moved = false;
+  // 4. decode and accumulate.  The row_ptr check comes after the first pass,
+  // so the common case never waits for row_ptr before decoding; a row stored
+  // away from the format's offset (wave-uniform) is re-fetched and decoded
+  // again.
+  float acc[RPW];
+  for (int pass = 0;; ++pass) {
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) moved |= (uint32_t)rp[r] != rstart[r];
-  if (moved) {
+    for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < UPL; ++k) {
+      const int u = lane + 64 * k;
+      if (u < units) {
+        uint32_t xr[32];
+        const uint4 *xv = reinterpret_cast<const uint4 *>(xs + u * kStrideB1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint4 t = xv[i];
+          xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
+        }
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          const float gsum = unit_dot_b1<NK>(wr[k][r], xr, lut);
+          acc[r] = fmaf(fp16_bits_to_float(wr[k][r].s), gsum, acc[r]);
+        }
+      }
+    }
+    bool moved = false;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) moved |= (uint32_t)rp[r] != rstart[r];
+    if (pass == 1 || !moved) break;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       rstart[r] = (uint32_t)rp[r];
@@ -442,30 +470,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
     }
   }
 
-  // 5. decode and accumulate
-  float acc[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
-#pragma unroll
-  for (int k = 0; k < UPL; ++k) {
-    const int u = lane + 64 * k;
-    if (u < units) {
-      uint32_t xr[32];
-      const uint4 *xv = reinterpret_cast<const uint4 *>(xs + u * kStrideB1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 t = xv[i];
-        xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
-      }
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const float gsum = unit_dot_b1<NK>(wr[k][r], xr, lut);
-        acc[r] = fmaf(fp16_bits_to_float(wr[k][r].s), gsum, acc[r]);
-      }
-    }
-  }
-
-  // 6. reduce and store
+  // 5. reduce and store
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const float t = wave_sum(acc[r]);
@@ -1057,8 +1062,9 @@ hipError_t launch_b1_direct(const i4s_packed &w, const uint16_t *x, uint16_t *y,
   const size_t lds = (size_t)units * kStrideB1 * 2;
   const int rows_per_block = kB1Waves * RPW;
   const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kB1Waves);
+  const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
   hipLaunchKernelGGL((gemv_b1_direct_kernel<NK, RPW, UPL, kB1Waves>), grid, block, lds, stream, w.rows,
-                     w.cols, w.group_size, w.row_ptr, w.vals, w.codes, w.scales, x, y);
+                     units, sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, y);
   return hipGetLastError();
 }
 
