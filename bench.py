@@ -36,7 +36,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD specification
 METRIC = "µs/call and effective HBM GB/s (% of peak) of packed INT4 SparseGEMV, 4096×4096 b=1"
-GEMV_SRC = os.path.join(ROOT, "int4_sparse_gemv_amd", "csrc", "i4s_gemv.hip")
+# the batch-1 kernel's sources: a traffic profile is used only while they are unchanged
+B1_SRCS = [os.path.join(ROOT, "int4_sparse_gemv_amd", "csrc", f) for f in ("i4s_gemv_b1.hip", "i4s_gemv_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_c2_4096.json")
 
 
@@ -56,12 +57,17 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time plain stream launches instead of a graph")
     ap.add_argument("--suite", default=None, help="also measure every workload and write a table here")
     ap.add_argument("--no-stack", action="store_true", help="with --suite: skip the 224-matrix 7B stack")
+    ap.add_argument("--no-floors", action="store_true",
+                    help="skip the read-only and latency floor measurements")
     return ap.parse_args()
 
 
-def sha_of(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def sha_of(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 class Runner:
@@ -186,6 +192,82 @@ class Runner:
             res.append(e0.elapsed_time(e1) * 1e3 / steps)
         return float(np.median(res))
 
+    def floors(self, nbytes, steps=2000, trials=3):
+        """What one launch can reach at this size on this part, timed like the GEMV.
+
+        stream_read_*: a kernel that only reads nbytes once (libi4s_floor.so,
+        one 16-byte load per lane), cold over >= 1.5 GB of copies and hot;
+        load_latency_ns: one lane chasing 4000 dependent loads through a random
+        cycle spread over 2 GiB (one entry per KiB)."""
+        import numpy as np
+        from int4_sparse_gemv_amd import build as BLD
+        torch = self.torch
+        lib = ctypes.CDLL(BLD.FLOOR_LIB)
+        lib.i4sf_stream_read.restype = ctypes.c_int
+        lib.i4sf_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+        lib.i4sf_chase.restype = ctypes.c_int
+        lib.i4sf_chase.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+        nb = nbytes // 16 * 16
+        sink = torch.zeros(16, dtype=torch.int32, device=self.dev)
+        copies = max(4, math.ceil(1.5 * (1 << 30) / nb))
+        bufs = [torch.full((nb,), 0x5A, dtype=torch.uint8, device=self.dev) for _ in range(copies)]
+
+        def timed_reads(nbuf, nt):
+            cap = torch.cuda.Stream(self.dev)
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(steps):
+                    st = lib.i4sf_stream_read(bufs[i % nbuf].data_ptr(), nb, nt, sink.data_ptr(), cap.cuda_stream)
+                    if st != 0:
+                        raise RuntimeError(f"i4sf_stream_read returned {st}")
+            res = []
+            for _ in range(trials):
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(self.stream)
+                g.replay()
+                e1.record(self.stream)
+                torch.cuda.synchronize()
+                res.append(e0.elapsed_time(e1) * 1e3 / steps)
+            del g
+            return float(np.median(res))
+
+        out = {"bytes": nb, "copies": copies,
+               "stream_read_cold_us": {"nontemporal": timed_reads(copies, 1), "plain": timed_reads(copies, 0)},
+               "stream_read_hot_us": timed_reads(1, 0)}
+        del bufs
+        # pointer chase: a single random cycle through M entries 1 KiB apart
+        M, spacing, hops = 1 << 21, 256, 4000
+        gen = torch.Generator(device=self.dev)
+        gen.manual_seed(0)
+        order = torch.randperm(M, device=self.dev, generator=gen, dtype=torch.int64)
+        nxt = torch.zeros(M * spacing, dtype=torch.int32, device=self.dev)
+        nxt[order * spacing] = (torch.roll(order, -1) * spacing).to(torch.int32)
+        outv = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        lat = []
+        for _ in range(trials):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            st = lib.i4sf_chase(nxt.data_ptr(), nxt.numel(), hops, outv.data_ptr(), self.stream.cuda_stream)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            if st != 0:
+                raise RuntimeError(f"i4sf_chase returned {st}")
+            lat.append(e0.elapsed_time(e1) * 1e6 / hops)
+        k0 = int((order == 0).nonzero()[0])
+        expect = int(order[(k0 + hops) % M]) * spacing
+        if int(outv.item()) != expect:
+            raise RuntimeError(f"pointer chase ended at {int(outv.item())}, expected {expect}")
+        out["load_latency_ns"] = float(np.median(lat))
+        del nxt, order
+        torch.cuda.empty_cache()
+        return out
+
     def measure_layer(self, m, batch, steps, warmup, trials):
         """Cold and hot timing of one matrix at one batch size."""
         import workloads as WL
@@ -267,11 +349,10 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if (tr.get("kernel_source_sha") == sha_of(GEMV_SRC) and tr.get("workload") == args.workload
+        if (tr.get("kernel_source_sha") == sha_of(B1_SRCS) and tr.get("workload") == args.workload
                 and tr.get("batch") == batch):
             traffic = tr.get("hbm_bytes_per_launch")
-    kname = (f"gemv_b1_kernel<{m.n_keep}>" if batch == 1 and m.n_keep in (2, 4)
-             else f"gemv_kernel<{m.n_keep},BT>=" + str(batch))
+    kname = kernel_label(m, batch)
 
     result = {
         "metric": METRIC,
@@ -305,6 +386,17 @@ def main():
                      "algorithmic_bytes_per_launch": nbytes},
     }
 
+    if not args.no_floors:
+        fl = R.floors(nbytes)
+        best = min(fl["stream_read_cold_us"].values())
+        fl["read_only_ceiling_gbs"] = round(nbytes / (best * 1e-6) / 1e9, 2)
+        fl["gemv_frac_of_read_only_ceiling"] = round(achieved / fl["read_only_ceiling_gbs"], 4)
+        fl["empty_launch_us"] = round(floor_us, 4)
+        for k in ("stream_read_hot_us", "load_latency_ns"):
+            fl[k] = round(fl[k], 4)
+        fl["stream_read_cold_us"] = {k: round(v, 4) for k, v in fl["stream_read_cold_us"].items()}
+        result["floors"] = fl
+
     if args.suite:
         rows = run_suite(R, args)
         with open(args.suite, "w") as f:
@@ -315,6 +407,19 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args, m, batch, w16, x16, nbytes)
 
     print(json.dumps(result), flush=True)
+
+
+def kernel_label(m, batch):
+    """Name of the kernel the library dispatches for this call (labels only)."""
+    units = m.cols // 64
+    if batch == 1 and m.n_keep in (2, 4):
+        rpw = 2 if m.rows > 8192 else 1
+        if units <= 256:
+            return f"gemv_b1_direct_kernel<{m.n_keep},{rpw},{(units + 63) // 64},8>"
+        return f"gemv_b1_kernel<{m.n_keep},{rpw},8>"
+    if m.n_keep == 2 and batch >= 2:
+        return "gemv_smfmac_kernel / gemv_smfmac_split_kernel"
+    return f"gemv_kernel<{m.n_keep},BT>=" + str(batch)
 
 
 def run_suite(R, args):

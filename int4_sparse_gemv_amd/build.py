@@ -1,8 +1,10 @@
 """Build libi4s.so in-tree with hipcc for gfx950.
 
-``python -m int4_sparse_gemv_amd.build`` (or ``build()``) compiles every HIP
-and C++ source under ``csrc/`` into ``int4_sparse_gemv_amd/libi4s.so``.  It
-always recompiles.  hipcc cross-compiles for gfx950 without a GPU present.
+``python -m int4_sparse_gemv_amd.build`` (or ``build()``) compiles the
+library's HIP and C++ sources under ``csrc/`` into
+``int4_sparse_gemv_amd/libi4s.so``, and the benchmark's floor kernels
+(``csrc/i4s_floor.hip``) into ``libi4s_floor.so``.  It always recompiles.
+hipcc cross-compiles for gfx950 without a GPU present.
 """
 
 from __future__ import annotations
@@ -18,8 +20,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libi4s.so")
+FLOOR_LIB = os.path.join(PKG, "libi4s_floor.so")
 
-SOURCES = ("i4s_api.cpp", "i4s_pack.hip", "i4s_gemv.hip")
+SOURCES = ("i4s_api.cpp", "i4s_pack.hip", "i4s_gemv_b1.hip", "i4s_gemv_batch.hip")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -54,21 +57,26 @@ def _run(cmd):
     return out
 
 
+def _link(cc, sources, lib, tmp, verbose):
+    objs = []
+    for src in sources:
+        obj = os.path.join(tmp, src + ".o")
+        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        out = _run(cmd)
+        if verbose and out.strip():
+            print(out)
+        objs.append(obj)
+    tmp_lib = lib + ".tmp"
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib])
+    os.replace(tmp_lib, lib)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libi4s.so; returns its path."""
+    """Compile libi4s.so and libi4s_floor.so; returns the path of libi4s.so."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="i4s_build_") as tmp:
-        objs = []
-        for src in SOURCES:
-            obj = os.path.join(tmp, src + ".o")
-            cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
-            out = _run(cmd)
-            if verbose and out.strip():
-                print(out)
-            objs.append(obj)
-        tmp_lib = LIB + ".tmp"
-        _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib])
-        os.replace(tmp_lib, LIB)
+        _link(cc, SOURCES, LIB, tmp, verbose)
+        _link(cc, ("i4s_floor.hip",), FLOOR_LIB, tmp, verbose)
     return LIB
 
 

@@ -1,0 +1,392 @@
+// Batch-1 SparseGEMV kernels for gfx950: y = W_hat x over the 2-bit CSR INT4
+// format, one activation vector.
+//
+// Method: "Efficient LLM-based Advertising via Model Compression and Parallel
+// Verification", section 3.3, "Computational Acceleration": the activation
+// vector is staged in on-chip shared memory (LDS here) by the whole block,
+// INT4 weights are widened to fp16 in registers and the 2-bit indices pick
+// the activations each kept weight multiplies.  No matrix instructions: at
+// batch 1 the work is a stream of packed bytes with a few VALU operations
+// per element.
+//
+// Mapping.  A block is 8 waves; each wave owns RPW consecutive rows.  A row
+// is cut into 64-column "units" (16 groups of 4 columns: 8*NK bytes of vals,
+// 4*NK bytes of codes, one scale); lane l takes units l, l+64, ...  Adjacent
+// lanes therefore read adjacent 16-byte pieces of a row (dwordx4 for 2:4),
+// and one unit never straddles a quantization group.  The RPW rows of a wave
+// share the same columns, so each activation fetch from LDS feeds RPW rows.
+// For 2:4 the v_perm_b32 selectors come from a 16-entry table in LDS and
+// v_dot2_f32_f16 multiplies and accumulates in fp32; the group scale is
+// applied once per unit.
+//
+// Row starts: the kernels read row_ptr, but issue the weight loads of a row
+// at the offset the format prescribes (row * K * N / 4) without waiting for
+// that read; when row_ptr disagrees, the row is fetched again from row_ptr's
+// offset.  A dependent round trip to memory is thus kept off the common path.
+//
+// LDS layout of x: each 64-column unit occupies 72 halfs, so the 16-byte
+// reads that 64 lanes issue for 64 different units fall in distinct banks.
+
+#include "i4s_gemv_common.h"
+
+namespace i4s {
+namespace {
+
+// ---------------------------------------------------------------------------
+// batch-1 kernel (2:4 and dense): the lane's 64 activations live in registers
+
+template <int NK>
+__device__ inline float unit_dot_b1(const UnitRegs<NK> &u, const uint32_t (&xr)[32], const uint32_t *lut) {
+  float g = 0.0f;
+  if constexpr (NK == 2) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {  // code dword c: groups 8c..8c+7
+      const uint32_t me = (u.c[c] << 2) & 0x3C3C3C3Cu;  // byte k: 4 * code nibble of group 8c+2k
+      const uint32_t mo = (u.c[c] >> 2) & 0x3C3C3C3Cu;  // byte k: 4 * code nibble of group 8c+2k+1
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {  // vals word j = 2c + half: groups 8c+4half .. +3
+        h2_t q[4];
+        dequant_word(u.v[2 * c + half], q);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int gi = 4 * half + p;  // group within the code dword
+          const uint32_t m = (gi & 1) ? mo : me;
+          const uint32_t sel = lut_read(lut, (m >> (8 * (gi >> 1))) & 0xFFu);
+          const int grp = 8 * c + gi;
+          const uint32_t xp = __builtin_amdgcn_perm(xr[2 * grp + 1], xr[2 * grp], sel);
+          g = __builtin_amdgcn_fdot2(q[p], as_h2(xp), g, false);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // vals word j: columns 8j..8j+7
+      h2_t q[4];
+      dequant_word(u.v[j], q);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) g = __builtin_amdgcn_fdot2(q[p], as_h2(xr[4 * j + p]), g, false);
+    }
+  }
+  return g;
+}
+
+template <int NK, int RPW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
+    int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
+    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
+    uint16_t *__restrict__ y, int kc_units) {
+  extern __shared__ __align__(16) uint16_t xs[];  // [kc_units][kStrideB1]
+  __shared__ uint32_t lut[16];
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  const int row0 = (blockIdx.x * WAVES + wave) * RPW;
+  const int units = cols / kSegCols;
+  const uint32_t nnz_row = (uint32_t)cols / 4 * NK;
+  const int sg_shift = group_size == 64 ? 0 : (group_size == 128 ? 1 : 2);  // log2(G / 64)
+  const uint32_t ngroups = (uint32_t)(cols / group_size);
+
+  // Rows past the end re-read the last row (their sums are never stored),
+  // so every load and every decode below works on real data.
+  uint32_t rstart[RPW], srow[RPW];
+  bool rvalid[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    rvalid[r] = row0 + r < rows;
+    const int rr = min(row0 + r, rows - 1);
+    rstart[r] = (uint32_t)rr * nnz_row;  // the format's offset
+    srow[r] = (uint32_t)rr * ngroups;    // first scale of the row
+  }
+
+  float acc[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+
+  for (int ub = 0; ub < units; ub += kc_units) {
+    const int ue = min(units, ub + kc_units);
+    int u = ub + lane;
+    bool has = u < ue;
+    UnitRegs<NK> cur[RPW];
+    if (has) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                      srow[r] + ((uint32_t)u >> sg_shift));
+    }
+    int32_t rp[RPW];
+    if (ub == 0) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) rp[r] = row_ptr[min(row0 + r, rows - 1)];
+    }
+
+    if (ub > 0) __syncthreads();  // the previous chunk is fully consumed
+    {
+      const int nvec = (ue - ub) * (kSegCols / 8);  // uint4 = 8 halfs
+      for (int i = threadIdx.x; i < nvec; i += 64 * WAVES) {
+        const int un = i >> 3, part = i & 7;
+        *reinterpret_cast<uint4 *>(xs + un * kStrideB1 + 8 * part) =
+            *reinterpret_cast<const uint4 *>(x + (int64_t)ub * kSegCols + 8 * i);
+      }
+      if (NK == 2 && ub == 0 && threadIdx.x < 16) init_selector_table(lut);
+    }
+    __syncthreads();
+
+    if (ub == 0) {
+      // row_ptr check (wave-uniform): re-fetch rows stored elsewhere
+      bool moved = false;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) moved |= (uint32_t)rp[r] != rstart[r];
+      if (moved) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          rstart[r] = (uint32_t)rp[r];
+          if (has)
+            load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                          srow[r] + ((uint32_t)u >> sg_shift));
+        }
+      }
+    }
+
+    while (has) {
+      const int un = u + 64;
+      const bool hn = un < ue;
+      UnitRegs<NK> nxt[RPW];
+      if (hn) {  // prefetch the lane's next unit
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+          load_unit<NK>(nxt[r], vals, codes, scales, rstart[r] + (uint32_t)un * 16 * NK,
+                        srow[r] + ((uint32_t)un >> sg_shift));
+      }
+      uint32_t xr[32];
+      const uint4 *xv = reinterpret_cast<const uint4 *>(xs + (u - ub) * kStrideB1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 t = xv[i];
+        xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float gsum = unit_dot_b1<NK>(cur[r], xr, lut);
+        acc[r] = fmaf(fp16_bits_to_float(cur[r].s), gsum, acc[r]);
+      }
+      if (!hn) break;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) cur[r] = nxt[r];
+      u = un;
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float t = wave_sum(acc[r]);
+    if (lane == 0 && rvalid[r]) y[row0 + r] = (uint16_t)float_to_fp16_bits(t);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// batch-1 kernel for rows of at most 64 * UPL units: every load up front.
+//
+// A wave issues the block's share of the activation loads first, then all of
+// its lanes' weight loads (UPL units per lane, nontemporal: the weights are
+// read once).  Vector loads retire in issue order, so the LDS write of x --
+// and the block barrier after it -- waits for the activations only, not for
+// the weight stream; each wave starts computing as soon as its own weights
+// are in, which overlaps the decode with the stream.
+
+// units = K / 64; sg_shift = log2(G / 64).  Shapes arrive pre-divided so the
+// prologue before the first load is a handful of scalar shifts.
+template <int NK, int RPW, int UPL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
+    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
+    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
+    uint16_t *__restrict__ y) {
+  extern __shared__ __align__(16) uint16_t xs[];  // [units][kStrideB1]
+  __shared__ uint32_t lut[16];
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  const int row0 = (blockIdx.x * WAVES + wave) * RPW;
+  const int nvec = units * (kSegCols / 8);  // uint4 pieces of x
+  const uint32_t nnz_row = (uint32_t)units * 16 * NK;
+  const uint32_t ngroups = (uint32_t)units >> sg_shift;
+
+  // 1. activations (nvec <= 64 * WAVES * UPL, so UPL pieces per thread cover
+  // them).  Every load below is unconditional, at a clamped index, so the
+  // wait before the LDS write counts exactly the loads issued after it.
+  uint4 xg[UPL];
+  int xi[UPL];
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    xi[j] = min((int)threadIdx.x + j * 64 * WAVES, nvec - 1);
+    xg[j] = reinterpret_cast<const uint4 *>(x)[xi[j]];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. weights: rows past the end re-read the last row (never stored)
+  uint32_t rstart[RPW], srow[RPW];
+  bool rvalid[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    rvalid[r] = row0 + r < rows;
+    const int rr = min(row0 + r, rows - 1);
+    rstart[r] = (uint32_t)rr * nnz_row;
+    srow[r] = (uint32_t)rr * ngroups;
+  }
+  UnitRegs<NK> wr[UPL][RPW];
+#pragma unroll
+  for (int k = 0; k < UPL; ++k) {
+    const int u = min(lane + 64 * k, units - 1);  // lanes past the row re-read its last unit
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      load_unit_nt<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                       srow[r] + ((uint32_t)u >> sg_shift));
+  }
+  // row_ptr: a vector load, issued last and needed only after decoding.  (A
+  // scalar load would share its counter with LDS and, returning out of
+  // order, hold up the block barrier and the first LDS reads.)
+  int32_t rp[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) rp[r] = row_ptr[min(row0 + r, rows - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. stage x in LDS (threads with a clamped index write the same piece
+  // to the same place again)
+#pragma unroll
+  for (int j = 0; j < UPL; ++j)
+    *reinterpret_cast<uint4 *>(xs + (xi[j] >> 3) * kStrideB1 + 8 * (xi[j] & 7)) = xg[j];
+  if (NK == 2 && threadIdx.x < 16) init_selector_table(lut);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 4. decode and accumulate.  The row_ptr check comes after the first pass,
+  // so the common case never waits for row_ptr before decoding; a row stored
+  // away from the format's offset (wave-uniform) is re-fetched and decoded
+  // again.
+  float acc[RPW];
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < UPL; ++k) {
+      const int u = lane + 64 * k;
+      if (u < units) {
+        uint32_t xr[32];
+        const uint4 *xv = reinterpret_cast<const uint4 *>(xs + u * kStrideB1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint4 t = xv[i];
+          xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
+        }
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          const float gsum = unit_dot_b1<NK>(wr[k][r], xr, lut);
+          acc[r] = fmaf(fp16_bits_to_float(wr[k][r].s), gsum, acc[r]);
+        }
+      }
+    }
+    bool moved = false;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) moved |= (uint32_t)rp[r] != rstart[r];
+    if (pass == 1 || !moved) break;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      rstart[r] = (uint32_t)rp[r];
+#pragma unroll
+      for (int k = 0; k < UPL; ++k) {
+        const int u = min(lane + 64 * k, units - 1);
+        load_unit<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                      srow[r] + ((uint32_t)u >> sg_shift));
+      }
+    }
+  }
+
+  // 5. reduce and store
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float t = wave_sum(acc[r]);
+    if (lane == 0 && rvalid[r]) y[row0 + r] = (uint16_t)float_to_fp16_bits(t);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+
+// Batch-1 kernel: 8 waves per block (512 threads), RPW rows per wave.
+constexpr int kB1Waves = 8;
+
+template <int NK, int RPW, int UPL>
+hipError_t launch_b1_direct(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  const int units = w.cols / kSegCols;
+  const size_t lds = (size_t)units * kStrideB1 * 2;
+  const int rows_per_block = kB1Waves * RPW;
+  const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kB1Waves);
+  const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
+  hipLaunchKernelGGL((gemv_b1_direct_kernel<NK, RPW, UPL, kB1Waves>), grid, block, lds, stream, w.rows,
+                     units, sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, y);
+  return hipGetLastError();
+}
+
+// I4S_B1_KERNEL=stream forces the pipelined batch-1 kernel (tuning); read once.
+bool b1_direct_enabled() {
+  static const bool v = [] {
+    const char *e = getenv("I4S_B1_KERNEL");
+    return !(e && e[0] == 's');
+  }();
+  return v;
+}
+
+template <int NK, int RPW>
+hipError_t launch_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  const int units = w.cols / kSegCols;
+  if (b1_direct_enabled()) {
+    switch ((units + 63) / 64) {
+      case 1: return launch_b1_direct<NK, RPW, 1>(w, x, y, stream);
+      case 2: return launch_b1_direct<NK, RPW, 2>(w, x, y, stream);
+      case 3: return launch_b1_direct<NK, RPW, 3>(w, x, y, stream);
+      case 4: return launch_b1_direct<NK, RPW, 4>(w, x, y, stream);
+      default: break;  // longer rows: the pipelined kernel
+    }
+  }
+  int kc = kLdsBudget / (kStrideB1 * 2);
+  if (kc > units) kc = units;
+  const size_t lds = (size_t)kc * kStrideB1 * 2;
+  const int rows_per_block = kB1Waves * RPW;
+  const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kB1Waves);
+  hipLaunchKernelGGL((gemv_b1_kernel<NK, RPW, kB1Waves>), grid, block, lds, stream, w.rows, w.cols,
+                     w.group_size, w.row_ptr, w.vals, w.codes, w.scales, x, y, kc);
+  return hipGetLastError();
+}
+
+// Rows per wave of the batch-1 kernel.  One row per wave keeps 2+ blocks on
+// every CU up to ~8k rows; taller matrices take two rows per wave so each
+// block's staged activations feed more rows.  I4S_B1_RPW (1, 2 or 4)
+// overrides the choice for tuning; it is read once.
+int b1_rows_per_wave(int rows) {
+  static const int forced = [] {
+    const char *e = getenv("I4S_B1_RPW");
+    const int r = e ? atoi(e) : 0;
+    return (r == 1 || r == 2 || r == 4) ? r : 0;
+  }();
+  if (forced) return forced;
+  return rows > 8192 ? 2 : 1;
+}
+
+}  // namespace
+
+hipError_t launch_gemv_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  const int rpw = b1_rows_per_wave(w.rows);
+  if (w.n_keep == 2) {
+    switch (rpw) {
+      case 2: return launch_b1<2, 2>(w, x, y, stream);
+      case 4: return launch_b1<2, 4>(w, x, y, stream);
+      default: return launch_b1<2, 1>(w, x, y, stream);
+    }
+  }
+  switch (rpw) {
+    case 2: return launch_b1<4, 2>(w, x, y, stream);
+    case 4: return launch_b1<4, 4>(w, x, y, stream);
+    default: return launch_b1<4, 1>(w, x, y, stream);
+  }
+}
+
+}  // namespace i4s

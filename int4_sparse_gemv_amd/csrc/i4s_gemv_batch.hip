@@ -1,482 +1,24 @@
-// SparseGEMV kernels for gfx950: y = W_hat x over the 2-bit CSR INT4 format.
+// Batch SparseGEMV kernels for gfx950 (1 <= batch <= 16, and batch 1 for
+// the 1:4 pattern) and the dispatch of every GEMV call.
 //
 // Method: "Efficient LLM-based Advertising via Model Compression and Parallel
-// Verification", section 3.3, "Computational Acceleration": activations are
-// staged in on-chip shared memory (LDS here) by the whole block, INT4 weights
-// are widened to fp16 with a few bit operations, and the 2-bit indices packed
-// in uint16 words are decoded with shifts and masks.  The design below is
-// written for CDNA4 (wave64, v_perm_b32, v_dot2_f32_f16, DPP, 64 KB+ LDS),
-// not taken from the page's NVIDIA kernel.
+// Verification", section 3.3, "Computational Acceleration" (activations
+// staged on chip, INT4 widened in registers, 2-bit indices decoded with bit
+// operations), and section 3.4, "Tree-based Parallel Verification", whose
+// candidate sequences, decoded in parallel, make the batch of activation
+// vectors.
 //
-// Mapping.  A block is 8 waves (batch-1 kernel) or 4 waves (batch kernel);
-// each wave owns RPW consecutive rows.  A row
-// is cut into 64-column "units" (16 groups of 4 columns: 8*NK bytes of vals,
-// 4*NK bytes of codes, one scale); lane l takes units l, l+64, ...  Adjacent
-// lanes therefore read adjacent 16-byte pieces of a row (dwordx4 for 2:4),
-// and one unit never straddles a quantization group.  The RPW rows of a wave
-// share the same columns, so each activation fetch from LDS feeds RPW rows.
-//
-// Row starts: the kernel reads row_ptr, but it issues the weight loads of a
-// row at the offset the format prescribes (row * K * N / 4) without waiting
-// for that read; when row_ptr disagrees, the row is re-fetched from
-// row_ptr's offset.  A dependent round trip to memory is thus kept off the
-// common path.
-//
-// Per 8 stored elements (one 32-bit vals word) the decode is one shift, four
-// v_and_or_b32 that drop nibble pairs into the mantissa of 1024.0 (fp16
-// 0x6400) and four packed fp16 adds/fmas that remove the bias exactly; the
-// nibble interleave of the format puts elements (2p, 2p+1) in bits 4p and
-// 16+4p so one mask yields one pair.  For 2:4, a group's 4-bit code picks a
-// v_perm_b32 selector (from a 16-entry table in LDS) that moves the two kept
-// activations out of the group's four into one fp16 pair, and
-// v_dot2_f32_f16 multiplies and accumulates in fp32.  The group scale is
-// applied once per unit.  Row sums across lanes use DPP row rotations and
-// four lane reads (no LDS traffic).
-//
-// LDS layout of x: each 64-column unit occupies 72 (batch-1 kernel) or 68
-// (batch kernel) halfs, so the 16-byte or 8-byte reads that 64 lanes issue
-// for 64 different units fall in distinct banks.
-//
-// Batch kernel: BT activation vectors (BT >= batch, rounded up to 1, 2, 4,
-// 8, 16; the extra vectors are zero in LDS and never stored).  When the
-// staged activations exceed the LDS budget the K axis is processed in
-// chunks, re-staging x.
+// VALU batch kernel: a block is 4 waves; each wave owns RPW rows and the
+// lanes take 64-column units as in the batch-1 kernels.  BT activation
+// vectors (BT >= batch, rounded up to 1, 2, 4, 8, 16; the extra vectors are
+// zero in LDS and never stored) are staged in LDS with 68 halfs per unit, so
+// the 8-byte reads of 64 lanes fall in distinct banks.  When the staged
+// activations exceed the LDS budget the K axis is processed in chunks.
 
-#include <stdlib.h>
-
-#include "i4s_internal.h"
+#include "i4s_gemv_common.h"
 
 namespace i4s {
 namespace {
-
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kLdsBudget = 64 * 1024;  // bytes of LDS for staged activations
-constexpr int kStrideB1 = 72;          // halfs per unit, batch-1 kernel (16-byte reads)
-constexpr int kStrideBT = 68;          // halfs per unit, batch kernel (8-byte reads)
-
-__device__ inline h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
-
-// (a & m) | c in one VALU op; GFX9 VOP3 takes no literal, so m comes in an SGPR.
-__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
-  return d;
-}
-
-// Four exact fp16 pairs (q_{2p}, q_{2p+1}), p = 0..3, of one vals word.
-__device__ inline void dequant_word(uint32_t w, h2_t q[4]) {
-  const uint32_t magic = 0x64006400u;  // 1024.0 in both halves
-  const uint32_t t = w >> 8;
-  const h2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const h2_t bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  // slots 0/4 and 2/6: nibble in mantissa bits 0..3 -> 1024 + u
-  q[0] = as_h2(and_or(w, 0x000F000Fu, magic)) + bias;
-  q[2] = as_h2(and_or(t, 0x000F000Fu, magic)) + bias;
-  // slots 1/5 and 3/7: nibble in mantissa bits 4..7 -> 1024 + 16u
-  q[1] = __builtin_elementwise_fma(as_h2(and_or(w, 0x00F000F0u, magic)), sixteenth, bias16);
-  q[3] = __builtin_elementwise_fma(as_h2(and_or(t, 0x00F000F0u, magic)), sixteenth, bias16);
-}
-
-// v_perm_b32 selector taking fp16 lanes cf and cs of a group's four
-// activations (held as two dwords {x0|x1<<16, x2|x3<<16}) into (lo, hi):
-// bytes [2cf, 2cf+1, 2cs, 2cs+1], for the code nibble h = cf | cs << 2.
-// The multiply spreads the two 2-bit fields into four byte lanes without
-// carries between them.
-__host__ __device__ constexpr uint32_t pair_selector(uint32_t h) {
-  return ((h * 0x808202u) & 0x06060606u) | 0x01000100u;
-}
-
-__device__ inline float fp16_bits_to_float(uint32_t b) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
-}
-
-// float -> fp16 bits, round to nearest even
-__device__ inline uint32_t float_to_fp16_bits(float f) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
-template <int CTRL>
-__device__ inline float dpp_rot_add(float v) {
-  const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
-  return v + __builtin_bit_cast(float, s);
-}
-
-// Sum over the 64 lanes; every lane gets the result.  Rotations by 8, 4, 2,
-// 1 inside each 16-lane row (DPP row_ror), then the four row sums.
-__device__ inline float wave_sum(float v) {
-  v = dpp_rot_add<0x128>(v);
-  v = dpp_rot_add<0x124>(v);
-  v = dpp_rot_add<0x122>(v);
-  v = dpp_rot_add<0x121>(v);
-  const int b = __builtin_bit_cast(int, v);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-  return (r0 + r1) + (r2 + r3);
-}
-
-template <int NK>
-struct UnitRegs {
-  uint32_t v[2 * NK];                 // vals words of the unit
-  uint32_t c[NK < 4 ? NK : 1];        // code dwords (16 codes each)
-  uint32_t s;                         // scale bits
-};
-
-// Loads one unit: elem0 is the unit's first element (row start + 16*NK*u).
-template <int NK>
-__device__ inline void load_unit(UnitRegs<NK> &r, const uint8_t *__restrict__ vals,
-                                 const uint16_t *__restrict__ codes,
-                                 const uint16_t *__restrict__ scales, uint32_t elem0,
-                                 uint32_t scale_idx) {
-  const uint32_t *vp = reinterpret_cast<const uint32_t *>(vals + (elem0 >> 1));
-  if constexpr (NK == 1) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(vp);
-    r.v[0] = a.x; r.v[1] = a.y;
-  } else if constexpr (NK == 2) {
-    const uint4 a = *reinterpret_cast<const uint4 *>(vp);
-    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
-  } else {
-    const uint4 a = reinterpret_cast<const uint4 *>(vp)[0];
-    const uint4 b = reinterpret_cast<const uint4 *>(vp)[1];
-    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
-    r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
-  }
-  if constexpr (NK == 1) {
-    r.c[0] = *reinterpret_cast<const uint32_t *>(codes + (elem0 >> 3));
-  } else if constexpr (NK == 2) {
-    const uint2 c = *reinterpret_cast<const uint2 *>(codes + (elem0 >> 3));
-    r.c[0] = c.x; r.c[1] = c.y;
-  }
-  r.s = scales[scale_idx];
-}
-
-// Fill the 16-entry selector table (2:4 only); call with threadIdx.x < 16.
-__device__ inline void init_selector_table(uint32_t *lut) {
-  lut[threadIdx.x] = pair_selector(threadIdx.x);
-}
-
-__device__ inline uint32_t lut_read(const uint32_t *lut, uint32_t byte_off) {
-  return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lut) + byte_off);
-}
-
-// ---------------------------------------------------------------------------
-// batch-1 kernel (2:4 and dense): the lane's 64 activations live in registers
-
-template <int NK>
-__device__ inline float unit_dot_b1(const UnitRegs<NK> &u, const uint32_t (&xr)[32], const uint32_t *lut) {
-  float g = 0.0f;
-  if constexpr (NK == 2) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {  // code dword c: groups 8c..8c+7
-      const uint32_t me = (u.c[c] << 2) & 0x3C3C3C3Cu;  // byte k: 4 * code nibble of group 8c+2k
-      const uint32_t mo = (u.c[c] >> 2) & 0x3C3C3C3Cu;  // byte k: 4 * code nibble of group 8c+2k+1
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {  // vals word j = 2c + half: groups 8c+4half .. +3
-        h2_t q[4];
-        dequant_word(u.v[2 * c + half], q);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int gi = 4 * half + p;  // group within the code dword
-          const uint32_t m = (gi & 1) ? mo : me;
-          const uint32_t sel = lut_read(lut, (m >> (8 * (gi >> 1))) & 0xFFu);
-          const int grp = 8 * c + gi;
-          const uint32_t xp = __builtin_amdgcn_perm(xr[2 * grp + 1], xr[2 * grp], sel);
-          g = __builtin_amdgcn_fdot2(q[p], as_h2(xp), g, false);
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {  // vals word j: columns 8j..8j+7
-      h2_t q[4];
-      dequant_word(u.v[j], q);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) g = __builtin_amdgcn_fdot2(q[p], as_h2(xr[4 * j + p]), g, false);
-    }
-  }
-  return g;
-}
-
-template <int NK, int RPW, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
-    int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
-    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
-    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
-    uint16_t *__restrict__ y, int kc_units) {
-  extern __shared__ __align__(16) uint16_t xs[];  // [kc_units][kStrideB1]
-  __shared__ uint32_t lut[16];
-  const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
-  const int row0 = (blockIdx.x * WAVES + wave) * RPW;
-  const int units = cols / kSegCols;
-  const uint32_t nnz_row = (uint32_t)cols / 4 * NK;
-  const int sg_shift = group_size == 64 ? 0 : (group_size == 128 ? 1 : 2);  // log2(G / 64)
-  const uint32_t ngroups = (uint32_t)(cols / group_size);
-
-  // Rows past the end re-read the last row (their sums are never stored),
-  // so every load and every decode below works on real data.
-  uint32_t rstart[RPW], srow[RPW];
-  bool rvalid[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    rvalid[r] = row0 + r < rows;
-    const int rr = min(row0 + r, rows - 1);
-    rstart[r] = (uint32_t)rr * nnz_row;  // the format's offset
-    srow[r] = (uint32_t)rr * ngroups;    // first scale of the row
-  }
-
-  float acc[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
-
-  for (int ub = 0; ub < units; ub += kc_units) {
-    const int ue = min(units, ub + kc_units);
-    int u = ub + lane;
-    bool has = u < ue;
-    UnitRegs<NK> cur[RPW];
-    if (has) {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r)
-        load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
-                      srow[r] + ((uint32_t)u >> sg_shift));
-    }
-    int32_t rp[RPW];
-    if (ub == 0) {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) rp[r] = row_ptr[min(row0 + r, rows - 1)];
-    }
-
-    if (ub > 0) __syncthreads();  // the previous chunk is fully consumed
-    {
-      const int nvec = (ue - ub) * (kSegCols / 8);  // uint4 = 8 halfs
-      for (int i = threadIdx.x; i < nvec; i += 64 * WAVES) {
-        const int un = i >> 3, part = i & 7;
-        *reinterpret_cast<uint4 *>(xs + un * kStrideB1 + 8 * part) =
-            *reinterpret_cast<const uint4 *>(x + (int64_t)ub * kSegCols + 8 * i);
-      }
-      if (NK == 2 && ub == 0 && threadIdx.x < 16) init_selector_table(lut);
-    }
-    __syncthreads();
-
-    if (ub == 0) {
-      // row_ptr check (wave-uniform): re-fetch rows stored elsewhere
-      bool moved = false;
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) moved |= (uint32_t)rp[r] != rstart[r];
-      if (moved) {
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          rstart[r] = (uint32_t)rp[r];
-          if (has)
-            load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
-                          srow[r] + ((uint32_t)u >> sg_shift));
-        }
-      }
-    }
-
-    while (has) {
-      const int un = u + 64;
-      const bool hn = un < ue;
-      UnitRegs<NK> nxt[RPW];
-      if (hn) {  // prefetch the lane's next unit
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-          load_unit<NK>(nxt[r], vals, codes, scales, rstart[r] + (uint32_t)un * 16 * NK,
-                        srow[r] + ((uint32_t)un >> sg_shift));
-      }
-      uint32_t xr[32];
-      const uint4 *xv = reinterpret_cast<const uint4 *>(xs + (u - ub) * kStrideB1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 t = xv[i];
-        xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
-      }
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const float gsum = unit_dot_b1<NK>(cur[r], xr, lut);
-        acc[r] = fmaf(fp16_bits_to_float(cur[r].s), gsum, acc[r]);
-      }
-      if (!hn) break;
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) cur[r] = nxt[r];
-      u = un;
-    }
-  }
-
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const float t = wave_sum(acc[r]);
-    if (lane == 0 && rvalid[r]) y[row0 + r] = (uint16_t)float_to_fp16_bits(t);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// batch-1 kernel for rows of at most 64 * UPL units: every load up front.
-//
-// A wave issues the block's share of the activation loads first, then all of
-// its lanes' weight loads (UPL units per lane, nontemporal: the weights are
-// read once).  Vector loads retire in issue order, so the LDS write of x --
-// and the block barrier after it -- waits for the activations only, not for
-// the weight stream; each wave starts computing as soon as its own weights
-// are in, which overlaps the decode with the stream.
-
-// Block barrier that orders LDS only: the fences are restricted to the local
-// address space, so no wave waits here for its outstanding global loads.
-__device__ inline void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-template <int NK>
-__device__ inline void load_unit_nt(UnitRegs<NK> &r, const uint8_t *__restrict__ vals,
-                                    const uint16_t *__restrict__ codes,
-                                    const uint16_t *__restrict__ scales, uint32_t elem0,
-                                    uint32_t scale_idx) {
-  const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(vals + (elem0 >> 1));
-  if constexpr (NK == 1) {
-    const u32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(vp));
-    r.v[0] = a.x; r.v[1] = a.y;
-  } else if constexpr (NK == 2) {
-    const u32x4_t a = __builtin_nontemporal_load(vp);
-    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
-  } else {
-    const u32x4_t a = __builtin_nontemporal_load(vp);
-    const u32x4_t b = __builtin_nontemporal_load(vp + 1);
-    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
-    r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
-  }
-  if constexpr (NK == 1) {
-    r.c[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + (elem0 >> 3)));
-  } else if constexpr (NK == 2) {
-    const u32x2_t c = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(codes + (elem0 >> 3)));
-    r.c[0] = c.x; r.c[1] = c.y;
-  }
-  r.s = __builtin_nontemporal_load(scales + scale_idx);
-}
-
-// units = K / 64; sg_shift = log2(G / 64).  Shapes arrive pre-divided so the
-// prologue before the first load is a handful of scalar shifts.
-template <int NK, int RPW, int UPL, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
-    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
-    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
-    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
-    uint16_t *__restrict__ y) {
-  extern __shared__ __align__(16) uint16_t xs[];  // [units][kStrideB1]
-  __shared__ uint32_t lut[16];
-  const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
-  const int row0 = (blockIdx.x * WAVES + wave) * RPW;
-  const int nvec = units * (kSegCols / 8);  // uint4 pieces of x
-  const uint32_t nnz_row = (uint32_t)units * 16 * NK;
-  const uint32_t ngroups = (uint32_t)units >> sg_shift;
-
-  // 1. activations (nvec <= 64 * WAVES * UPL, so UPL pieces per thread cover
-  // them).  Every load below is unconditional, at a clamped index, so the
-  // wait before the LDS write counts exactly the loads issued after it.
-  uint4 xg[UPL];
-  int xi[UPL];
-#pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    xi[j] = min((int)threadIdx.x + j * 64 * WAVES, nvec - 1);
-    xg[j] = reinterpret_cast<const uint4 *>(x)[xi[j]];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 2. weights: rows past the end re-read the last row (never stored)
-  uint32_t rstart[RPW], srow[RPW];
-  bool rvalid[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    rvalid[r] = row0 + r < rows;
-    const int rr = min(row0 + r, rows - 1);
-    rstart[r] = (uint32_t)rr * nnz_row;
-    srow[r] = (uint32_t)rr * ngroups;
-  }
-  UnitRegs<NK> wr[UPL][RPW];
-#pragma unroll
-  for (int k = 0; k < UPL; ++k) {
-    const int u = min(lane + 64 * k, units - 1);  // lanes past the row re-read its last unit
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-      load_unit_nt<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
-                       srow[r] + ((uint32_t)u >> sg_shift));
-  }
-  // row_ptr: a vector load, issued last and needed only after decoding.  (A
-  // scalar load would share its counter with LDS and, returning out of
-  // order, hold up the block barrier and the first LDS reads.)
-  int32_t rp[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) rp[r] = row_ptr[min(row0 + r, rows - 1)];
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 3. stage x in LDS (threads with a clamped index write the same piece
-  // to the same place again)
-#pragma unroll
-  for (int j = 0; j < UPL; ++j)
-    *reinterpret_cast<uint4 *>(xs + (xi[j] >> 3) * kStrideB1 + 8 * (xi[j] & 7)) = xg[j];
-  if (NK == 2 && threadIdx.x < 16) init_selector_table(lut);
-  lds_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 4. decode and accumulate.  The row_ptr check comes after the first pass,
-  // so the common case never waits for row_ptr before decoding; a row stored
-  // away from the format's offset (wave-uniform) is re-fetched and decoded
-  // again.
-  float acc[RPW];
-  for (int pass = 0;; ++pass) {
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < UPL; ++k) {
-      const int u = lane + 64 * k;
-      if (u < units) {
-        uint32_t xr[32];
-        const uint4 *xv = reinterpret_cast<const uint4 *>(xs + u * kStrideB1);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint4 t = xv[i];
-          xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
-        }
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          const float gsum = unit_dot_b1<NK>(wr[k][r], xr, lut);
-          acc[r] = fmaf(fp16_bits_to_float(wr[k][r].s), gsum, acc[r]);
-        }
-      }
-    }
-    bool moved = false;
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) moved |= (uint32_t)rp[r] != rstart[r];
-    if (pass == 1 || !moved) break;
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      rstart[r] = (uint32_t)rp[r];
-#pragma unroll
-      for (int k = 0; k < UPL; ++k) {
-        const int u = min(lane + 64 * k, units - 1);
-        load_unit<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
-                      srow[r] + ((uint32_t)u >> sg_shift));
-      }
-    }
-  }
-
-  // 5. reduce and store
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const float t = wave_sum(acc[r]);
-    if (lane == 0 && rvalid[r]) y[row0 + r] = (uint16_t)float_to_fp16_bits(t);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // batch kernel (any N, 1 <= batch <= 16)
@@ -1053,66 +595,6 @@ hipError_t launch_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint1
   return hipGetLastError();
 }
 
-// Batch-1 kernel: 8 waves per block (512 threads), RPW rows per wave.
-constexpr int kB1Waves = 8;
-
-template <int NK, int RPW, int UPL>
-hipError_t launch_b1_direct(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  const int units = w.cols / kSegCols;
-  const size_t lds = (size_t)units * kStrideB1 * 2;
-  const int rows_per_block = kB1Waves * RPW;
-  const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kB1Waves);
-  const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
-  hipLaunchKernelGGL((gemv_b1_direct_kernel<NK, RPW, UPL, kB1Waves>), grid, block, lds, stream, w.rows,
-                     units, sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, y);
-  return hipGetLastError();
-}
-
-// I4S_B1_KERNEL=stream forces the pipelined batch-1 kernel (tuning); read once.
-bool b1_direct_enabled() {
-  static const bool v = [] {
-    const char *e = getenv("I4S_B1_KERNEL");
-    return !(e && e[0] == 's');
-  }();
-  return v;
-}
-
-template <int NK, int RPW>
-hipError_t launch_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  const int units = w.cols / kSegCols;
-  if (b1_direct_enabled()) {
-    switch ((units + 63) / 64) {
-      case 1: return launch_b1_direct<NK, RPW, 1>(w, x, y, stream);
-      case 2: return launch_b1_direct<NK, RPW, 2>(w, x, y, stream);
-      case 3: return launch_b1_direct<NK, RPW, 3>(w, x, y, stream);
-      case 4: return launch_b1_direct<NK, RPW, 4>(w, x, y, stream);
-      default: break;  // longer rows: the pipelined kernel
-    }
-  }
-  int kc = kLdsBudget / (kStrideB1 * 2);
-  if (kc > units) kc = units;
-  const size_t lds = (size_t)kc * kStrideB1 * 2;
-  const int rows_per_block = kB1Waves * RPW;
-  const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kB1Waves);
-  hipLaunchKernelGGL((gemv_b1_kernel<NK, RPW, kB1Waves>), grid, block, lds, stream, w.rows, w.cols,
-                     w.group_size, w.row_ptr, w.vals, w.codes, w.scales, x, y, kc);
-  return hipGetLastError();
-}
-
-// Rows per wave of the batch-1 kernel.  One row per wave keeps 2+ blocks on
-// every CU up to ~8k rows; taller matrices take two rows per wave so each
-// block's staged activations feed more rows.  I4S_B1_RPW (1, 2 or 4)
-// overrides the choice for tuning; it is read once.
-int b1_rows_per_wave(int rows) {
-  static const int forced = [] {
-    const char *e = getenv("I4S_B1_RPW");
-    const int r = e ? atoi(e) : 0;
-    return (r == 1 || r == 2 || r == 4) ? r : 0;
-  }();
-  if (forced) return forced;
-  return rows > 8192 ? 2 : 1;
-}
-
 hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                          hipStream_t stream) {
   const dim3 grid((unsigned)((w.rows + 15) / 16)), block(64 * kMWaves);
@@ -1150,14 +632,7 @@ hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint
     return launch_smfmac(w, x, batch, y, stream);
   }
   if (batch <= 1) {
-    if constexpr (NK == 2 || NK == 4) {
-      switch (b1_rows_per_wave(w.rows)) {
-        case 1: return launch_b1<NK, 1>(w, x, y, stream);
-        case 4: return launch_b1<NK, 4>(w, x, y, stream);
-        case 2: return launch_b1<NK, 2>(w, x, y, stream);
-        default: return launch_b1<NK, 1>(w, x, y, stream);
-      }
-    }
+    if constexpr (NK == 2 || NK == 4) return launch_gemv_b1(w, x, y, stream);
     return launch_t<NK, 1, 4>(w, x, batch, y, stream);
   }
   if (batch <= 2) return launch_t<NK, 2, 4>(w, x, batch, y, stream);

@@ -43,7 +43,9 @@ hipError_t launch_pack_emit(const uint16_t *w, int32_t rows, int32_t cols,
                             int32_t n_keep, int32_t group_size,
                             const i4s_packed &out, hipStream_t stream);
 
-// GEMV kernels (i4s_gemv.hip).
+// GEMV kernels.  launch_gemv (i4s_gemv_batch.hip) dispatches every call;
+// launch_gemv_b1 (i4s_gemv_b1.hip) runs batch 1 for n_keep 2 and 4.
+hipError_t launch_gemv_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream);
 hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch,
                        uint16_t *y, hipStream_t stream);
 

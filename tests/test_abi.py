@@ -188,3 +188,24 @@ def test_run_ws_validation_fails_before_any_device_call(lib):
     assert B.i4s_run_ws(d, x, 16, y, ws + 8, n.value, None) == B.I4S_ERR_INVALID_ARGUMENT
     assert B.i4s_run_ws(d, x, 16, y, x, n.value, None) == B.I4S_ERR_INVALID_ARGUMENT  # overlaps x
     assert B.i4s_run_ws(d, x, 17, y, ws, n.value, None) == B.I4S_ERR_INVALID_ARGUMENT
+
+
+def test_floor_library_exports_and_rejects_bad_arguments():
+    """The benchmark's floor kernels (libi4s_floor.so): exported, and argument
+    errors are reported before anything is launched (no device needed)."""
+    import ctypes
+    from int4_sparse_gemv_amd import build as BLD
+    out = subprocess.run(["nm", "-D", "--defined-only", BLD.FLOOR_LIB], capture_output=True, text=True).stdout
+    names = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    assert {"i4sf_stream_read", "i4sf_chase"} <= names
+    f = ctypes.CDLL(BLD.FLOOR_LIB)
+    f.i4sf_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f.i4sf_chase.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    fake = 1 << 20  # never dereferenced: every call below fails its checks first
+    assert f.i4sf_stream_read(None, 16, 0, fake, None) == 1
+    assert f.i4sf_stream_read(fake, 0, 0, fake, None) == 1
+    assert f.i4sf_stream_read(fake, 24, 0, fake, None) == 1      # not a multiple of 16
+    assert f.i4sf_stream_read(fake + 4, 16, 0, fake, None) == 1  # misaligned
+    assert f.i4sf_chase(None, 16, 10, fake, None) == 1
+    assert f.i4sf_chase(fake, 0, 10, fake, None) == 1
+    assert f.i4sf_chase(fake, 16, 0, fake, None) == 1
