@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time plain stream launches instead of a graph")
     ap.add_argument("--suite", default=None, help="also measure every workload and write a table here")
     ap.add_argument("--no-stack", action="store_true", help="with --suite: skip the 224-matrix 7B stack")
+    ap.add_argument("--only", default=None, help="with --suite: comma-separated workloads to measure")
     ap.add_argument("--no-floors", action="store_true",
                     help="skip the read-only and latency floor measurements")
     return ap.parse_args()
@@ -105,8 +106,8 @@ class Runner:
     def calls(self, items):
         """items: list of (packed, x tensor, y tensor, batch) -> list of i4s_run_ws argument tuples.
 
-        Calls that can use a workspace share one zero-filled buffer (they run
-        in order on one stream, and each leaves it zero-filled)."""
+        Calls that can use a workspace share one scratch buffer (they run in
+        order on one stream)."""
         out, need = [], 0
         for p, x, y, b in items:
             d = p.descriptor()
@@ -115,7 +116,7 @@ class Runner:
             self.B.check(self.B.i4s_run_workspace_size(d, b, n), "i4s_run_workspace_size")
             need = max(need, n.value)
             out.append([ctypes.byref(d), x.data_ptr(), b, y.data_ptr(), n.value])
-        ws = self.torch.zeros(max(need, 256), dtype=self.torch.uint8, device=self.dev)
+        ws = self.torch.empty(max(need, 256), dtype=self.torch.uint8, device=self.dev)
         self.keep.append(ws)
         return [(d, xp, b, yp, ws.data_ptr() if n else None, ws.numel()) for d, xp, b, yp, n in out]
 
@@ -425,7 +426,10 @@ def kernel_label(m, batch):
 def run_suite(R, args):
     import workloads as WL
     out = []
-    for name in ("c1_512", "c2_4096", "c3_mlp7b", "c5_verify13b", "c4_stack7b"):
+    names = ("c1_512", "c2_4096", "c3_mlp7b", "c5_verify13b", "c4_stack7b")
+    if args.only:
+        names = tuple(n for n in names if n in args.only.split(","))
+    for name in names:
         wl = WL.WORKLOADS[name]
         mats = wl.matrices
         if name == "c4_stack7b":
@@ -438,7 +442,7 @@ def run_suite(R, args):
                 print(f"suite {name}/{m.name} b{b}: cold {r['cold_us']:.2f} us ({r['cold_gbs']:.0f} GB/s), "
                       f"hot {r['hot_us']:.2f} us", file=sys.stderr, flush=True)
                 out.append(r)
-    if not args.no_stack:
+    if not args.no_stack and "c4_stack7b" in names:
         s = R.measure_stack(3)
         s["workload"] = "c4_stack7b/all"
         print(f"suite stack: {s['us_per_pass']:.1f} us per 224-call pass ({s['gbs']:.0f} GB/s)",

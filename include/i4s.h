@@ -155,28 +155,29 @@ i4s_status i4s_run(const i4s_packed *w /* host */, const uint16_t *x_fp16,
                    int32_t batch, uint16_t *y_fp16, void *stream);
 
 /* Bytes of device workspace i4s_run_ws needs for this layer and batch; 0
- * when the call needs none (batch 1, or a pattern other than 2:4).
- * Host-only and pure.  Errors: I4S_ERR_INVALID_ARGUMENT (descriptor
- * inconsistent, batch out of range, bytes == NULL). */
+ * when the call needs none (batch 1, a pattern other than 2:4, or a layer
+ * whose K split has a single slice).  Host-only and pure.  Errors:
+ * I4S_ERR_INVALID_ARGUMENT (descriptor inconsistent, batch out of range,
+ * bytes == NULL). */
 i4s_status i4s_run_workspace_size(const i4s_packed *w /* host */, int32_t batch,
                                   uint64_t *bytes /* host */);
 
 /* y = W_hat x as i4s_run, using a caller workspace that lets the 2:4 batch
- * kernel split K across blocks (section 3.3 of the page; the activations of
- * a block's slice are staged once for 128 rows).  Same arguments as i4s_run
- * plus:
+ * kernel split K across blocks (section 3.3 of the page: the activations of
+ * a block's slice are staged on chip once for 256 rows).  Same arguments as
+ * i4s_run plus:
  *   workspace       : device buffer of at least i4s_run_workspace_size()
  *                     bytes, 16-byte aligned (may be NULL when that size is
- *                     0).  Its first 16384 bytes hold per-row-group counters:
- *                     they must be zero before the first use, and every
- *                     completed call leaves them zero again, so one workspace
- *                     (sized for the largest layer) serves any sequence of
- *                     layers; the rest is scratch.  Calls that share a
- *                     workspace must not overlap (order them on one stream).
- *                     Must not overlap x or y.
+ *                     0).  Scratch for the fp32 partial sums of each slice:
+ *                     its contents on entry do not matter and on return are
+ *                     unspecified.  Calls that share a workspace must not
+ *                     overlap (order them on one stream).  Must not overlap
+ *                     x or y.
  *   workspace_bytes : its size.
- * One kernel launch; asynchronous; allocates nothing.  The result is
- * deterministic (partial sums are added in a fixed order).
+ * Two kernel launches on `stream` when the workspace size is nonzero (the
+ * sliced product, then the sum of the slices), one otherwise; asynchronous;
+ * allocates nothing.  The result is deterministic: slices are added in a
+ * fixed order.
  * Errors: as i4s_run, plus I4S_ERR_WORKSPACE_TOO_SMALL. */
 i4s_status i4s_run_ws(const i4s_packed *w /* host */, const uint16_t *x_fp16,
                       int32_t batch, uint16_t *y_fp16, void *workspace,

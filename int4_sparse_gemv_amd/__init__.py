@@ -118,9 +118,8 @@ def run_workspace_size(p: PackedWeight, batch: int) -> int:
     return n.value
 
 
-# One zero-filled workspace per (device, stream), grown on demand.  Calls on
-# one stream are ordered, and every completed call leaves the workspace
-# zero-filled again, so it can be reused by the next call on that stream.
+# One scratch workspace per (device, stream), grown on demand.  Calls on one
+# stream are ordered, so they can share it.
 _WORKSPACES: Dict[tuple, object] = {}
 
 
@@ -129,7 +128,7 @@ def _workspace(device, stream_handle: int, nbytes: int):
     key = (device.index, stream_handle)
     t = _WORKSPACES.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WORKSPACES[key] = t
     return t
 
@@ -139,8 +138,9 @@ def run(p: PackedWeight, x, out=None, descriptor: Optional[B.i4s_packed] = None,
     """y = W_hat x for x of shape [batch][cols] (or [cols]) fp16 on the GPU.
 
     With ``use_workspace`` (the default) calls that can use one go through
-    ``i4s_run_ws`` with ``workspace`` (a zero-filled uint8 tensor) or a
-    cached per-stream workspace; otherwise through ``i4s_run``.
+    ``i4s_run_ws`` with ``workspace`` (a uint8 device tensor of at least
+    ``run_workspace_size`` bytes) or a cached per-stream workspace; otherwise
+    through ``i4s_run``.
     """
     torch = _torch()
     squeeze = x.dim() == 1

@@ -420,18 +420,27 @@ __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
 // ---------------------------------------------------------------------------
 // batch kernel on the sparse matrix cores with a K split across blocks
 //
-// Same matrix-core step as above, but a block owns 128 rows (8 waves x one
-// 16-row tile) and one slice of K.  The slice of x (batch vectors x the
-// slice's columns) is staged once in LDS and shared by the 8 tiles, so the
-// activations cross from L2 once per 128 rows instead of once per 16.  Each
-// block writes its 8 partial fp32 tiles to the caller's workspace; the block
-// that finishes a row group last (a per-group counter in the workspace) sums
-// the slices in slice order -- the result does not depend on which block is
-// last -- stores y and resets the counter to zero for the next call.
+// Same matrix-core step as above, but a block owns 256 rows (8 waves, each
+// two 16-row tiles) and one slice of K.  The slice of x (batch vectors x the
+// slice's columns) is staged once in LDS and shared by the 16 tiles, and
+// each B fragment a wave reads from LDS feeds the matrix steps of both of
+// its tiles.  A block writes its 16 partial fp32 tiles to the caller's
+// workspace with plain stores; a second, small kernel on the same stream sums
+// the slices in slice order (deterministic) and stores y.  The kernel
+// boundary makes the partials visible across the XCDs' L2 caches, so no
+// device-scope atomics, fences or counters are needed, and the workspace is
+// plain scratch.
+//
+// Order of issue per wave: the activation slice, the first block of weights
+// of both tiles, the LDS write of the slice (which waits for those loads
+// only), then every other weight load.  A wave with more loads outstanding
+// than its CU accepts stalls at issue, so this puts the slice in LDS before
+// the bulk of the weight stream; the barrier orders LDS only.
 
-constexpr int kSWaves = 8;              // tiles (waves) per block
-constexpr int kSRows = 16 * kSWaves;    // rows per block
-constexpr int kSMaxBlocks = 8;          // blocks of 4 units per slice (all loaded up front)
+constexpr int kSWaves = 8;                       // waves per block
+constexpr int kSTiles = 2;                       // 16-row tiles per wave
+constexpr int kSRows = 16 * kSTiles * kSWaves;   // 256 rows per block
+constexpr int kSMaxBlocks = 8;                   // blocks of 4 units per slice (all loaded up front)
 
 // Weight registers of one block of 4 units for one lane.
 struct WBlock {
@@ -440,142 +449,399 @@ struct WBlock {
   uint32_t s;
 };
 
+// partial tile index: slice ks, row group rg, tile t (0..15) of the group;
+// each tile is 64 lanes x 4 floats (lane j + 16q: rows 4q..4q+3, vector j)
+__device__ inline size_t split_tile(int ks, int ngrp, int rg, int t) {
+  return ((size_t)ks * ngrp + rg) * (kSWaves * kSTiles) + t;
+}
+
+// The activation slice is staged by ROUNDS loads per thread (two vectors per
+// round, 256 threads per vector, so ROUNDS = ceil(batch / 2)); NB = ups / 4
+// blocks of 4 units per tile.  Both are template parameters so that every
+// load is issued unconditionally (clamped indices) and the compiler can count
+// exactly the loads issued after the activations.
+template <int NB, int ROUNDS>
 __global__ __launch_bounds__(64 * kSWaves) void gemv_smfmac_split_kernel(
-    int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
+    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
-    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
-    uint16_t *__restrict__ y, uint32_t *__restrict__ counters, f4_t *__restrict__ partial,
-    int ksplit, int ups) {
+    const uint16_t *__restrict__ scales, const uint16_t *x, int batch,
+    uint16_t *__restrict__ y, f4_t *__restrict__ partial, int ksplit, int ups) {
   extern __shared__ __align__(16) uint16_t xs[];          // [batch][ups * 64 + 8]
-  __shared__ __align__(16) uint16_t scs[kSWaves][4][16];
-  __shared__ int last_block;
+  __shared__ __align__(16) uint16_t scs[kSWaves][kSTiles][4][16];
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
   const int li = lane % 16, lq = lane / 16;
   const int rg = blockIdx.x, ks = blockIdx.y, ngrp = gridDim.x;
-  const int row0 = rg * kSRows + 16 * wave;
-  const int units = cols / kSegCols;
+  const int cols = units * kSegCols;
   const int u0 = ks * ups, u1 = min(units, u0 + ups);
   const int xst = ups * kSegCols + 8;  // halfs per vector in LDS (16-byte pad)
-  const uint32_t nnz_row = (uint32_t)cols / 2;
-  const int sg = group_size / kSegCols;
-  const int sg_shift = sg == 1 ? 0 : (sg == 2 ? 1 : 2);
-  const uint32_t ngroups = (uint32_t)(cols / group_size);
+  const uint32_t nnz_row = (uint32_t)units * 32;
+  const uint32_t ngroups = (uint32_t)units >> sg_shift;
+  const int sgm = (1 << sg_shift) - 1;  // a group ends with unit u when ((u + 1) & sgm) == 0
 
-  const int arow = min(row0 + li, rows - 1);
-  uint32_t rstart = (uint32_t)arow * nnz_row;
+  // 1. the activation slice: vector 2r + (tid / 256), piece tid % 256 (16 B)
+  const int vpb = (u1 - u0) * (kSegCols / 8);  // pieces per vector, <= 256
+  const int xc = threadIdx.x % 256, xh = threadIdx.x / 256;
+  const int xcc = min(xc, vpb - 1);
+  u32x4_t xg[ROUNDS];  // a native vector type: one load, no struct copy
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int bv = min(2 * r + xh, batch - 1);
+    xg[r] = *reinterpret_cast<const u32x4_t *>(x + (int64_t)bv * cols + (int64_t)u0 * kSegCols + 8 * xcc);
+  }
+  // x is deliberately not __restrict__: its loads then stay ordered before
+  // the weight loads across the scheduling barriers below (invariant loads
+  // would float past them).
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. weights of the wave's two tiles (units past the slice re-read its last
+  // unit; their matrix steps are skipped)
+  int arow[kSTiles];
+  uint32_t rstart[kSTiles];
+#pragma unroll
+  for (int t = 0; t < kSTiles; ++t) {
+    arow[t] = min(rg * kSRows + (wave * kSTiles + t) * 16 + li, rows - 1);
+    rstart[t] = (uint32_t)arow[t] * nnz_row;
+  }
+  const int b0 = u0 / 4;
+  auto load = [&](WBlock &m, int t, int b, bool nt) {  // block b (units 4b..4b+3) of tile t
+    const int u = min(4 * b + lq, u1 - 1);
+    const uint32_t e0 = rstart[t] + (uint32_t)u * 32;
+    const uint32_t si = (uint32_t)arow[t] * ngroups + ((uint32_t)u >> sg_shift);
+    if (nt) {
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vals + (e0 >> 1)));
+      const u32x2_t c = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(codes + (e0 >> 3)));
+      m.v[0] = v.x; m.v[1] = v.y; m.v[2] = v.z; m.v[3] = v.w;
+      m.c[0] = c.x; m.c[1] = c.y;
+      m.s = __builtin_nontemporal_load(scales + si);
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4 *>(vals + (e0 >> 1));
+      const uint2 c = *reinterpret_cast<const uint2 *>(codes + (e0 >> 3));
+      m.v[0] = v.x; m.v[1] = v.y; m.v[2] = v.z; m.v[3] = v.w;
+      m.c[0] = c.x; m.c[1] = c.y;
+      m.s = scales[si];
+    }
+  };
+  WBlock mw[kSTiles][NB];
+#pragma unroll
+  for (int t = 0; t < kSTiles; ++t) load(mw[t][0], t, b0, true);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. the slice to LDS (threads with a clamped index write the same piece
+  // to the same place again), then the rest of the weight stream
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r)
+    *reinterpret_cast<u32x4_t *>(xs + min(2 * r + xh, batch - 1) * xst + 8 * xcc) = xg[r];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 1; i < NB; ++i)
+#pragma unroll
+    for (int t = 0; t < kSTiles; ++t) load(mw[t][i], t, b0 + i, true);
+  int32_t rp[kSTiles];
+#pragma unroll
+  for (int t = 0; t < kSTiles; ++t) rp[t] = row_ptr[arow[t]];
+  lds_barrier();  // orders LDS only: no wave waits here for its weights
+  __builtin_amdgcn_sched_barrier(0);
+
   // B lane (vector li, column quarter lq); lanes past `batch` read the last
   // real vector (their output columns are never stored)
   const uint16_t *xl = xs + min(li, batch - 1) * xst + 8 * lq;
-
-  auto load = [&](WBlock &m, int b) {  // weights of block b (units 4b..4b+3) of this tile
-    const int u = min(4 * b + lq, u1 - 1);
-    const uint32_t e0 = rstart + (uint32_t)u * 32;
-    const uint4 v = *reinterpret_cast<const uint4 *>(vals + (e0 >> 1));
-    const uint2 c = *reinterpret_cast<const uint2 *>(codes + (e0 >> 3));
-    m.v[0] = v.x; m.v[1] = v.y; m.v[2] = v.z; m.v[3] = v.w;
-    m.c[0] = c.x; m.c[1] = c.y;
-    m.s = scales[(uint32_t)arow * ngroups + ((uint32_t)u >> sg_shift)];
-  };
-
-  f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto process = [&](const WBlock &m, int b) {
-    uint32_t W0 = m.v[0], W1 = m.v[1], W2 = m.v[2], W3 = m.v[3], P, Q;
-    transpose4(W0, W1, W2, W3);
-    transpose_codes(m.c[0], m.c[1], P, Q);
-    scs[wave][lq][li] = (uint16_t)m.s;
-    f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+  f4_t acc[kSTiles];
+#pragma unroll
+  for (int t = 0; t < kSTiles; ++t) acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto process = [&](const WBlock (&m)[kSTiles], int b) {
+    uint32_t W[kSTiles][4], P[kSTiles], Q[kSTiles];
+    f4_t cg[kSTiles];
+#pragma unroll
+    for (int t = 0; t < kSTiles; ++t) {
+      W[t][0] = m[t].v[0]; W[t][1] = m[t].v[1]; W[t][2] = m[t].v[2]; W[t][3] = m[t].v[3];
+      transpose4(W[t][0], W[t][1], W[t][2], W[t][3]);
+      transpose_codes(m[t].c[0], m[t].c[1], P[t], Q[t]);
+      scs[wave][t][lq][li] = (uint16_t)m[t].s;
+      cg[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int u = 4 * b + s;
       if (u >= u1) break;
       const uint4 xa = *reinterpret_cast<const uint4 *>(xl + (u - u0) * kSegCols);
-      const uint4 xc = *reinterpret_cast<const uint4 *>(xl + (u - u0) * kSegCols + 32);
-      const u8_t xv = {xa.x, xa.y, xa.z, xa.w, xc.x, xc.y, xc.z, xc.w};
+      const uint4 xb = *reinterpret_cast<const uint4 *>(xl + (u - u0) * kSegCols + 32);
+      const u8_t xv = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
       const h16_t bx = __builtin_bit_cast(h16_t, xv);
-      if (s == 0) cg = smfmac_step<0>(W0, bx, cg, P, Q);
-      if (s == 1) cg = smfmac_step<1>(W1, bx, cg, P, Q);
-      if (s == 2) cg = smfmac_step<2>(W2, bx, cg, P, Q);
-      if (s == 3) cg = smfmac_step<3>(W3, bx, cg, P, Q);
-      if (((u + 1) & (sg - 1)) == 0) {
-        const uint2 sv = *reinterpret_cast<const uint2 *>(&scs[wave][s][4 * lq]);
-        acc[0] = fmaf(fp16_bits_to_float(sv.x & 0xFFFFu), cg[0], acc[0]);
-        acc[1] = fmaf(fp16_bits_to_float(sv.x >> 16), cg[1], acc[1]);
-        acc[2] = fmaf(fp16_bits_to_float(sv.y & 0xFFFFu), cg[2], acc[2]);
-        acc[3] = fmaf(fp16_bits_to_float(sv.y >> 16), cg[3], acc[3]);
-        cg = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < kSTiles; ++t) {
+        if (s == 0) cg[t] = smfmac_step<0>(W[t][0], bx, cg[t], P[t], Q[t]);
+        if (s == 1) cg[t] = smfmac_step<1>(W[t][1], bx, cg[t], P[t], Q[t]);
+        if (s == 2) cg[t] = smfmac_step<2>(W[t][2], bx, cg[t], P[t], Q[t]);
+        if (s == 3) cg[t] = smfmac_step<3>(W[t][3], bx, cg[t], P[t], Q[t]);
+      }
+      if (((s + 1) & sgm) == 0) {  // the group ends with this unit (slices start on 4-unit bounds)
+#pragma unroll
+        for (int t = 0; t < kSTiles; ++t) {
+          const uint2 sv = *reinterpret_cast<const uint2 *>(&scs[wave][t][s][4 * lq]);
+          acc[t][0] = fmaf(fp16_bits_to_float(sv.x & 0xFFFFu), cg[t][0], acc[t][0]);
+          acc[t][1] = fmaf(fp16_bits_to_float(sv.x >> 16), cg[t][1], acc[t][1]);
+          acc[t][2] = fmaf(fp16_bits_to_float(sv.y & 0xFFFFu), cg[t][2], acc[t][2]);
+          acc[t][3] = fmaf(fp16_bits_to_float(sv.y >> 16), cg[t][3], acc[t][3]);
+          cg[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
       }
     }
   };
 
-  // All of this tile's weights for the slice are requested at once, before
-  // the activations are staged, so the memory latency is paid once.
-  const int b0 = u0 / 4, nb = (u1 + 3) / 4 - b0;  // nb <= kSMaxBlocks
-  WBlock mw[kSMaxBlocks];
+  // 4. multiply as the weights arrive; the row_ptr check comes afterwards (a
+  // wave with a row stored away from the format's offset fetches its
+  // weights again and recomputes; the check is the same for the whole wave)
 #pragma unroll
-  for (int i = 0; i < kSMaxBlocks; ++i)
-    if (i < nb) load(mw[i], b0 + i);
-  const int32_t rp = row_ptr[arow];
-  {
-    const int vpb = (u1 - u0) * (kSegCols / 8);  // uint4 per vector
-    for (int i = threadIdx.x; i < batch * vpb; i += 64 * kSWaves) {
-      const int bv = i / vpb, c = i % vpb;
-      *reinterpret_cast<uint4 *>(xs + bv * xst + 8 * c) =
-          *reinterpret_cast<const uint4 *>(x + (int64_t)bv * cols + (int64_t)u0 * kSegCols + 8 * c);
+  for (int i = 0; i < NB; ++i) {
+    WBlock cur[kSTiles];
+#pragma unroll
+    for (int t = 0; t < kSTiles; ++t) cur[t] = mw[t][i];
+    process(cur, b0 + i);
+  }
+  bool moved = false;
+#pragma unroll
+  for (int t = 0; t < kSTiles; ++t) moved |= (uint32_t)rp[t] != rstart[t];
+  if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+    for (int t = 0; t < kSTiles; ++t) {
+      rstart[t] = (uint32_t)rp[t];
+      acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      WBlock cur[kSTiles];
+#pragma unroll
+      for (int t = 0; t < kSTiles; ++t) load(cur[t], t, b0 + i, false);
+      process(cur, b0 + i);
     }
   }
-  if ((uint32_t)rp != rstart) {  // a row stored elsewhere: re-fetch from row_ptr's offset
-    rstart = (uint32_t)rp;
-#pragma unroll
-    for (int i = 0; i < kSMaxBlocks; ++i)
-      if (i < nb) load(mw[i], b0 + i);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kSMaxBlocks; ++i)
-    if (i < nb) process(mw[i], b0 + i);
 
-  if (ksplit == 1) {  // no split: store directly
+  // 5. one slice: store y; several: the partial tiles (the columns of real
+  // vectors only)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 4 * lq + r;
-      if (li < batch && row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(acc[r]);
+  for (int t = 0; t < kSTiles; ++t) {
+    const int tile = wave * kSTiles + t;
+    if (ksplit == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rg * kSRows + tile * 16 + 4 * lq + r;
+        if (li < batch && row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(acc[t][r]);
+      }
+    } else if (li < batch) {
+      partial[split_tile(ks, ngrp, rg, tile) * 64 + lane] = acc[t];
     }
-    return;
   }
-  // Partial tile -> workspace, then the last block of the row group sums.
-  // The 8 XCDs' L2 caches are not coherent with each other, and a device-
-  // scope fence would write back and invalidate the whole L2; instead every
-  // access to the workspace is a device-scope atomic, performed at the
-  // memory-side coherence point, and the counter is bumped only after this
-  // block's partial stores have completed (s_waitcnt on outstanding stores,
-  // then the block barrier).
-  {
-    float *dst = reinterpret_cast<float *>(partial + ((size_t)(ks * ngrp + rg) * kSWaves + wave) * 64 + lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) __hip_atomic_store(dst + r, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // all of this wave's stores acknowledged
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_block = old == (uint32_t)(ksplit - 1);
-  }
-  __syncthreads();
-  if (!last_block) return;
+}
+
+// Sums the ksplit partial tiles of every row in slice order and stores y.
+// One thread per (row group, tile, lane); lanes of vectors past `batch` idle.
+__global__ __launch_bounds__(256) void gemv_split_reduce_kernel(
+    int rows, int batch, int ngrp, int ksplit, const f4_t *__restrict__ partial, uint16_t *__restrict__ y) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;  // < ngrp * 16 * 64 by the grid
+  const int lane = gid % 64, tile = (gid / 64) % (kSWaves * kSTiles), rg = gid / (64 * kSWaves * kSTiles);
+  const int li = lane % 16, lq = lane / 16;
+  if (li >= batch) return;
   f4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k = 0; k < ksplit; ++k) {
-    const float *src = reinterpret_cast<const float *>(partial + ((size_t)(k * ngrp + rg) * kSWaves + wave) * 64 + lane);
+  for (int k0 = 0; k0 < ksplit; k0 += 8) {  // up to 8 loads in flight, summed in slice order
+    f4_t part[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sum[r] += __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int k = 0; k < 8; ++k)
+      part[k] = partial[split_tile(min(k0 + k, ksplit - 1), ngrp, rg, tile) * 64 + lane];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k0 + k < ksplit) sum += part[k];
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int row = row0 + 4 * lq + r;
-    if (li < batch && row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(sum[r]);
+    const int row = rg * kSRows + tile * 16 + 4 * lq + r;
+    if (row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(sum[r]);
   }
-  if (threadIdx.x == 0)  // ready for the next call
-    __hip_atomic_store(&counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// batch kernel on the sparse matrix cores, one 16-row tile per block over the
+// whole of K (2:4, 2 <= batch <= 16, K <= 16384; no workspace)
+//
+// How the weights of a tile are read decides the rate (measured on MI355X on
+// a 13824x5120 layer): loads of 16 rows x 64 bytes per instruction -- the
+// layout the matrix step wants -- stream at ~1.9 TB/s, while loads of 4 rows
+// x 256 bytes per instruction, with each block covering whole rows, stream at
+// ~4.9 TB/s, as fast as the batch-1 kernel's whole-row loads.  So each wave
+// reads its 16-unit chunks of the tile's 16 rows in that shape (lane (u, r):
+// row 4k + r, unit u), writes them to a wave-private LDS area and reads them
+// back in the matrix layout (lane (i, kq): row i, unit 4b + kq), then goes
+// on as the other SMFMAC kernels (4x4 transposes across the lane groups, one
+// matrix step per unit, group scales on the fp32 tiles).  Only the wave
+// itself touches its area, so no barrier is needed until the waves' partial
+// tiles are summed in LDS at the end.  B fragments come from L2, two 4-unit
+// blocks ahead of the matrix steps.
+
+constexpr int kRUnits = 16;                  // units per chunk
+constexpr int kRMaxWaves = 8;                // 8 x 7040 bytes of LDS; 2 waves per SIMD
+constexpr int kRStride = kRUnits + 1;        // LDS row stride in elements (bank spread)
+constexpr int kRValsBytes = 16 * kRStride * 16;
+constexpr int kRCodesBytes = 16 * kRStride * 8;
+constexpr int kRWaveLds = kRValsBytes + kRCodesBytes + kRUnits * 16 * 2;  // 7040 bytes
+
+// CPW = 16-unit chunks per wave; waves per block = ceil(units / (16 * CPW)).
+// SG = units per quantization group (G / 64: 1, 2 or 4), so where a group
+// ends inside a block of 4 units is known at compile time.
+template <int CPW, int SG>
+__global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
+    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
+    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
+    uint16_t *__restrict__ y) {
+  extern __shared__ __align__(16) uint8_t lds[];  // [waves][kRWaveLds]
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nwaves = blockDim.x / 64;
+  const int li = lane % 16, lq = lane / 16;
+  const int row0 = blockIdx.x * 16;
+  const uint32_t nnz_row = (uint32_t)units * 32;
+  const uint32_t ngroups = (uint32_t)units >> sg_shift;
+  uint8_t *wl = lds + wave * kRWaveLds;
+  u32x4_t *lv = reinterpret_cast<u32x4_t *>(wl);                                 // [16 rows][17] vals
+  u32x2_t *lc = reinterpret_cast<u32x2_t *>(wl + kRValsBytes);                   // [16 rows][17] codes
+  uint16_t *lsc = reinterpret_cast<uint16_t *>(wl + kRValsBytes + kRCodesBytes);  // [16 units][16 rows]
+
+  // B fragments: lane (vector li, column quarter lq); vectors past `batch`
+  // read the last real one (their output columns are never stored).  Block
+  // n of the wave = units 4n..4n+3 of its chunks, in order.
+  const int cols = units * kSegCols;
+  const uint16_t *xrow = x + (int64_t)min(li, batch - 1) * cols + 8 * lq;
+  auto unit_of = [&](int n, int s) { return (wave * CPW + n / 4) * kRUnits + 4 * (n % 4) + s; };
+  auto load_b = [&](u32x4_t (&bx)[8], int n) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int u = min(unit_of(n, s), units - 1);
+      bx[2 * s] = *reinterpret_cast<const u32x4_t *>(xrow + u * kSegCols);
+      bx[2 * s + 1] = *reinterpret_cast<const u32x4_t *>(xrow + u * kSegCols + 32);
+    }
+  };
+
+  // every weight load of the wave: lane (unit li, row lq): row 4k + lq
+  int wrow[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) wrow[k] = min(row0 + 4 * k + lq, rows - 1);
+  u32x4_t bq[2][8];
+  load_b(bq[0], 0);
+  load_b(bq[1], 1);
+  u32x4_t wv[CPW][4];
+  u32x2_t wc[CPW][4];
+  uint16_t wsc[CPW][4];
+  auto load_w = [&](int c, const uint32_t (&base)[4], bool nt) {
+    const int u = min((wave * CPW + c) * kRUnits + li, units - 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t e0 = base[k] + (uint32_t)u * 32;
+      const uint32_t si = (uint32_t)wrow[k] * ngroups + ((uint32_t)u >> sg_shift);
+      if (nt) {
+        wv[c][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vals + (e0 >> 1)));
+        wc[c][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(codes + (e0 >> 3)));
+        wsc[c][k] = __builtin_nontemporal_load(scales + si);
+      } else {
+        wv[c][k] = *reinterpret_cast<const u32x4_t *>(vals + (e0 >> 1));
+        wc[c][k] = *reinterpret_cast<const u32x2_t *>(codes + (e0 >> 3));
+        wsc[c][k] = scales[si];
+      }
+    }
+  };
+  uint32_t base[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) base[k] = (uint32_t)wrow[k] * nnz_row;  // the format's offsets
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) load_w(c, base, true);
+  int32_t rp[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) rp[k] = row_ptr[wrow[k]];
+
+  // row_ptr check before the pass: row_ptr is the wave's last load and loads
+  // retire in order, so this waits for little beyond the weights the pass
+  // needs anyway.  A tile with a row stored away from the format's offset
+  // fetches its weights again from row_ptr's offsets (every wave of the
+  // block sees the same rows, so each decides alone).
+  bool moved = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) moved |= (uint32_t)rp[k] != base[k];
+  if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) base[k] = (uint32_t)rp[k];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) load_w(c, base, false);
+  }
+
+  // one pass over the wave's chunks; B fragments two blocks ahead
+  f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      // chunk c to the wave's LDS area, in the load layout
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        lv[(4 * k + lq) * kRStride + li] = wv[c][k];
+        lc[(4 * k + lq) * kRStride + li] = wc[c][k];
+        lsc[li * 16 + 4 * k + lq] = wsc[c][k];
+      }
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int n = 4 * c + bb;
+        u32x4_t (&bx)[8] = bq[n % 2];
+        // the matrix layout: lane (row li, chunk lq) takes unit 4bb + lq
+        const u32x4_t v = lv[li * kRStride + 4 * bb + lq];
+        const u32x2_t cw = lc[li * kRStride + 4 * bb + lq];
+        uint32_t W0 = v.x, W1 = v.y, W2 = v.z, W3 = v.w, P, Q;
+        transpose4(W0, W1, W2, W3);
+        transpose_codes(cw.x, cw.y, P, Q);
+        // the scales of the block's groups (rows 4lq..4lq+3 of each group's
+        // last unit), read before the matrix steps
+        u32x2_t sv[4 / SG];
+#pragma unroll
+        for (int g = 0; g < 4 / SG; ++g)
+          sv[g] = *reinterpret_cast<const u32x2_t *>(&lsc[(4 * bb + SG * g + SG - 1) * 16 + 4 * lq]);
+        f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int u = unit_of(n, s);
+          if (u >= units) break;  // only the last chunk of a row can end early, on a group bound
+          const u8_t xv = {bx[2 * s].x, bx[2 * s].y, bx[2 * s].z, bx[2 * s].w,
+                           bx[2 * s + 1].x, bx[2 * s + 1].y, bx[2 * s + 1].z, bx[2 * s + 1].w};
+          const h16_t hb = __builtin_bit_cast(h16_t, xv);
+          if (s == 0) cg = smfmac_step<0>(W0, hb, cg, P, Q);
+          if (s == 1) cg = smfmac_step<1>(W1, hb, cg, P, Q);
+          if (s == 2) cg = smfmac_step<2>(W2, hb, cg, P, Q);
+          if (s == 3) cg = smfmac_step<3>(W3, hb, cg, P, Q);
+          if ((s + 1) % SG == 0) {  // the group ends with this unit (chunks start on 4-unit bounds)
+            const u32x2_t g2 = sv[s / SG];
+            acc[0] = fmaf(fp16_bits_to_float(g2.x & 0xFFFFu), cg[0], acc[0]);
+            acc[1] = fmaf(fp16_bits_to_float(g2.x >> 16), cg[1], acc[1]);
+            acc[2] = fmaf(fp16_bits_to_float(g2.y & 0xFFFFu), cg[2], acc[2]);
+            acc[3] = fmaf(fp16_bits_to_float(g2.y >> 16), cg[3], acc[3]);
+            cg = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+        }
+        // the buffer just used takes block n + 2; the scheduling barriers keep
+        // the loads here, so only two buffers are ever live
+        __builtin_amdgcn_sched_barrier(0);
+        if (n + 2 < 4 * CPW) load_b(bx, n + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // sum the waves' partial tiles (each wave writes into its own area, which
+  // it no longer reads) and store y
+  f4_t *red = reinterpret_cast<f4_t *>(wl);
+  red[lane] = acc;
+  lds_barrier();
+  if (wave == 0) {
+    f4_t sum = acc;
+    for (int w = 1; w < nwaves; ++w) sum += reinterpret_cast<const f4_t *>(lds + w * kRWaveLds)[lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 4 * lq + r;
+      if (li < batch && row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(sum[r]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -595,24 +861,81 @@ hipError_t launch_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint1
   return hipGetLastError();
 }
 
+// I4S_ROWS_KERNEL=0 keeps the older tile kernel (tuning and cross-checks)
+bool rows_kernel_enabled() {
+  static const bool v = [] {
+    const char *e = getenv("I4S_ROWS_KERNEL");
+    return !(e && e[0] == '0');
+  }();
+  return v;
+}
+
 hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                          hipStream_t stream) {
+  const int units = w.cols / kSegCols;
+  const int chunks = (units + kRUnits - 1) / kRUnits;
+  // up to 8 waves of 1 or 2 chunks: K <= 16384
+  if (rows_kernel_enabled() && chunks <= 2 * kRMaxWaves) {
+    const int cpw = chunks > kRMaxWaves ? 2 : 1;
+    const int waves = (chunks + cpw - 1) / cpw;
+    const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
+    const dim3 grid((unsigned)((w.rows + 15) / 16)), block(64 * waves);
+    const size_t lds = (size_t)waves * kRWaveLds;
+#define I4S_ROWS(C, G) hipLaunchKernelGGL((gemv_smfmac_rows_kernel<C, G>), grid, block, lds, stream, w.rows, units, \
+                                          sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, batch, y)
+    if (cpw == 1) {
+      if (sg_shift == 0) I4S_ROWS(1, 1); else if (sg_shift == 1) I4S_ROWS(1, 2); else I4S_ROWS(1, 4);
+    } else {
+      if (sg_shift == 0) I4S_ROWS(2, 1); else if (sg_shift == 1) I4S_ROWS(2, 2); else I4S_ROWS(2, 4);
+    }
+#undef I4S_ROWS
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((w.rows + 15) / 16)), block(64 * kMWaves);
   hipLaunchKernelGGL(gemv_smfmac_kernel, grid, block, 0, stream, w.rows, w.cols, w.group_size, w.row_ptr,
                      w.vals, w.codes, w.scales, x, batch, y);
   return hipGetLastError();
 }
 
-hipError_t launch_smfmac_split(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
-                               const SplitPlan &pl, void *workspace, hipStream_t stream) {
-  uint8_t *ws = static_cast<uint8_t *>(workspace);
-  uint32_t *counters = reinterpret_cast<uint32_t *>(ws);
-  f4_t *partial = reinterpret_cast<f4_t *>(ws + pl.counter_bytes);
+template <int NB, int ROUNDS>
+hipError_t launch_split_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+                          const SplitPlan &pl, f4_t *partial, hipStream_t stream) {
   const size_t lds = (size_t)batch * (pl.ups * kSegCols + 8) * 2;
   const dim3 grid((unsigned)pl.row_groups, (unsigned)pl.ksplit), block(64 * kSWaves);
-  hipLaunchKernelGGL(gemv_smfmac_split_kernel, grid, block, lds, stream, w.rows, w.cols, w.group_size,
-                     w.row_ptr, w.vals, w.codes, w.scales, x, batch, y, counters, partial, pl.ksplit, pl.ups);
+  const int units = w.cols / kSegCols;
+  const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
+  hipLaunchKernelGGL((gemv_smfmac_split_kernel<NB, ROUNDS>), grid, block, lds, stream, w.rows, units, sg_shift,
+                     w.row_ptr, w.vals, w.codes, w.scales, x, batch, y, partial, pl.ksplit, pl.ups);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.ksplit == 1) return e;
+  const unsigned threads = (unsigned)pl.row_groups * kSWaves * kSTiles * 64;  // a multiple of 256
+  hipLaunchKernelGGL(gemv_split_reduce_kernel, dim3(threads / 256), dim3(256), 0, stream, w.rows, batch,
+                     pl.row_groups, pl.ksplit, partial, y);
   return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_split_nb(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+                           const SplitPlan &pl, f4_t *partial, hipStream_t stream) {
+  if (batch <= 2) return launch_split_t<NB, 1>(w, x, batch, y, pl, partial, stream);
+  if (batch <= 4) return launch_split_t<NB, 2>(w, x, batch, y, pl, partial, stream);
+  if (batch <= 8) return launch_split_t<NB, 4>(w, x, batch, y, pl, partial, stream);
+  return launch_split_t<NB, 8>(w, x, batch, y, pl, partial, stream);
+}
+
+hipError_t launch_smfmac_split(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+                               const SplitPlan &pl, void *workspace, hipStream_t stream) {
+  f4_t *partial = static_cast<f4_t *>(workspace);
+  switch (pl.ups / 4) {
+    case 1: return launch_split_nb<1>(w, x, batch, y, pl, partial, stream);
+    case 2: return launch_split_nb<2>(w, x, batch, y, pl, partial, stream);
+    case 3: return launch_split_nb<3>(w, x, batch, y, pl, partial, stream);
+    case 4: return launch_split_nb<4>(w, x, batch, y, pl, partial, stream);
+    case 5: return launch_split_nb<5>(w, x, batch, y, pl, partial, stream);
+    case 6: return launch_split_nb<6>(w, x, batch, y, pl, partial, stream);
+    case 7: return launch_split_nb<7>(w, x, batch, y, pl, partial, stream);
+    default: return launch_split_nb<8>(w, x, batch, y, pl, partial, stream);
+  }
 }
 
 // I4S_BATCH_PATH=valu forces the VALU batch kernel for 2:4 (tuning and
@@ -661,22 +984,20 @@ SplitPlan split_plan(const i4s_packed &w, int32_t batch) {
   if (ups > max_ups) ups = max_ups;
   pl.ups = ups;
   pl.ksplit = (units + ups - 1) / ups;
-  // The split pays for its cross-block reduction (three dependent trips to
-  // the memory-side coherence point, several microseconds) only when the
-  // activations would otherwise cross from L2 once per 16 rows for many rows
-  // or many columns: tall matrices, or wide ones at batch >= 8 (measured on
-  // the 13B-shaped layers).  Otherwise the barrier-free kernel runs and no
-  // workspace is needed.
-  const bool worth_it = pl.row_groups >= 64 || (units >= 128 && batch >= 8);
-  if (!worth_it || pl.row_groups > kSplitMaxRowGroups) return SplitPlan{};
-  if (pl.ksplit > 1) {
-    // The counters sit in a fixed region at the start of every workspace, so
-    // layers of any shape that share a workspace never see each other's
-    // partial tiles as counters; every completed call leaves that region zero.
-    pl.counter_bytes = kSplitCounterBytes;
-    pl.partial_bytes = (size_t)pl.ksplit * pl.row_groups * kSWaves * 64 * sizeof(float) * 4;
-  }
-  pl.workspace_bytes = pl.counter_bytes + pl.partial_bytes;
+  // When the split pays (measured on the 13B-shaped layers): the one-tile
+  // kernel reads its B fragments from L2, 32 loads per 16 units per wave at
+  // any batch, while the split kernel shares an LDS copy of x among 16 tiles.
+  // The split wins at batch > 8 and on long rows (K > 8192); below that the
+  // one-tile kernel (no workspace) is faster.  I4S_SPLIT=0 / 1 forces it off
+  // or on (tuning and cross-checks).
+  static const int split_env = [] {
+    const char *e = getenv("I4S_SPLIT");
+    return e ? (e[0] == '0' ? 0 : 1) : -1;
+  }();
+  const bool wanted = split_env >= 0 ? split_env == 1 : (batch > 8 || units > 128);
+  if (!wanted) return SplitPlan{};
+  if (pl.ksplit > 1) pl.partial_bytes = (size_t)pl.ksplit * pl.row_groups * kSWaves * kSTiles * 64 * sizeof(f4_t);
+  pl.workspace_bytes = pl.partial_bytes;
   return pl;
 }
 

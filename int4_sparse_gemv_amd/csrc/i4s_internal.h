@@ -50,17 +50,14 @@ hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch,
                        uint16_t *y, hipStream_t stream);
 
 // K split of the batch 2:4 GEMV across blocks (needs a caller workspace):
-// row_groups x ksplit blocks, ups 64-column units per slice.  Workspace:
-// [kSplitCounterBytes: one uint32 per row group, at fixed offsets for every
-// layer, zero between calls] [partial_bytes: fp32 partial tiles, scratch].
-// ksplit == 0 means "no split kernel" (batch 1, not 2:4, too few rows or
-// columns to pay for it, or more than kSplitMaxRowGroups row groups) and a
-// workspace of 0 bytes.
-constexpr size_t kSplitCounterBytes = 16384;
-constexpr int kSplitMaxRowGroups = (int)(kSplitCounterBytes / 4);
+// row_groups (of 256 rows) x ksplit blocks, ups 64-column units per slice.
+// The workspace holds the fp32 partial tiles of every slice (scratch: read
+// only after being written in the same call).  ksplit == 0 means "no split
+// kernel" (batch 1, not 2:4, or switched off) and a workspace of 0 bytes;
+// ksplit == 1 runs the split kernel without partials (0 bytes).
 struct SplitPlan {
   int row_groups = 0, ksplit = 0, ups = 0;
-  size_t counter_bytes = 0, partial_bytes = 0, workspace_bytes = 0;
+  size_t partial_bytes = 0, workspace_bytes = 0;
 };
 SplitPlan split_plan(const i4s_packed &w, int32_t batch);
 hipError_t launch_gemv_ws(const i4s_packed &w, const uint16_t *x, int32_t batch,
