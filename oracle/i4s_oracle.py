@@ -8,9 +8,11 @@ tables or helpers) and it never reads anything the GPU produced as an input.
 Source of every rule below: "Efficient LLM-based Advertising via Model
 Compression and Parallel Verification" (arXiv 2605.11582).
   * Section 3.2, "Sparsification" and Eq. (3): the element importance is
-    |W_ij|*||X_j||_2 + |W_ij|*|dE/dW_ij|.  With a constant activation norm and
-    no gradient term it orders elements by |W_ij|, which is the magnitude N:4
-    selection implemented here.
+    |W_ij|*||X_j||_2 + |W_ij|*|dE/dW_ij|; the N:4 mask keeps, per aligned group
+    of four columns, the N most important elements.  Without supplied
+    activation norms and gradients (a constant norm, no gradient term) it
+    orders elements by |W_ij| (magnitude pruning); with them, by the score
+    below.
   * Section 3.2, "Adaptive Group-Wise Quantization" and section 3.1: INT4
     weight-only quantization in groups whose size is chosen per layer.  The
     page does not give the selection rule; this oracle picks, per matrix, the
@@ -30,8 +32,16 @@ notes of the repository):
   * symmetric INT4: s = fp16_RNE(amax / 7); q = clamp(round_half_even(w / s),
     -8, 7); q = 0 where s == 0; the stored nibble is q + 8.
   * pruning happens on the fp16 weights before quantization; among equal
-    magnitudes the lower in-group column is kept; kept columns are listed in
-    ascending order.
+    magnitudes (or scores) the lower in-group column is kept; kept columns are
+    listed in ascending order.
+  * Eq. (3) is evaluated as |W_ij| * (n_j + |g_ij|), factored, in float32: the
+    sum n_j + |g_ij| is rounded once to float32 and the product once more
+    (round to nearest even).  n_j is the caller's float32 column norm
+    ||X_j||_2 (1 when none is given), g_ij the fp16 gradient (0 when none is
+    given); norms must be finite and non-negative, gradients finite.  A
+    product beyond float32's range is +inf (and ties other +inf scores).  A
+    defined precision is needed because the kept set is an exact decision;
+    with norms of 1 and no gradients the score is |W_ij| itself.
   * element order inside each 32-bit word of ``vals``: nibble slots 0..7 hold
     elements 0,2,4,6,1,3,5,7 of the word's 8 elements.
   * ``row_ptr[i] = i * K * N / 4`` (every row of an N:4 matrix has the same
@@ -65,7 +75,7 @@ class OracleError(ValueError):
 # validation
 
 
-def check_args(w16: np.ndarray, n_keep: int, group_size: int) -> None:
+def check_args(w16: np.ndarray, n_keep: int, group_size: int, col_norm=None, grad16=None) -> None:
     if w16.dtype != np.float16 or w16.ndim != 2:
         raise OracleError("W must be a 2-D float16 array")
     rows, cols = w16.shape
@@ -81,21 +91,51 @@ def check_args(w16: np.ndarray, n_keep: int, group_size: int) -> None:
             raise OracleError(f"cols={cols} is not a multiple of group size {g}")
     if not np.isfinite(w16).all():
         raise OracleError("W has a non-finite entry")
+    if col_norm is not None:
+        if col_norm.dtype != np.float32 or col_norm.shape != (cols,):
+            raise OracleError("column norms must be float32 of shape [cols]")
+        if not np.isfinite(col_norm).all() or (col_norm < 0).any():
+            raise OracleError("column norms must be finite and non-negative")
+    if grad16 is not None:
+        if grad16.dtype != np.float16 or grad16.shape != w16.shape:
+            raise OracleError("gradients must be float16 of W's shape")
+        if not np.isfinite(grad16).all():
+            raise OracleError("gradients must be finite")
 
 
 # --------------------------------------------------------------------------
-# step 1: N:4 magnitude mask (Eq. (3) with constant ||X_j|| and no gradient)
+# step 1: N:4 mask by the importance of Eq. (3)
 
 
-def nm_mask(w16: np.ndarray, n_keep: int) -> np.ndarray:
+def importance(w16: np.ndarray, col_norm=None, grad16=None) -> np.ndarray:
+    """Eq. (3), |W_ij| * ||X_j||_2 + |W_ij| * |dE/dW_ij|, as float32 scores.
+
+    Evaluated as |W_ij| * (n_j + |g_ij|) with one float32 rounding for the
+    sum and one for the product; n_j = 1 without norms, g_ij = 0 without
+    gradients.
+    """
+    rows, cols = w16.shape
+    n = np.ones(cols, np.float32) if col_norm is None else col_norm.astype(np.float32)
+    g = np.zeros((rows, cols), np.float32) if grad16 is None else np.abs(grad16.astype(np.float32))
+    a = (n[None, :] + g).astype(np.float32)  # float32 + float32: one rounding
+    with np.errstate(over="ignore"):          # a product past float32's range is +inf
+        return (np.abs(w16.astype(np.float32)) * a).astype(np.float32)
+
+
+def nm_mask(w16: np.ndarray, n_keep: int, col_norm=None, grad16=None) -> np.ndarray:
     """In-group columns kept per aligned group of 4 columns.
 
     Returns an int array [rows][cols/4][n_keep], ascending along the last
-    axis.  The kept set is the n_keep largest |w| of the group; among equal
-    magnitudes the smaller in-group column wins.
+    axis.  The kept set is the n_keep most important elements of the group
+    (by |w| when neither norms nor gradients are given, else by the float32
+    score of ``importance``); among equal values the smaller in-group column
+    wins.
     """
     rows, cols = w16.shape
-    mag = np.abs(w16.astype(np.float64)).reshape(rows, cols // 4, 4)
+    if col_norm is None and grad16 is None:
+        mag = np.abs(w16.astype(np.float64)).reshape(rows, cols // 4, 4)
+    else:
+        mag = importance(w16, col_norm, grad16).astype(np.float64).reshape(rows, cols // 4, 4)
     # a stable sort of -|w| lists equal magnitudes in ascending column order
     order = np.argsort(-mag, axis=-1, kind="stable")
     return np.sort(order[..., :n_keep], axis=-1)
@@ -229,17 +269,21 @@ def encode_codes(kept: np.ndarray) -> np.ndarray:
     return word.astype(np.uint16).reshape(-1)
 
 
-def pack(w16: np.ndarray, n_keep: int, group_size: int) -> Dict[str, object]:
+def pack(w16: np.ndarray, n_keep: int, group_size: int, col_norm=None, grad16=None) -> Dict[str, object]:
     """Prune, quantize and encode W; ``group_size`` 0 picks it per matrix.
+
+    ``col_norm`` (float32 [cols], the activation norms ||X_j||_2) and
+    ``grad16`` (float16, W's shape, dE/dW) are the optional inputs of Eq. (3);
+    without them the mask is by magnitude.
 
     Returns a dict with the four buffers (``row_ptr`` int32, ``vals`` uint8,
     ``codes`` uint16 (empty when n_keep == 4), ``scales`` uint16 fp16 bits),
     the shape and pattern, the group size used and, when chosen adaptively,
     the exact SSE of each candidate in units of 2**-48.
     """
-    check_args(w16, n_keep, group_size)
+    check_args(w16, n_keep, group_size, col_norm, grad16)
     rows, cols = w16.shape
-    kept = nm_mask(w16, n_keep)
+    kept = nm_mask(w16, n_keep, col_norm, grad16)
     val, _ = element_stream(w16, kept)
     sse: Dict[int, int] = {}
     if group_size == 0:

@@ -50,6 +50,25 @@ def round_fraction_to_fp16(v: Fraction) -> Fraction:
     return n * ulp
 
 
+def round_fraction_to_fp32(v: Fraction) -> Fraction:
+    """Round a non-negative rational to the nearest float32, ties to even mantissa."""
+    assert v >= 0
+    if v == 0:
+        return Fraction(0)
+    e = -126
+    while v >= Fraction(2) ** (e + 1) and e < 127:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    m = v / ulp
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    if n * ulp >= Fraction(2) ** 128:
+        return None                         # overflows to +inf
+    return n * ulp
+
+
 def round_half_even(v: Fraction) -> int:
     n = v.numerator // v.denominator
     rem = v - n
@@ -239,6 +258,100 @@ def check_gemv_exact_small(seed=4):
             if abs(Fraction(float(a[b, i])) - absum) > Fraction(1, 10 ** 12) * (absum + 1):
                 return False
     return True
+
+
+CASES = ("A", "B", "C", "D", "E", "F")
+
+
+def check_golden_importance():
+    """Hand-worked masks of Eq. (3) with norms and gradients."""
+    fx = read_fixture("importance_cases.txt")
+    for c in CASES:
+        w = np.array([float(v) for v in fx[c + "_w"]], np.float16).reshape(1, 8)
+        n = np.array([float(v) for v in fx[c + "_norm"]], np.float32)
+        g = np.array([float(v) for v in fx[c + "_grad"]], np.float16).reshape(1, 8)
+        n_keep = int(fx[c + "_n"][0])
+        want = [int(v) for v in fx[c + "_kept"]]
+        if O.nm_mask(w, n_keep, n, g).reshape(-1).tolist() != want:
+            return False
+    return True
+
+
+def check_importance_exact(seed=20, rows=7, cols=96):
+    """Scores equal fp32(|w| * fp32(n + |g|)) computed with exact rationals."""
+    rng = np.random.default_rng(seed)
+    w = random_fp16(rng, (rows, cols), 1.0)
+    w[0, :6] = np.float16([0.0, -0.0, 6e-8, -65504, 1e-5, 2.0 ** -14])
+    n = (np.exp2(rng.uniform(-30, 30, cols)) * rng.uniform(0.5, 1.0, cols)).astype(np.float32)
+    n[:3] = np.float32([0.0, 1.0, 3.4e38])
+    g = random_fp16(rng, (rows, cols), 4.0)
+    g[1, :4] = np.float16([65504, -65504, 6e-8, -0.0])
+    got = O.importance(w, n, g)
+    if got.dtype != np.float32 or got.shape != (rows, cols):
+        return False
+    for i in range(rows):
+        for j in range(cols):
+            a = round_fraction_to_fp32(Fraction(float(n[j])) + abs(Fraction(float(g[i, j]))))
+            want = round_fraction_to_fp32(abs(Fraction(float(w[i, j]))) * a)
+            if want is None:
+                if not np.isposinf(got[i, j]):
+                    return False
+            elif not np.isfinite(got[i, j]) or Fraction(float(got[i, j])) != want:
+                return False
+    return True
+
+
+def _bruteforce_kept(scores, n_keep):
+    """Max-sum subset of 4 exact scores, lexicographically smallest on ties."""
+    best = None
+    for sub in itertools.combinations(range(4), n_keep):
+        s = sum(scores[c] for c in sub)
+        if best is None or s > best[0]:
+            best = (s, sub)
+    return best[1]
+
+
+def check_importance_mask_bruteforce(seed=21, rows=5, cols=64):
+    """Tie-heavy exact inputs: no rounding, so the mask is the brute force's."""
+    rng = np.random.default_rng(seed)
+    w = rng.integers(-3, 4, size=(rows, cols)).astype(np.float16)
+    n = rng.choice(np.float32([0.0, 0.5, 1.0, 2.0, 3.0]), cols)
+    g = rng.choice(np.float16([0.0, 0.5, -0.5, 1.0, -1.0]), (rows, cols))
+    for n_keep in (1, 2, 4):
+        kept = O.nm_mask(w, n_keep, n, g)
+        for i in range(rows):
+            for t in range(cols // 4):
+                sc = [abs(Fraction(float(w[i, 4 * t + c]))) *
+                      (Fraction(float(n[4 * t + c])) + abs(Fraction(float(g[i, 4 * t + c]))))
+                      for c in range(4)]
+                if tuple(int(c) for c in kept[i, t]) != _bruteforce_kept(sc, n_keep):
+                    return False
+    return True
+
+
+def check_importance_mask_continuous(seed=22, rows=16, cols=256):
+    """Continuous inputs: the mask equals the one the exact (unrounded) Eq. (3)
+    scores give wherever the N-th and (N+1)-th exact scores of a group are
+    separated by more than float32 rounding can bridge."""
+    rng = np.random.default_rng(seed)
+    w = random_fp16(rng, (rows, cols), 1.0)
+    n = np.exp2(rng.uniform(-3, 3, cols)).astype(np.float32)
+    g = random_fp16(rng, (rows, cols), 2.0)
+    checked = 0
+    for n_keep in (1, 2):
+        kept = O.nm_mask(w, n_keep, n, g)
+        for i in range(rows):
+            for t in range(cols // 4):
+                sc = [abs(Fraction(float(w[i, 4 * t + c]))) *
+                      (Fraction(float(n[4 * t + c])) + abs(Fraction(float(g[i, 4 * t + c]))))
+                      for c in range(4)]
+                srt = sorted(sc, reverse=True)
+                if srt[n_keep - 1] - srt[n_keep] <= Fraction(1, 1 << 20) * srt[n_keep - 1]:
+                    continue
+                checked += 1
+                if tuple(int(c) for c in kept[i, t]) != _bruteforce_kept(sc, n_keep):
+                    return False
+    return checked > 1000
 
 
 # ---------------------------------------------------------------------------
@@ -442,6 +555,75 @@ def test_dense_pattern_is_plain_group_rtn():
                 assert Fraction(float(w_hat[i, gi * 128 + j])) == s * q
 
 
+def test_golden_importance_cases():
+    assert check_golden_importance()
+
+
+def test_importance_scores_exact_in_float32():
+    assert check_importance_exact()
+
+
+def test_importance_mask_matches_bruteforce_on_exact_inputs():
+    assert check_importance_mask_bruteforce()
+
+
+def test_importance_mask_matches_exact_scores_outside_near_ties():
+    assert check_importance_mask_continuous()
+
+
+def test_unit_norms_without_gradients_reduce_to_magnitude():
+    rng = np.random.default_rng(23)
+    ties = rng.integers(-3, 4, size=(6, 128)).astype(np.float16)
+    for w in (random_fp16(rng, (12, 256)), ties):
+        ones = np.ones(w.shape[1], np.float32)
+        zeros = np.zeros(w.shape, np.float16)
+        for n_keep in (1, 2, 4):
+            want = O.nm_mask(w, n_keep)
+            assert np.array_equal(O.nm_mask(w, n_keep, ones), want)
+            assert np.array_equal(O.nm_mask(w, n_keep, ones, zeros), want)
+            assert np.array_equal(O.nm_mask(w, n_keep, None, zeros), want)
+    w = random_fp16(rng, (4, 128))
+    a = O.pack(w, 2, 64)
+    b = O.pack(w, 2, 64, np.ones(128, np.float32), np.zeros(w.shape, np.float16))
+    for k in ("row_ptr", "vals", "codes", "scales"):
+        assert np.array_equal(a[k], b[k])
+
+
+def test_importance_mask_invariant_under_power_of_two_scaling():
+    # multiplying every norm and gradient by 2^k multiplies every score by 2^k
+    # exactly (no overflow or underflow here), so the mask cannot change
+    rng = np.random.default_rng(24)
+    w = random_fp16(rng, (8, 128), 1.0)
+    n = np.exp2(rng.uniform(-2, 2, 128)).astype(np.float32)
+    g = random_fp16(rng, (8, 128), 1.0)
+    for n_keep in (1, 2):
+        base = O.nm_mask(w, n_keep, n, g)
+        for k in (-3, 5):
+            f = 2.0 ** k
+            assert np.array_equal(O.nm_mask(w, n_keep, (n * f).astype(np.float32),
+                                            (g.astype(np.float32) * f).astype(np.float16)), base)
+
+
+def test_importance_pack_keeps_only_selected_elements():
+    rng = np.random.default_rng(25)
+    w = random_fp16(rng, (6, 128), 1.0)
+    n = np.exp2(rng.uniform(-4, 4, 128)).astype(np.float32)
+    g = random_fp16(rng, (6, 128), 1.0)
+    p = O.pack(w, 2, 64, n, g)
+    kept = O.nm_mask(w, 2, n, g)
+    w_hat = O.reconstruct(p)
+    mask = np.zeros((6, 32, 4), bool)
+    np.put_along_axis(mask, kept, True, axis=-1)
+    assert not w_hat.reshape(6, 32, 4)[~mask].any()
+    # the kept elements quantize exactly as a magnitude pack of the same
+    # kept values would: zero the pruned entries and pack by magnitude
+    w2 = np.where(mask.reshape(6, 128), w, np.float16(0))
+    q = O.pack(w2, 2, 64)
+    # a group where the pruned entries are zero may break ties differently,
+    # so compare reconstructions, which only hold kept values
+    assert np.array_equal(O.reconstruct(q), w_hat)
+
+
 def test_check_args_rejects_bad_input():
     ok = np.zeros((2, 128), np.float16)
     with pytest.raises(O.OracleError):
@@ -454,6 +636,18 @@ def test_check_args_rejects_bad_input():
     bad[1, 5] = np.inf
     with pytest.raises(O.OracleError):
         O.pack(bad, 2, 64)
+    good_n = np.ones(128, np.float32)
+    for n in (np.ones(127, np.float32), np.ones(128, np.float64),
+              np.where(np.arange(128) == 3, -1.0, 1.0).astype(np.float32),
+              np.where(np.arange(128) == 3, np.nan, 1.0).astype(np.float32),
+              np.where(np.arange(128) == 3, np.inf, 1.0).astype(np.float32)):
+        with pytest.raises(O.OracleError):
+            O.pack(ok, 2, 64, n)
+    for g in (np.zeros((2, 64), np.float16), np.zeros((2, 128), np.float32),
+              np.where(np.arange(256).reshape(2, 128) == 7, np.inf, 0).astype(np.float16)):
+        with pytest.raises(O.OracleError):
+            O.pack(ok, 2, 64, good_n, g)
+    O.pack(ok, 2, 64, good_n, np.zeros((2, 128), np.float16))
 
 
 # ---------------------------------------------------------------------------
@@ -466,7 +660,7 @@ def _swap(monkeypatch, name, fn):
 def test_planted_mask_tiebreak_is_caught(monkeypatch):
     real = O.nm_mask
 
-    def upper_wins(w16, n_keep):
+    def upper_wins(w16, n_keep, col_norm=None, grad16=None):
         rows, cols = w16.shape
         mag = np.abs(w16.astype(np.float64)).reshape(rows, cols // 4, 4)[..., ::-1]
         order = 3 - np.argsort(-mag, axis=-1, kind="stable")
@@ -556,3 +750,59 @@ def test_planted_transposed_gemv_is_caught(monkeypatch):
     w_hat = O.reconstruct(p)
     y, _ = O.gemv(w_hat, np.eye(64, dtype=np.float16))
     assert not np.array_equal(y, w_hat.T)
+
+
+def _planted_importance(monkeypatch, fn):
+    monkeypatch.setattr(O, "importance", fn)
+    caught = [not check_golden_importance(), not check_importance_exact(),
+              not check_importance_mask_bruteforce(), not check_importance_mask_continuous()]
+    return any(caught)
+
+
+def test_planted_importance_gradient_not_scaled_by_weight_is_caught(monkeypatch):
+    def unscaled(w16, col_norm=None, grad16=None):
+        rows, cols = w16.shape
+        n = np.ones(cols, np.float32) if col_norm is None else col_norm
+        g = np.zeros((rows, cols), np.float32) if grad16 is None else np.abs(grad16.astype(np.float32))
+        return (np.abs(w16.astype(np.float32)) * n[None, :] + g).astype(np.float32)
+    assert _planted_importance(monkeypatch, unscaled)
+
+
+def test_planted_importance_squared_norm_is_caught(monkeypatch):
+    def squared(w16, col_norm=None, grad16=None):
+        rows, cols = w16.shape
+        n = np.ones(cols, np.float32) if col_norm is None else col_norm * col_norm
+        g = np.zeros((rows, cols), np.float32) if grad16 is None else np.abs(grad16.astype(np.float32))
+        return (np.abs(w16.astype(np.float32)) * (n[None, :] + g)).astype(np.float32)
+    assert _planted_importance(monkeypatch, squared)
+
+
+def test_planted_importance_signed_gradient_is_caught(monkeypatch):
+    def signed(w16, col_norm=None, grad16=None):
+        rows, cols = w16.shape
+        n = np.ones(cols, np.float32) if col_norm is None else col_norm
+        g = np.zeros((rows, cols), np.float32) if grad16 is None else grad16.astype(np.float32)
+        return (np.abs(w16.astype(np.float32)) * (n[None, :] + g)).astype(np.float32)
+    assert _planted_importance(monkeypatch, signed)
+
+
+def test_planted_importance_unfactored_rounding_is_caught(monkeypatch):
+    # |w|*n + |w|*|g| rounds three times instead of twice: same real value,
+    # different float32 scores
+    def unfactored(w16, col_norm=None, grad16=None):
+        rows, cols = w16.shape
+        n = np.ones(cols, np.float32) if col_norm is None else col_norm
+        g = np.zeros((rows, cols), np.float32) if grad16 is None else np.abs(grad16.astype(np.float32))
+        a = np.abs(w16.astype(np.float32))
+        return (a * n[None, :] + a * g).astype(np.float32)
+    monkeypatch.setattr(O, "importance", unfactored)
+    assert not check_importance_exact()
+
+
+def test_planted_importance_norm_per_row_is_caught(monkeypatch):
+    def per_row(w16, col_norm=None, grad16=None):
+        rows, cols = w16.shape
+        n = np.ones(rows, np.float32) if col_norm is None else np.resize(col_norm, rows)
+        g = np.zeros((rows, cols), np.float32) if grad16 is None else np.abs(grad16.astype(np.float32))
+        return (np.abs(w16.astype(np.float32)) * (n[:, None] + g)).astype(np.float32)
+    assert _planted_importance(monkeypatch, per_row)
