@@ -5,9 +5,11 @@
  * What is computed follows "Efficient LLM-based Advertising via Model
  * Compression and Parallel Verification" (arXiv 2605.11582):
  *   - section 3.2, "Sparsification", Eq. (3): N:M pruning by element
- *     importance; with a constant activation norm and no gradient term the
- *     importance is |W_ij|, so each aligned group of 4 columns keeps its
- *     n_keep largest-magnitude weights (2 for 2:4, 1 for 1:4, 4 = dense);
+ *     importance |W_ij| * ||X_j||_2 + |W_ij| * |dE/dW_ij|; each aligned
+ *     group of 4 columns keeps its n_keep most important weights (2 for 2:4,
+ *     1 for 1:4, 4 = dense).  i4s_pack takes a constant activation norm and
+ *     no gradient term, so the importance is |W_ij|; i4s_pack_ex takes the
+ *     norms and gradients from the caller;
  *   - section 3.1 and 3.2, "Adaptive Group-Wise Quantization": symmetric INT4
  *     weight-only quantization with a group size chosen per layer;
  *   - section 3.3, "Sparse Index Structure": CSR rows whose column index is a
@@ -136,6 +138,32 @@ i4s_status i4s_pack(const uint16_t *w_fp16, int32_t rows, int32_t cols,
                     uint64_t workspace_bytes, i4s_packed *inout /* host */,
                     i4s_pack_report *report /* host, may be NULL */,
                     void *stream);
+
+/* i4s_pack with the full importance score of Eq. (3) of the page (section
+ * 3.2): |W_ij| * ||X_j||_2 + |W_ij| * |dE/dW_ij|.  The N:4 mask keeps the
+ * n_keep elements of each aligned group of four columns with the largest
+ * score, evaluated as |W_ij| * (n_j + |g_ij|) in fp32 with the sum and the
+ * product each rounded to nearest even; among equal scores the lower column
+ * is kept.  Same arguments and behaviour as i4s_pack plus:
+ *   col_norm  : device, [cols] fp32 activation norms ||X_j||_2, 16-byte
+ *               aligned, or NULL for n_j = 1.  Finite and >= 0 (-0 allowed).
+ *   grad_fp16 : device, [rows][cols] fp16 bits of dE/dW, row-major, 16-byte
+ *               aligned, or NULL for g_ij = 0.  Finite.
+ * Both NULL gives exactly i4s_pack's magnitude mask, and so do norms that are
+ * all 1 without gradients.  Only the mask depends on them: the kept weights
+ * are quantized and encoded as in i4s_pack.  A score beyond fp32's range is
+ * +inf and ties other +inf scores.  Both inputs are only read.
+ * Errors: as i4s_pack, plus I4S_ERR_INVALID_ARGUMENT for a misaligned
+ * col_norm or grad_fp16, a negative or non-finite norm or a non-finite
+ * gradient (detected on the device; a non-finite weight is reported first). */
+i4s_status i4s_pack_ex(const uint16_t *w_fp16, int32_t rows, int32_t cols,
+                       int32_t n_keep, int32_t group_size,
+                       const float *col_norm /* device, may be NULL */,
+                       const uint16_t *grad_fp16 /* device, may be NULL */,
+                       void *workspace, uint64_t workspace_bytes,
+                       i4s_packed *inout /* host */,
+                       i4s_pack_report *report /* host, may be NULL */,
+                       void *stream);
 
 /* y = W_hat x for `batch` activation vectors (section 3.3 of the page: the
  * SparseGemv kernel over the 2-bit CSR format).

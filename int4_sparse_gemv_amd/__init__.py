@@ -1,6 +1,7 @@
 """INT4 2-bit-CSR SparseGEMV for AMD Instinct MI355X (gfx950).
 
-``pack`` prunes (N:4 by magnitude), quantizes (symmetric INT4, fp16 group
+``pack`` prunes (N:4 by magnitude, or by the full Eq. (3) importance when
+column norms and/or gradients are given), quantizes (symmetric INT4, fp16 group
 scales, group size fixed or chosen per matrix by minimum SSE) and encodes a
 dense fp16 weight; ``run`` computes y = W_hat x for 1-16 fp16 vectors.  Both
 call the HIP kernels of ``libi4s.so`` through its C ABI (``include/i4s.h``);
@@ -18,12 +19,12 @@ import ctypes
 
 from . import _binding as B
 from ._binding import (  # noqa: F401  (the C names)
-    I4SError, i4s_format_version, i4s_last_error, i4s_pack, i4s_pack_sizes, i4s_run,
+    I4SError, i4s_format_version, i4s_last_error, i4s_pack, i4s_pack_ex, i4s_pack_sizes, i4s_run,
     i4s_run_workspace_size, i4s_run_ws, i4s_status_string, i4s_version,
 )
 
 __all__ = ["PackedWeight", "pack", "run", "pack_sizes", "run_workspace_size", "I4SError",
-           "i4s_pack_sizes", "i4s_pack", "i4s_run", "i4s_run_workspace_size", "i4s_run_ws",
+           "i4s_pack_sizes", "i4s_pack", "i4s_pack_ex", "i4s_run", "i4s_run_workspace_size", "i4s_run_ws",
            "i4s_status_string", "i4s_last_error", "i4s_version", "i4s_format_version"]
 
 
@@ -79,13 +80,27 @@ class PackedWeight:
         return self.nnz // 2 + codes + 2 * self.rows * (self.cols // self.group_size) + 4 * (self.rows + 1)
 
 
-def pack(w, n_keep: int = 2, group_size: int = 128) -> PackedWeight:
-    """Pack a [rows][cols] fp16 CUDA tensor.  group_size 0 chooses G per matrix."""
+def pack(w, n_keep: int = 2, group_size: int = 128, col_norm=None, grad=None) -> PackedWeight:
+    """Pack a [rows][cols] fp16 CUDA tensor.  group_size 0 chooses G per matrix.
+
+    ``col_norm`` (float32 [cols], the activation norms ||X_j||_2) and
+    ``grad`` (float16 [rows][cols], dE/dW) are the optional inputs of the
+    Eq. (3) importance score (``i4s_pack_ex``); without them the mask is by
+    magnitude (``i4s_pack``).
+    """
     torch = _torch()
     if w.dtype != torch.float16 or w.dim() != 2 or not w.is_cuda:
         raise ValueError("w must be a 2-D float16 tensor on a GPU")
     w = w.contiguous()
     rows, cols = w.shape
+    if col_norm is not None:
+        if col_norm.dtype != torch.float32 or tuple(col_norm.shape) != (cols,) or col_norm.device != w.device:
+            raise ValueError("col_norm must be a float32 [cols] tensor on w's device")
+        col_norm = col_norm.contiguous()
+    if grad is not None:
+        if grad.dtype != torch.float16 or tuple(grad.shape) != (rows, cols) or grad.device != w.device:
+            raise ValueError("grad must be a float16 tensor of w's shape on w's device")
+        grad = grad.contiguous()
     sz = pack_sizes(rows, cols, n_keep, group_size)
     dev = w.device
     row_ptr = torch.empty(sz["row_ptr"] // 4, dtype=torch.int32, device=dev)
@@ -99,8 +114,14 @@ def pack(w, n_keep: int = 2, group_size: int = 128) -> PackedWeight:
     d.scales = scales.data_ptr()
     rep = B.i4s_pack_report()
     with torch.cuda.device(dev):
-        st = B.i4s_pack(w.data_ptr(), rows, cols, n_keep, group_size, ws.data_ptr(), sz["workspace"],
-                        d, rep, _stream_handle(dev))
+        if col_norm is None and grad is None:
+            st = B.i4s_pack(w.data_ptr(), rows, cols, n_keep, group_size, ws.data_ptr(), sz["workspace"],
+                            d, rep, _stream_handle(dev))
+        else:
+            st = B.i4s_pack_ex(w.data_ptr(), rows, cols, n_keep, group_size,
+                               col_norm.data_ptr() if col_norm is not None else None,
+                               grad.data_ptr() if grad is not None else None,
+                               ws.data_ptr(), sz["workspace"], d, rep, _stream_handle(dev))
     B.check(st, "i4s_pack")
     g = d.group_size
     scales = scales[: rows * (cols // g)]

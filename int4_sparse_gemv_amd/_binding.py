@@ -67,6 +67,10 @@ SIGNATURES = {
                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_uint64,
                                 ctypes.POINTER(i4s_packed), ctypes.POINTER(i4s_pack_report),
                                 ctypes.c_void_p]),
+    "i4s_pack_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_uint64, ctypes.POINTER(i4s_packed),
+                                   ctypes.POINTER(i4s_pack_report), ctypes.c_void_p]),
     "i4s_run": (ctypes.c_int, [ctypes.POINTER(i4s_packed), ctypes.c_void_p, ctypes.c_int32,
                                ctypes.c_void_p, ctypes.c_void_p]),
     "i4s_run_workspace_size": (ctypes.c_int, [ctypes.POINTER(i4s_packed), ctypes.c_int32,
@@ -121,6 +125,13 @@ def i4s_pack(w_ptr, rows, cols, n_keep, group_size, ws_ptr, ws_bytes, inout, rep
     rep = ctypes.byref(report) if report is not None else None
     return load().i4s_pack(w_ptr, rows, cols, n_keep, group_size, ws_ptr, ws_bytes,
                            ctypes.byref(inout), rep, stream)
+
+
+def i4s_pack_ex(w_ptr, rows, cols, n_keep, group_size, norm_ptr, grad_ptr, ws_ptr, ws_bytes, inout,
+                report, stream):
+    rep = ctypes.byref(report) if report is not None else None
+    return load().i4s_pack_ex(w_ptr, rows, cols, n_keep, group_size, norm_ptr, grad_ptr, ws_ptr,
+                              ws_bytes, ctypes.byref(inout), rep, stream)
 
 
 def i4s_run(packed, x_ptr, batch, y_ptr, stream):

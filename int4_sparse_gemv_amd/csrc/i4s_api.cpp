@@ -113,10 +113,20 @@ i4s_status i4s_pack_sizes(int32_t rows, int32_t cols, int32_t n_keep, int32_t gr
 i4s_status i4s_pack(const uint16_t *w_fp16, int32_t rows, int32_t cols, int32_t n_keep,
                     int32_t group_size, void *workspace, uint64_t workspace_bytes,
                     i4s_packed *inout, i4s_pack_report *report, void *stream) {
+  return i4s_pack_ex(w_fp16, rows, cols, n_keep, group_size, nullptr, nullptr, workspace,
+                     workspace_bytes, inout, report, stream);
+}
+
+i4s_status i4s_pack_ex(const uint16_t *w_fp16, int32_t rows, int32_t cols, int32_t n_keep,
+                       int32_t group_size, const float *col_norm, const uint16_t *grad_fp16,
+                       void *workspace, uint64_t workspace_bytes, i4s_packed *inout,
+                       i4s_pack_report *report, void *stream) {
   i4s_sizes sz;
   i4s_status st = i4s_pack_sizes(rows, cols, n_keep, group_size, &sz);
   if (st != I4S_OK) return st;
   if (!w_fp16 || !aligned(w_fp16, 16)) return fail(I4S_ERR_INVALID_ARGUMENT, "w_fp16 is NULL or not 16-byte aligned");
+  if (col_norm && !aligned(col_norm, 16)) return fail(I4S_ERR_INVALID_ARGUMENT, "col_norm is not 16-byte aligned");
+  if (grad_fp16 && !aligned(grad_fp16, 16)) return fail(I4S_ERR_INVALID_ARGUMENT, "grad_fp16 is not 16-byte aligned");
   if (!inout) return fail(I4S_ERR_INVALID_ARGUMENT, "inout is NULL");
   if (!inout->row_ptr || !aligned(inout->row_ptr, 16) || !inout->vals || !aligned(inout->vals, 16) ||
       !inout->scales || !aligned(inout->scales, 16))
@@ -132,7 +142,7 @@ i4s_status i4s_pack(const uint16_t *w_fp16, int32_t rows, int32_t cols, int32_t 
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool adaptive = group_size == 0;
-  hipError_t e = i4s::launch_pack_analyze(w_fp16, rows, cols, n_keep, adaptive, workspace, s);
+  hipError_t e = i4s::launch_pack_analyze(w_fp16, col_norm, grad_fp16, rows, cols, n_keep, adaptive, workspace, s);
   if (e != hipSuccess) return device_error(e, "pack analyze launch");
   uint64_t head[i4s::kWsPartialsOffset / 8];
   e = hipMemcpyAsync(head, workspace, sizeof(head), hipMemcpyDeviceToHost, s);
@@ -141,7 +151,10 @@ i4s_status i4s_pack(const uint16_t *w_fp16, int32_t rows, int32_t cols, int32_t 
   if (e != hipSuccess) return device_error(e, "pack synchronize");
   uint32_t flag;
   std::memcpy(&flag, reinterpret_cast<const uint8_t *>(head) + i4s::kWsFlagOffset, 4);
-  if (flag) return fail(I4S_ERR_NONFINITE_WEIGHT, "W holds an Inf or NaN");
+  if (flag & i4s::kPackFlagNonfiniteWeight) return fail(I4S_ERR_NONFINITE_WEIGHT, "W holds an Inf or NaN");
+  if (flag & i4s::kPackFlagBadNorm)
+    return fail(I4S_ERR_INVALID_ARGUMENT, "col_norm holds a negative, infinite or NaN value");
+  if (flag & i4s::kPackFlagBadGrad) return fail(I4S_ERR_INVALID_ARGUMENT, "grad_fp16 holds an Inf or NaN");
 
   U128 sse[3] = {};
   int32_t g = group_size;
@@ -160,7 +173,7 @@ i4s_status i4s_pack(const uint16_t *w_fp16, int32_t rows, int32_t cols, int32_t 
   out.group_size = g;
   out.nnz = (int64_t)rows * cols / 4 * n_keep;
   if (n_keep == 4) out.codes = nullptr;
-  e = i4s::launch_pack_emit(w_fp16, rows, cols, n_keep, g, out, s);
+  e = i4s::launch_pack_emit(w_fp16, col_norm, grad_fp16, rows, cols, n_keep, g, out, s);
   if (e != hipSuccess) return device_error(e, "pack emit launch");
   *inout = out;
   if (report) {

@@ -15,7 +15,8 @@ namespace i4s {
 constexpr int kSegCols = 64;
 
 // Pack workspace layout (bytes from the workspace base):
-//   [0, 4)     uint32 non-finite flag
+//   [0, 4)     uint32 flag bits: 1 non-finite weight, 2 negative or
+//              non-finite column norm, 4 non-finite gradient
 //   [16, 64)   three 128-bit SSE totals (lo, hi) for G = 64, 128, 256
 //   [64, ...)  per-block 128-bit partials, 3 per analyze block
 constexpr size_t kWsFlagOffset = 0;
@@ -33,14 +34,17 @@ inline size_t pack_workspace_bytes(int32_t rows, int32_t cols) {
   return kWsPartialsOffset + (size_t)pack_blocks(rows, cols) * 3 * 16;
 }
 
+constexpr uint32_t kPackFlagNonfiniteWeight = 1u, kPackFlagBadNorm = 2u, kPackFlagBadGrad = 4u;
+
 // Pack kernels (i4s_pack.hip).  `adaptive` selects whether the analyze pass
 // also accumulates the exact SSE of every candidate group size; it always
-// raises the non-finite flag.
-hipError_t launch_pack_analyze(const uint16_t *w, int32_t rows, int32_t cols,
-                               int32_t n_keep, bool adaptive, void *ws,
+// raises the flag bits.  col_norm ([cols] fp32) and grad ([rows][cols] fp16)
+// are the optional importance inputs (null when absent).
+hipError_t launch_pack_analyze(const uint16_t *w, const float *col_norm, const uint16_t *grad,
+                               int32_t rows, int32_t cols, int32_t n_keep, bool adaptive, void *ws,
                                hipStream_t stream);
-hipError_t launch_pack_emit(const uint16_t *w, int32_t rows, int32_t cols,
-                            int32_t n_keep, int32_t group_size,
+hipError_t launch_pack_emit(const uint16_t *w, const float *col_norm, const uint16_t *grad,
+                            int32_t rows, int32_t cols, int32_t n_keep, int32_t group_size,
                             const i4s_packed &out, hipStream_t stream);
 
 // GEMV kernels.  launch_gemv (i4s_gemv_batch.hip) dispatches every call;

@@ -1,11 +1,13 @@
-// Packer kernels for gfx950: N:4 magnitude pruning, symmetric INT4 group
-// quantization with fp16 scales, the exact-SSE choice of the group size, and
-// the encoding of the 2-bit CSR buffers.
+// Packer kernels for gfx950: N:4 pruning by magnitude or by the full
+// importance score, symmetric INT4 group quantization with fp16 scales, the
+// exact-SSE choice of the group size, and the encoding of the 2-bit CSR
+// buffers.
 //
 // Method: "Efficient LLM-based Advertising via Model Compression and Parallel
-// Verification", section 3.2 (N:M pruning ordered by the Eq. (3) importance,
-// which is |w| when the activation norm is constant and the gradient term is
-// absent; layer-adaptive group-wise INT4 quantization) and section 3.3
+// Verification", section 3.2 (N:M pruning ordered by the Eq. (3) importance
+// |W_ij| * ||X_j||_2 + |W_ij| * |dE/dW_ij|, which orders by |w| when the
+// activation norm is constant and the gradient term is absent; layer-adaptive
+// group-wise INT4 quantization) and section 3.3
 // ("Sparse Index Structure": CSR with 2-bit in-group column indices packed
 // into uint16 words from the least significant bits).
 //
@@ -14,6 +16,12 @@
 // the amax of a group of G columns is the max over G/64 neighbouring
 // segments; those sit in neighbouring lanes of one wave (K is a multiple of
 // G), and a lane shuffle combines them.
+//
+// Importance: with caller-supplied column norms n_j (fp32) and/or gradients
+// g_ij (fp16) the score is |w| * (n_j + |g_ij|) in fp32, the sum and the
+// product each rounded to nearest even (n_j = 1 and g_ij = 0 when absent).
+// The scores are non-negative (or -0 / +inf), so their bit patterns with the
+// sign cleared order like their values.
 //
 // Exactness: every fp16 value is an integer multiple of 2^-24, and so is an
 // fp16 scale times a small integer; the squared errors are therefore summed
@@ -84,12 +92,10 @@ __device__ inline int quantize(uint32_t w_bits, uint32_t s_bits) {
 }
 
 // In-group columns kept for one group of 4, ascending.  The kept set is the
-// NK largest magnitudes; among equal magnitudes the lower column wins.
-// (Magnitudes of finite fp16 values order like their low 15 bits.)
+// NK largest keys; among equal keys the lower column wins.
 template <int NK>
-__device__ inline void select_group(const uint32_t h[4], int code[NK]) {
-  const uint32_t m0 = h[0] & 0x7FFFu, m1 = h[1] & 0x7FFFu;
-  const uint32_t m2 = h[2] & 0x7FFFu, m3 = h[3] & 0x7FFFu;
+__device__ inline void select_group(const uint32_t key[4], int code[NK]) {
+  const uint32_t m0 = key[0], m1 = key[1], m2 = key[2], m3 = key[3];
   if constexpr (NK == 4) {
     code[0] = 0; code[1] = 1; code[2] = 2; code[3] = 3;
   } else {
@@ -113,26 +119,64 @@ __device__ inline uint32_t pick4(const uint32_t h[4], int c) {
   return c == 0 ? h[0] : (c == 1 ? h[1] : (c == 2 ? h[2] : h[3]));
 }
 
+// Optional inputs of the importance score (device pointers, may be null).
+struct ImportanceIn {
+  const float *norm;     // [cols] fp32 column norms
+  const uint16_t *grad;  // [rows][cols] fp16 gradient bits
+};
+
+constexpr uint32_t kFlagNonfiniteWeight = kPackFlagNonfiniteWeight;
+constexpr uint32_t kFlagBadNorm = kPackFlagBadNorm, kFlagBadGrad = kPackFlagBadGrad;
+
 // Load the 64 fp16 values of a segment as 64 bit patterns (zero if !valid)
-// and compute the kept elements (bits) and codes.
-template <int NK>
-__device__ inline bool load_and_select(const uint16_t *__restrict__ w, int64_t row,
-                                       int seg, int cols, bool valid,
-                                       uint32_t kv[16 * NK], int kc[16 * NK]) {
-  uint32_t words[32];
+// and compute the kept elements (bits) and codes.  HN / HG: column norms /
+// gradients are given.  Returns the flag bits this segment raises.
+template <int NK, bool HN, bool HG>
+__device__ inline uint32_t load_and_select(const uint16_t *__restrict__ w, ImportanceIn imp,
+                                           int64_t row, int seg, int cols, bool valid,
+                                           uint32_t kv[16 * NK], int kc[16 * NK]) {
+  uint32_t words[32], gwords[HG ? 32 : 1];
+  float nv[HN ? 64 : 1];
+  const int64_t off = row * (int64_t)cols + (int64_t)seg * kSegCols;
   if (valid) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(w + row * (int64_t)cols + (int64_t)seg * kSegCols);
+    const uint4 *src = reinterpret_cast<const uint4 *>(w + off);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint4 v = src[i];
       words[4 * i + 0] = v.x; words[4 * i + 1] = v.y;
       words[4 * i + 2] = v.z; words[4 * i + 3] = v.w;
     }
+    if constexpr (HG) {
+      const uint4 *gsrc = reinterpret_cast<const uint4 *>(imp.grad + off);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 v = gsrc[i];
+        gwords[4 * i + 0] = v.x; gwords[4 * i + 1] = v.y;
+        gwords[4 * i + 2] = v.z; gwords[4 * i + 3] = v.w;
+      }
+    }
+    if constexpr (HN) {
+      const float4 *nsrc = reinterpret_cast<const float4 *>(imp.norm + (int64_t)seg * kSegCols);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 v = nsrc[i];
+        nv[4 * i + 0] = v.x; nv[4 * i + 1] = v.y;
+        nv[4 * i + 2] = v.z; nv[4 * i + 3] = v.w;
+      }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 32; ++i) words[i] = 0u;
+    if constexpr (HG) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) gwords[i] = 0u;
+    }
+    if constexpr (HN) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) nv[i] = 0.0f;
+    }
   }
-  bool nonfinite = false;
+  uint32_t flags = 0;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     uint32_t h[4];
@@ -140,17 +184,39 @@ __device__ inline bool load_and_select(const uint16_t *__restrict__ w, int64_t r
     h[1] = words[2 * t] >> 16;
     h[2] = words[2 * t + 1] & 0xFFFFu;
     h[3] = words[2 * t + 1] >> 16;
+    uint32_t key[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) nonfinite |= (h[c] & 0x7C00u) == 0x7C00u;
+    for (int c = 0; c < 4; ++c) {
+      if ((h[c] & 0x7C00u) == 0x7C00u) flags |= kFlagNonfiniteWeight;
+      if constexpr (!HN && !HG) {
+        key[c] = h[c] & 0x7FFFu;  // finite fp16 magnitudes order like their low 15 bits
+      } else {
+        float n = 1.0f, g = 0.0f;
+        if constexpr (HN) {
+          n = nv[4 * t + c];
+          const uint32_t nb = __builtin_bit_cast(uint32_t, n);
+          // finite and not below zero (-0 is allowed)
+          if ((nb & 0x7F800000u) == 0x7F800000u || (nb > 0x80000000u)) flags |= kFlagBadNorm;
+        }
+        if constexpr (HG) {
+          const uint32_t gb = (gwords[2 * t + (c >> 1)] >> (16 * (c & 1))) & 0xFFFFu;
+          if ((gb & 0x7C00u) == 0x7C00u) flags |= kFlagBadGrad;
+          g = fp16_bits_to_float(gb & 0x7FFFu);
+        }
+        const float a = n + g;  // one rounding; -0 + +0 = +0
+        const float sc = fp16_bits_to_float(h[c] & 0x7FFFu) * a;
+        key[c] = __builtin_bit_cast(uint32_t, sc) & 0x7FFFFFFFu;
+      }
+    }
     int code[NK];
-    select_group<NK>(h, code);
+    select_group<NK>(key, code);
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
       kc[NK * t + k] = code[k];
       kv[NK * t + k] = pick4(h, code[k]);
     }
   }
-  return nonfinite;
+  return flags;
 }
 
 template <int NK>
@@ -168,9 +234,9 @@ __device__ inline uint32_t group_amax(uint32_t a, int group_size) {
   return a;
 }
 
-template <int NK>
+template <int NK, bool HN, bool HG>
 __global__ __launch_bounds__(kPackThreads) void pack_analyze_kernel(
-    const uint16_t *__restrict__ w, int rows, int cols, int adaptive,
+    const uint16_t *__restrict__ w, ImportanceIn imp, int rows, int cols, int adaptive,
     uint8_t *__restrict__ ws) {
   const int S = cols / kSegCols;
   const int64_t total = (int64_t)rows * S;
@@ -181,8 +247,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_analyze_kernel(
 
   uint32_t kv[16 * NK];
   int kc[16 * NK];
-  const bool nonfinite = load_and_select<NK>(w, row, seg, cols, valid, kv, kc);
-  if (nonfinite) atomicOr(reinterpret_cast<unsigned int *>(ws + kWsFlagOffset), 1u);
+  const uint32_t flags = load_and_select<NK, HN, HG>(w, imp, row, seg, cols, valid, kv, kc);
+  if (flags) atomicOr(reinterpret_cast<unsigned int *>(ws + kWsFlagOffset), flags);
   if (!adaptive) return;  // uniform across the grid
 
   const uint32_t a64 = segment_amax<NK>(kv);
@@ -253,9 +319,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_reduce_kernel(uint8_t *__re
 // mask of 0x000F000F (after a shift by 4p) yields elements (2p, 2p+1).
 __host__ __device__ constexpr int nibble_slot(int k) { return (k & 1) ? 4 + (k >> 1) : (k >> 1); }
 
-template <int NK>
+template <int NK, bool HN, bool HG>
 __global__ __launch_bounds__(kPackThreads) void pack_emit_kernel(
-    const uint16_t *__restrict__ w, int rows, int cols, int group_size,
+    const uint16_t *__restrict__ w, ImportanceIn imp, int rows, int cols, int group_size,
     int32_t *__restrict__ row_ptr, uint8_t *__restrict__ vals,
     uint16_t *__restrict__ codes, uint16_t *__restrict__ scales) {
   const int S = cols / kSegCols;
@@ -267,7 +333,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_emit_kernel(
 
   uint32_t kv[16 * NK];
   int kc[16 * NK];
-  load_and_select<NK>(w, row, seg, cols, valid, kv, kc);
+  load_and_select<NK, HN, HG>(w, imp, row, seg, cols, valid, kv, kc);
   // every lane (valid or not) takes part in the shuffles
   const uint32_t s = scale_bits(group_amax(segment_amax<NK>(kv), group_size));
   if (!valid) return;
@@ -325,48 +391,80 @@ __global__ __launch_bounds__(kPackThreads) void pack_emit_kernel(
   }
 }
 
+template <int NK, bool HN, bool HG>
+hipError_t analyze_t(const uint16_t *w, ImportanceIn imp, int32_t rows, int32_t cols, bool adaptive,
+                     uint8_t *wsb, hipStream_t stream) {
+  hipLaunchKernelGGL((pack_analyze_kernel<NK, HN, HG>), dim3((unsigned)pack_blocks(rows, cols)),
+                     dim3(kPackThreads), 0, stream, w, imp, rows, cols, (int)adaptive, wsb);
+  return hipGetLastError();
+}
+
+template <int NK, bool HN, bool HG>
+hipError_t emit_t(const uint16_t *w, ImportanceIn imp, int32_t rows, int32_t cols, int32_t group_size,
+                  const i4s_packed &out, hipStream_t stream) {
+  hipLaunchKernelGGL((pack_emit_kernel<NK, HN, HG>), dim3((unsigned)pack_blocks(rows, cols)),
+                     dim3(kPackThreads), 0, stream, w, imp, rows, cols, group_size, out.row_ptr,
+                     out.vals, out.codes, out.scales);
+  return hipGetLastError();
+}
+
+// Instantiate a launcher for the runtime (n_keep, norms?, gradients?) triple.
+template <template <int, bool, bool> class F, typename... A>
+hipError_t dispatch_pack(int32_t n_keep, bool hn, bool hg, A... args) {
+#define I4S_PACK_NK(NK)                                  \
+  if (hn && hg) return F<NK, true, true>::go(args...);   \
+  if (hn) return F<NK, true, false>::go(args...);        \
+  if (hg) return F<NK, false, true>::go(args...);        \
+  return F<NK, false, false>::go(args...);
+  switch (n_keep) {
+    case 1: { I4S_PACK_NK(1) }
+    case 2: { I4S_PACK_NK(2) }
+    default: { I4S_PACK_NK(4) }
+  }
+#undef I4S_PACK_NK
+}
+
+template <int NK, bool HN, bool HG>
+struct AnalyzeF {
+  static hipError_t go(const uint16_t *w, ImportanceIn imp, int32_t rows, int32_t cols, bool adaptive,
+                       uint8_t *wsb, hipStream_t stream) {
+    return analyze_t<NK, HN, HG>(w, imp, rows, cols, adaptive, wsb, stream);
+  }
+};
+
+template <int NK, bool HN, bool HG>
+struct EmitF {
+  static hipError_t go(const uint16_t *w, ImportanceIn imp, int32_t rows, int32_t cols, int32_t group_size,
+                       const i4s_packed *out, hipStream_t stream) {
+    return emit_t<NK, HN, HG>(w, imp, rows, cols, group_size, *out, stream);
+  }
+};
+
 }  // namespace
 
-hipError_t launch_pack_analyze(const uint16_t *w, int32_t rows, int32_t cols,
-                               int32_t n_keep, bool adaptive, void *ws,
+hipError_t launch_pack_analyze(const uint16_t *w, const float *col_norm, const uint16_t *grad,
+                               int32_t rows, int32_t cols, int32_t n_keep, bool adaptive, void *ws,
                                hipStream_t stream) {
   uint8_t *wsb = static_cast<uint8_t *>(ws);
   // the flag and the totals start at zero (a fill kernel, not a memset node)
   hipLaunchKernelGGL(pack_clear_kernel, dim3(1), dim3(64), 0, stream, wsb);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t nblocks = pack_blocks(rows, cols);
-  const dim3 grid((unsigned)nblocks), block(kPackThreads);
-  switch (n_keep) {
-    case 1: hipLaunchKernelGGL(pack_analyze_kernel<1>, grid, block, 0, stream, w, rows, cols, (int)adaptive, wsb); break;
-    case 2: hipLaunchKernelGGL(pack_analyze_kernel<2>, grid, block, 0, stream, w, rows, cols, (int)adaptive, wsb); break;
-    default: hipLaunchKernelGGL(pack_analyze_kernel<4>, grid, block, 0, stream, w, rows, cols, (int)adaptive, wsb); break;
-  }
-  err = hipGetLastError();
+  const ImportanceIn imp = {col_norm, grad};
+  err = dispatch_pack<AnalyzeF>(n_keep, col_norm != nullptr, grad != nullptr, w, imp, rows, cols,
+                                adaptive, wsb, stream);
   if (err != hipSuccess || !adaptive) return err;
-  hipLaunchKernelGGL(pack_reduce_kernel, dim3(1), block, 0, stream, wsb, nblocks);
+  hipLaunchKernelGGL(pack_reduce_kernel, dim3(1), dim3(kPackThreads), 0, stream, wsb,
+                     pack_blocks(rows, cols));
   return hipGetLastError();
 }
 
-hipError_t launch_pack_emit(const uint16_t *w, int32_t rows, int32_t cols,
-                            int32_t n_keep, int32_t group_size,
+hipError_t launch_pack_emit(const uint16_t *w, const float *col_norm, const uint16_t *grad,
+                            int32_t rows, int32_t cols, int32_t n_keep, int32_t group_size,
                             const i4s_packed &out, hipStream_t stream) {
-  const dim3 grid((unsigned)pack_blocks(rows, cols)), block(kPackThreads);
-  switch (n_keep) {
-    case 1:
-      hipLaunchKernelGGL(pack_emit_kernel<1>, grid, block, 0, stream, w, rows, cols, group_size,
-                         out.row_ptr, out.vals, out.codes, out.scales);
-      break;
-    case 2:
-      hipLaunchKernelGGL(pack_emit_kernel<2>, grid, block, 0, stream, w, rows, cols, group_size,
-                         out.row_ptr, out.vals, out.codes, out.scales);
-      break;
-    default:
-      hipLaunchKernelGGL(pack_emit_kernel<4>, grid, block, 0, stream, w, rows, cols, group_size,
-                         out.row_ptr, out.vals, out.codes, out.scales);
-      break;
-  }
-  return hipGetLastError();
+  const ImportanceIn imp = {col_norm, grad};
+  return dispatch_pack<EmitF>(n_keep, col_norm != nullptr, grad != nullptr, w, imp, rows, cols,
+                              group_size, &out, stream);
 }
 
 }  // namespace i4s

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["i4s_pack_sizes", "i4s_pack", "i4s_run", "i4s_run_workspace_size", "i4s_run_ws",
+        ["i4s_pack_sizes", "i4s_pack", "i4s_pack_ex", "i4s_run", "i4s_run_workspace_size", "i4s_run_ws",
          "i4s_status_string", "i4s_last_error", "i4s_version", "i4s_format_version"])
 
 
@@ -152,6 +152,13 @@ def test_pack_validation_fails_before_any_device_call(lib):
     assert B.i4s_pack(w, 64, 250, 2, 0, ws, sz.workspace, d, rep, None) == B.I4S_ERR_INVALID_ARGUMENT
     d.codes = None
     assert B.i4s_pack(w, 64, 256, 2, 0, ws, sz.workspace, d, rep, None) == B.I4S_ERR_INVALID_ARGUMENT
+    # i4s_pack_ex: misaligned importance inputs are rejected on the host
+    d = _desc()
+    n, g = 1 << 32, 1 << 33
+    assert B.i4s_pack_ex(w, 64, 256, 2, 0, n + 4, None, ws, sz.workspace, d, rep, None) == B.I4S_ERR_INVALID_ARGUMENT
+    assert B.i4s_pack_ex(w, 64, 256, 2, 0, None, g + 2, ws, sz.workspace, d, rep, None) == B.I4S_ERR_INVALID_ARGUMENT
+    assert B.i4s_pack_ex(w, 64, 256, 2, 0, n, g, ws, sz.workspace - 1, d, rep, None) == B.I4S_ERR_WORKSPACE_TOO_SMALL
+    assert B.i4s_pack_ex(w, 64, 250, 2, 0, n, g, ws, sz.workspace, d, rep, None) == B.I4S_ERR_INVALID_ARGUMENT
 
 
 def test_binding_without_library_fails_loudly(tmp_path):

@@ -137,6 +137,114 @@ def test_pack_rejects_nonfinite():
         gpu_pack(w, 4, 64)
 
 
+def gpu_pack_ex(w16, n_keep, g, norm, grad):
+    import int4_sparse_gemv_amd as I
+    w = torch.from_numpy(w16.view(np.int16)).cuda().view(torch.float16)
+    n = torch.from_numpy(norm).cuda() if norm is not None else None
+    gr = torch.from_numpy(grad.view(np.int16)).cuda().view(torch.float16) if grad is not None else None
+    p = I.pack(w, n_keep, g, col_norm=n, grad=gr)
+    torch.cuda.synchronize()
+    return p
+
+
+# rows, cols, n_keep, G, which importance inputs, tie-heavy inputs
+IMPORTANCE_CASES = [
+    (5, 256, 2, 64, "both", False), (33, 512, 2, 0, "both", False), (17, 384, 1, 128, "norm", False),
+    (9, 256, 4, 0, "both", False), (40, 1024, 2, 128, "grad", False), (300, 640, 2, 64, "both", True),
+    (64, 4160, 1, 64, "both", True), (7, 768, 2, 256, "norm", True), (130, 512, 1, 0, "grad", True),
+]
+
+
+@pytest.mark.parametrize("rows,cols,n_keep,g,which,ties", IMPORTANCE_CASES)
+def test_pack_importance_matches_oracle(rows, cols, n_keep, g, which, ties):
+    seed = rows * 7919 + cols + n_keep
+    if ties:
+        rng = np.random.default_rng(seed)
+        w = rng.integers(-3, 4, size=(rows, cols)).astype(np.float16)
+    else:
+        w = WL.make_weight(rows, cols, seed, outliers=True)
+    norm, grad = WL.make_importance_inputs(rows, cols, seed + 1, tie_heavy=ties)
+    if which == "norm":
+        grad = None
+    elif which == "grad":
+        norm = None
+    say(f"case pack-importance {rows}x{cols} n={n_keep} g={g} {which} ties={ties}")
+    ref = O.pack(w, n_keep, g, norm, grad)
+    p = gpu_pack_ex(w, n_keep, g, norm, grad)
+    assert_pack_equal(p, ref, f"importance {rows}x{cols} n{n_keep} g{g} {which}")
+    if rows == 40:
+        x = WL.make_x(np.random.default_rng(seed + 2), 3, cols)
+        y_ref, a_ref = O.gemv(O.reconstruct(ref), x)
+        assert_gemv_close(gpu_run(p, x), y_ref, a_ref, "importance-packed gemv")
+
+
+def test_pack_importance_special_values():
+    rng = np.random.default_rng(77)
+    rows, cols = 6, 256
+    w = rand16(rng, (rows, cols), 1.0)
+    w[0, :4] = np.float16([65504, -65504, 1, 0.5])
+    w[1, :8] = np.float16([6e-8, -6e-8, 1e-7, 0, -0.0, 2, 3, 1])
+    norm = np.exp2(rng.uniform(-20, 20, cols)).astype(np.float32)
+    norm[:4] = np.float32([3.0e38, 3.0e38, 3.0e38, 1.0])      # products past fp32's range -> +inf ties
+    norm[4:8] = np.float32([1e-40, 2e-40, -0.0, 1e-45])       # fp32 subnormals and -0
+    norm[8:12] = 0.0
+    grad = rand16(rng, (rows, cols), 1.0)
+    grad[1, :8] = np.float16([6e-8, -6e-8, 0, -0.0, 65504, -65504, 1e-5, 0])
+    grad[:, 4:8] = 0                                            # keep the subnormal norms visible
+    for n_keep in (1, 2):
+        for which in ("norm", "both"):
+            gr = grad if which == "both" else None
+            say(f"case pack-importance-special n={n_keep} {which}")
+            ref = O.pack(w, n_keep, 64, norm, gr)
+            assert_pack_equal(gpu_pack_ex(w, n_keep, 64, norm, gr), ref, f"special n{n_keep} {which}")
+
+
+def test_pack_importance_unit_norms_equal_magnitude_pack():
+    rng = np.random.default_rng(78)
+    w = rand16(rng, (48, 512))
+    w[:, ::5] = np.float16(rng.integers(-2, 3, (48, 103)))     # exact magnitude ties
+    say("case pack-importance-unit-norms")
+    for n_keep, g in ((1, 64), (2, 0), (2, 256)):
+        a = host_bytes(gpu_pack(w, n_keep, g))
+        b = host_bytes(gpu_pack_ex(w, n_keep, g, np.ones(512, np.float32), None))
+        c = host_bytes(gpu_pack_ex(w, n_keep, g, np.ones(512, np.float32), np.zeros(w.shape, np.float16)))
+        for k in a:
+            assert np.array_equal(a[k], b[k]) and np.array_equal(a[k], c[k]), k
+
+
+def test_pack_importance_rejects_bad_inputs():
+    import int4_sparse_gemv_amd as I
+    rows, cols = 4, 256
+    w = np.zeros((rows, cols), np.float16)
+    ok_n = np.ones(cols, np.float32)
+    ok_g = np.zeros((rows, cols), np.float16)
+    say("case pack-importance-bad-inputs")
+    for v in (-1.0, -1e-45, np.inf, np.nan):
+        n = ok_n.copy()
+        n[100] = v
+        with pytest.raises(I.I4SError) as e:
+            gpu_pack_ex(w, 2, 64, n, None)
+        assert e.value.status == I._binding.I4S_ERR_INVALID_ARGUMENT, v
+    for v in (np.inf, -np.inf, np.nan):
+        g = ok_g.copy()
+        g[3, 255] = v
+        with pytest.raises(I.I4SError) as e:
+            gpu_pack_ex(w, 1, 0, ok_n, g)
+        assert e.value.status == I._binding.I4S_ERR_INVALID_ARGUMENT, v
+    # a non-finite weight is reported first
+    w[1, 7] = np.inf
+    n = ok_n.copy()
+    n[0] = np.nan
+    with pytest.raises(I.I4SError) as e:
+        gpu_pack_ex(w, 2, 64, n, None)
+    assert e.value.status == I._binding.I4S_ERR_NONFINITE_WEIGHT
+    # -0 is an allowed norm
+    w[1, 7] = 0
+    n = ok_n.copy()
+    n[5] = -0.0
+    gpu_pack_ex(w, 2, 64, n, ok_g)
+
+
 def config_matrices():
     out = []
     for name in ("c1_512", "c2_4096", "c3_mlp7b", "c5_verify13b"):

@@ -13,6 +13,13 @@ Recipe (one numpy ``default_rng(seed)`` stream per matrix):
   rounded once to fp16 (round-to-nearest-even).
 * x: drawn from the same stream after W, ``standard_normal((B, K))`` rounded to
   fp16.  W is therefore identical for every batch size B of a given seed.
+* Importance inputs (``make_importance_inputs``, a stream of their own):
+  column norms ``16 * exp(0.5 * standard_normal(K))`` in float32, with 1 % of
+  the columns (at least one) set to 0 (dead channels) and 1 % (at least one)
+  multiplied by 20 (outlier channels); gradients ``1e-3 *
+  standard_normal((R, K))`` rounded to fp16.  The tie-heavy variant draws
+  norms from {0, 0.5, 1, 2} and gradients from {0, +-0.25, +-1} so that many
+  scores coincide exactly.
 
 The shapes stand in for the decoder layers of a 7B-class and a 13B-class
 model; the page this work follows measures a 1.5B model on proprietary and
@@ -27,7 +34,7 @@ from typing import List, Optional, Tuple
 import numpy as np
 
 __all__ = ["Matrix", "Workload", "WORKLOADS", "make_weight", "make_x",
-           "make_weight_and_x", "stack_7b_matrices"]
+           "make_weight_and_x", "make_importance_inputs", "stack_7b_matrices"]
 
 
 @dataclass(frozen=True)
@@ -74,6 +81,23 @@ def make_weight_and_x(m: Matrix, batch: int) -> Tuple[np.ndarray, np.ndarray]:
     w = make_weight(m.rows, m.cols, m.seed, m.outliers, rng=rng)
     x = make_x(rng, batch, m.cols)
     return w, x
+
+
+def make_importance_inputs(rows: int, cols: int, seed: int,
+                           tie_heavy: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """(column norms float32 [cols], gradients fp16 [rows][cols])."""
+    rng = np.random.default_rng(seed)
+    if tie_heavy:
+        norm = rng.choice(np.float32([0.0, 0.5, 1.0, 2.0]), cols)
+        grad = rng.choice(np.float16([0.0, 0.25, -0.25, 1.0, -1.0]), (rows, cols))
+        return norm.astype(np.float32), grad.astype(np.float16)
+    norm = 16.0 * np.exp(0.5 * rng.standard_normal(cols))
+    n = max(1, int(round(0.01 * cols)))
+    idx = rng.choice(cols, 2 * n, replace=False)
+    norm[idx[:n]] = 0.0
+    norm[idx[n:]] *= 20.0
+    grad = 1e-3 * rng.standard_normal((rows, cols))
+    return norm.astype(np.float32), grad.astype(np.float16)
 
 
 _PROJ = ("q", "k", "v", "o", "gate", "up", "down")
