@@ -293,11 +293,11 @@ class Runner:
                 "cold_gbs": nbytes / (cold_ev * 1e-3) / 1e9, "hot_gbs": nbytes / (hot_ev * 1e-3) / 1e9,
                 "cold_tflops": flops / (cold_ev * 1e-3) / 1e12}
 
-    def measure_stack(self, trials):
-        """The 224 projections of the 32-layer 7B stack, one call each, in layer order."""
+    def measure_stack(self, trials, name="c4_stack7b"):
+        """The 224 projections of a 32-layer 7B stack, one call each, in layer order."""
         import workloads as WL
         torch = self.torch
-        mats = WL.WORKLOADS["c4_stack7b"].matrices
+        mats = WL.WORKLOADS[name].matrices
         items, total, groups = [], 0, {}
         xs = {}
         for m in mats:
@@ -413,27 +413,28 @@ def main():
 def kernel_label(m, batch):
     """Name of the kernel the library dispatches for this call (labels only)."""
     units = m.cols // 64
-    if batch == 1 and m.n_keep in (2, 4):
+    if batch == 1:
         rpw = 2 if m.rows > 8192 else 1
         if units <= 256:
             return f"gemv_b1_direct_kernel<{m.n_keep},{rpw},{(units + 63) // 64},8>"
         return f"gemv_b1_kernel<{m.n_keep},{rpw},8>"
     if m.n_keep == 2 and batch >= 2:
-        return "gemv_smfmac_kernel / gemv_smfmac_split_kernel"
+        return "gemv_smfmac_rows_kernel / gemv_smfmac_split_kernel"
     return f"gemv_kernel<{m.n_keep},BT>=" + str(batch)
 
 
 def run_suite(R, args):
     import workloads as WL
     out = []
-    names = ("c1_512", "c2_4096", "c3_mlp7b", "c5_verify13b", "c4_stack7b")
+    names = ("c1_512", "c2_4096", "c3_mlp7b", "c5_verify13b", "c4_stack7b", "x1_4096_1to4", "x2_mix_stack7b")
+    stacks = ("c4_stack7b", "x2_mix_stack7b")
     if args.only:
         names = tuple(n for n in names if n in args.only.split(","))
     for name in names:
         wl = WL.WORKLOADS[name]
         mats = wl.matrices
-        if name == "c4_stack7b":
-            # one dense and one 2:4 layer individually; the whole stack below
+        if name in stacks:
+            # one outer and one inner layer individually; the whole stack below
             mats = [m for m in mats if m.name.startswith(("L0.", "L4."))]
         for m in mats:
             for b in wl.batches:
@@ -442,10 +443,12 @@ def run_suite(R, args):
                 print(f"suite {name}/{m.name} b{b}: cold {r['cold_us']:.2f} us ({r['cold_gbs']:.0f} GB/s), "
                       f"hot {r['hot_us']:.2f} us", file=sys.stderr, flush=True)
                 out.append(r)
-    if not args.no_stack and "c4_stack7b" in names:
-        s = R.measure_stack(3)
-        s["workload"] = "c4_stack7b/all"
-        print(f"suite stack: {s['us_per_pass']:.1f} us per 224-call pass ({s['gbs']:.0f} GB/s)",
+    for name in stacks:
+        if args.no_stack or name not in names:
+            continue
+        s = R.measure_stack(3, name)
+        s["workload"] = name + "/all"
+        print(f"suite {name}: {s['us_per_pass']:.1f} us per 224-call pass ({s['gbs']:.0f} GB/s)",
               file=sys.stderr, flush=True)
         out.append(s)
     return out

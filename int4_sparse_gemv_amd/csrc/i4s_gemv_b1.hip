@@ -15,9 +15,9 @@
 // lanes therefore read adjacent 16-byte pieces of a row (dwordx4 for 2:4),
 // and one unit never straddles a quantization group.  The RPW rows of a wave
 // share the same columns, so each activation fetch from LDS feeds RPW rows.
-// For 2:4 the v_perm_b32 selectors come from a 16-entry table in LDS and
-// v_dot2_f32_f16 multiplies and accumulates in fp32; the group scale is
-// applied once per unit.
+// For 2:4 and 1:4 the v_perm_b32 selectors come from a 16-entry table in
+// LDS and v_dot2_f32_f16 multiplies and accumulates in fp32; the group scale
+// is applied once per unit.
 //
 // Row starts: the kernels read row_ptr, but issue the weight loads of a row
 // at the offset the format prescribes (row * K * N / 4) without waiting for
@@ -33,7 +33,7 @@ namespace i4s {
 namespace {
 
 // ---------------------------------------------------------------------------
-// batch-1 kernel (2:4 and dense): the lane's 64 activations live in registers
+// batch-1 kernel (any N): the lane's 64 activations live in registers
 
 template <int NK>
 __device__ inline float unit_dot_b1(const UnitRegs<NK> &u, const uint32_t (&xr)[32], const uint32_t *lut) {
@@ -58,6 +58,24 @@ __device__ inline float unit_dot_b1(const UnitRegs<NK> &u, const uint32_t (&xr)[
         }
       }
     }
+  } else if constexpr (NK == 1) {
+    // one code dword per unit: nibble k holds the codes of elements 2k, 2k+1
+    const uint32_t me = (u.c[0] << 3) & 0x78787878u;  // byte b: 8 * nibble 2b
+    const uint32_t mo = (u.c[0] >> 1) & 0x78787878u;  // byte b: 8 * nibble 2b+1
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // vals word j: elements (= groups) 8j..8j+7
+      h2_t q[4];
+      dequant_word(u.v[j], q);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int k = 4 * j + p;  // pair k: groups 2k, 2k+1
+        const uint32_t m = (k & 1) ? mo : me;
+        const u32x2_lut_t sel = lut_read2(lut, (m >> (8 * (k >> 1))) & 0xFFu);
+        const uint32_t xa = __builtin_amdgcn_perm(xr[4 * k + 1], xr[4 * k], sel.x);
+        const uint32_t xb = __builtin_amdgcn_perm(xr[4 * k + 3], xr[4 * k + 2], sel.y);
+        g = __builtin_amdgcn_fdot2(q[p], as_h2(xa | xb), g, false);
+      }
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {  // vals word j: columns 8j..8j+7
@@ -77,7 +95,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
     uint16_t *__restrict__ y, int kc_units) {
   extern __shared__ __align__(16) uint16_t xs[];  // [kc_units][kStrideB1]
-  __shared__ uint32_t lut[16];
+  __shared__ __align__(8) uint32_t lut[32];
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
   const int row0 = (blockIdx.x * WAVES + wave) * RPW;
@@ -127,7 +145,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
         *reinterpret_cast<uint4 *>(xs + un * kStrideB1 + 8 * part) =
             *reinterpret_cast<const uint4 *>(x + (int64_t)ub * kSegCols + 8 * i);
       }
-      if (NK == 2 && ub == 0 && threadIdx.x < 16) init_selector_table(lut);
+      if (ub == 0) init_tables<NK>(lut);
     }
     __syncthreads();
 
@@ -151,12 +169,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
       const int un = u + 64;
       const bool hn = un < ue;
       UnitRegs<NK> nxt[RPW];
-      if (hn) {  // prefetch the lane's next unit
+      // prefetch the lane's next unit; past the chunk's end the last unit is
+      // read again and dropped.  Unconditional loads and a single exit at
+      // the end keep the body one basic block, so the compiler cannot hoist
+      // one iteration's LDS reads into the previous one.
+      const int uc = hn ? un : ue - 1;
 #pragma unroll
-        for (int r = 0; r < RPW; ++r)
-          load_unit<NK>(nxt[r], vals, codes, scales, rstart[r] + (uint32_t)un * 16 * NK,
-                        srow[r] + ((uint32_t)un >> sg_shift));
-      }
+      for (int r = 0; r < RPW; ++r)
+        load_unit<NK>(nxt[r], vals, codes, scales, rstart[r] + (uint32_t)uc * 16 * NK,
+                      srow[r] + ((uint32_t)uc >> sg_shift));
       uint32_t xr[32];
       const uint4 *xv = reinterpret_cast<const uint4 *>(xs + (u - ub) * kStrideB1);
 #pragma unroll
@@ -169,10 +190,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
         const float gsum = unit_dot_b1<NK>(cur[r], xr, lut);
         acc[r] = fmaf(fp16_bits_to_float(cur[r].s), gsum, acc[r]);
       }
-      if (!hn) break;
 #pragma unroll
       for (int r = 0; r < RPW; ++r) cur[r] = nxt[r];
       u = un;
+      has = hn;
     }
   }
 
@@ -202,7 +223,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
     uint16_t *__restrict__ y) {
   extern __shared__ __align__(16) uint16_t xs[];  // [units][kStrideB1]
-  __shared__ uint32_t lut[16];
+  __shared__ __align__(8) uint32_t lut[32];
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
   const int row0 = (blockIdx.x * WAVES + wave) * RPW;
@@ -254,7 +275,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
 #pragma unroll
   for (int j = 0; j < UPL; ++j)
     *reinterpret_cast<uint4 *>(xs + (xi[j] >> 3) * kStrideB1 + 8 * (xi[j] & 7)) = xg[j];
-  if (NK == 2 && threadIdx.x < 16) init_selector_table(lut);
+  init_tables<NK>(lut);
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
@@ -375,6 +396,13 @@ int b1_rows_per_wave(int rows) {
 
 hipError_t launch_gemv_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
   const int rpw = b1_rows_per_wave(w.rows);
+  if (w.n_keep == 1) {
+    switch (rpw) {
+      case 2: return launch_b1<1, 2>(w, x, y, stream);
+      case 4: return launch_b1<1, 4>(w, x, y, stream);
+      default: return launch_b1<1, 1>(w, x, y, stream);
+    }
+  }
   if (w.n_keep == 2) {
     switch (rpw) {
       case 2: return launch_b1<2, 2>(w, x, y, stream);

@@ -1,5 +1,5 @@
-// Batch SparseGEMV kernels for gfx950 (1 <= batch <= 16, and batch 1 for
-// the 1:4 pattern) and the dispatch of every GEMV call.
+// Batch SparseGEMV kernels for gfx950 (2 <= batch <= 16) and the dispatch
+// of every GEMV call.
 //
 // Method: "Efficient LLM-based Advertising via Model Compression and Parallel
 // Verification", section 3.3, "Computational Acceleration" (activations
@@ -14,6 +14,8 @@
 // zero in LDS and never stored) are staged in LDS with 68 halfs per unit, so
 // the 8-byte reads of 64 lanes fall in distinct banks.  When the staged
 // activations exceed the LDS budget the K axis is processed in chunks.
+
+#include <type_traits>
 
 #include "i4s_gemv_common.h"
 
@@ -79,26 +81,31 @@ __device__ inline void compute_unit(const UnitRegs<NK> (&u)[RPW], const uint16_t
       }
     }
   } else {  // NK == 1: element e of the unit is group e, column 4e + code
+    // per row: the 8 element pairs' weights and selector pairs, then one
+    // batch vector at a time (its 64 activations, 32 registers)
+    h2_t q[RPW][8];
+    u32x2_lut_t sel[RPW][8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      h2_t q[RPW][4];
+    for (int r = 0; r < RPW; ++r) {
+      dequant_word(u[r].v[0], &q[r][0]);
+      dequant_word(u[r].v[1], &q[r][4]);
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) dequant_word(u[r].v[j], q[r]);
+      for (int k = 0; k < 8; ++k) sel[r][k] = lut_read2(lut, ((u[r].c[0] >> (4 * k)) & 0xFu) << 3);
+    }
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int e0 = 8 * j + 2 * p;  // elements e0 (group e0) and e0+1
+    for (int b = 0; b < BT; ++b) {
+      uint2 xv[16];  // groups 0..15 of vector b
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          const uint32_t c0 = (u[r].c[0] >> (2 * e0)) & 3u;
-          const uint32_t c1 = (u[r].c[0] >> (2 * e0 + 2)) & 3u;
+      for (int i = 0; i < 16; ++i) xv[i] = *reinterpret_cast<const uint2 *>(xs + b * xstride + 4 * i);
 #pragma unroll
-          for (int b = 0; b < BT; ++b) {
-            const uint32_t lo = xs[b * xstride + 4 * e0 + c0];
-            const uint32_t hi = xs[b * xstride + 4 * e0 + 4 + c1];
-            g[r][b] = __builtin_amdgcn_fdot2(q[r][p], as_h2(lo | (hi << 16)), g[r][b], false);
-          }
+      for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t lo = __builtin_amdgcn_perm(xv[2 * k].y, xv[2 * k].x, sel[r][k].x);
+          const uint32_t hi = __builtin_amdgcn_perm(xv[2 * k + 1].y, xv[2 * k + 1].x, sel[r][k].y);
+          g[r][b] = __builtin_amdgcn_fdot2(q[r][k], as_h2(lo | hi), g[r][b], false);
         }
-      }
+
     }
   }
 #pragma unroll
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
     uint16_t *__restrict__ y, int kc_units) {
   extern __shared__ __align__(16) uint16_t xs[];  // [BT][kc_units][kStrideBT]
-  __shared__ uint32_t lut[16];
+  __shared__ __align__(8) uint32_t lut[32];
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
   const int row0 = (blockIdx.x * kWaves + wave) * RPW;
@@ -177,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         reinterpret_cast<uint2 *>(dst)[0] = lo;
         reinterpret_cast<uint2 *>(dst)[1] = hi;
       }
-      if (NK == 2 && ub == 0 && threadIdx.x < 16) init_selector_table(lut);
+      if (ub == 0) init_tables<NK>(lut);
     }
     __syncthreads();
 
@@ -200,17 +207,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       const int un = u + 64;
       const bool hn = un < ue;
       UnitRegs<NK> nxt[RPW];
-      if (hn) {  // prefetch the lane's next unit
+      // prefetch the lane's next unit; past the chunk's end the last unit is
+      // read again and dropped.  Unconditional loads and a single exit at
+      // the end keep the body one basic block: with a branch in the middle
+      // the compiler hoisted every activation read of a unit ahead of its
+      // dot products and spilled.
+      const int uc = hn ? un : ue - 1;
 #pragma unroll
-        for (int r = 0; r < RPW; ++r)
-          load_unit<NK>(nxt[r], vals, codes, scales, rstart[r] + (uint32_t)un * 16 * NK,
-                        srow[r] + ((uint32_t)un >> sg_shift));
-      }
+      for (int r = 0; r < RPW; ++r)
+        load_unit<NK>(nxt[r], vals, codes, scales, rstart[r] + (uint32_t)uc * 16 * NK,
+                      srow[r] + ((uint32_t)uc >> sg_shift));
       compute_unit<NK, BT, RPW>(cur, xs + (u - ub) * kStrideBT, xstride, lut, acc);
-      if (!hn) break;
 #pragma unroll
       for (int r = 0; r < RPW; ++r) cur[r] = nxt[r];
       u = un;
+      has = hn;  // the only exit, at the end: the body stays one basic block
     }
   }
 
@@ -661,7 +672,7 @@ __global__ __launch_bounds__(256) void gemv_split_reduce_kernel(
 
 // ---------------------------------------------------------------------------
 // batch kernel on the sparse matrix cores, one 16-row tile per block over the
-// whole of K (2:4, 2 <= batch <= 16, K <= 16384; no workspace)
+// whole of K (2:4 and 1:4, 2 <= batch <= 16, K <= 16384; no workspace)
 //
 // How the weights of a tile are read decides the rate (measured on MI355X on
 // a 13824x5120 layer): loads of 16 rows x 64 bytes per instruction -- the
@@ -676,6 +687,15 @@ __global__ __launch_bounds__(256) void gemv_split_reduce_kernel(
 // itself touches its area, so no barrier is needed until the waves' partial
 // tiles are summed in LDS at the end.  B fragments come from L2, two 4-unit
 // blocks ahead of the matrix steps.
+//
+// 1:4 on the same matrix step: each group of 4 columns keeps one weight, so
+// it is handed to the matrix core as a 2:4 group whose second kept value is
+// zero -- positions (c & 2, (c & 2) + 1), the weight in slot c & 1 -- which
+// is a canonical 2:4 group (two distinct ascending positions).  A unit is
+// 8 bytes of vals and 4 bytes of codes; lane (row i, kq) reads its quarter
+// (one half vals word, one code byte) straight from the wave's LDS area, so
+// no transposes are needed.  The multiply count per unit is that of 2:4;
+// the bytes are half.
 
 constexpr int kRUnits = 16;                  // units per chunk
 constexpr int kRMaxWaves = 8;                // 8 x 7040 bytes of LDS; 2 waves per SIMD
@@ -684,10 +704,41 @@ constexpr int kRValsBytes = 16 * kRStride * 16;
 constexpr int kRCodesBytes = 16 * kRStride * 8;
 constexpr int kRWaveLds = kRValsBytes + kRCodesBytes + kRUnits * 16 * 2;  // 7040 bytes
 
-// CPW = 16-unit chunks per wave; waves per block = ceil(units / (16 * CPW)).
-// SG = units per quantization group (G / 64: 1, 2 or 4), so where a group
-// ends inside a block of 4 units is known at compile time.
-template <int CPW, int SG>
+// The matrix-step operands of one 1:4 unit for lane (row, kq): the unit's
+// vals word kq / 2 and code byte kq (groups 4kq..4kq+3).  `sh` is 8 * (kq & 1):
+// elements 4(kq & 1)..+3 of the word sit in nibble slots shifted by it.
+__device__ inline f4_t smfmac_step_14(uint32_t wd, uint32_t cb, uint32_t sh, const h16_t &bx, const f4_t &c) {
+  const uint32_t magic = 0x64006400u;
+  const uint32_t t = wd >> sh;
+  const h2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h2_t bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  // (q_g0, q_g1) and (q_g2, q_g3) of the four groups
+  const h2_t q01 = as_h2(and_or(t, 0x000F000Fu, magic)) + bias;
+  const h2_t q23 = __builtin_elementwise_fma(as_h2(and_or(t, 0x00F000F0u, magic)), sixteenth, bias16);
+  const uint32_t d01 = __builtin_bit_cast(uint32_t, q01), d23 = __builtin_bit_cast(uint32_t, q23);
+  // group g's pair: its weight in slot (c_g & 1), a zero (selector byte
+  // 0x0C) in the other; bit 2g of cb is c_g & 1
+  const uint32_t b0 = cb & 1u, b1 = (cb >> 2) & 1u, b2 = (cb >> 4) & 1u, b3 = (cb >> 6) & 1u;
+  u4_t qa;
+  qa.x = __builtin_amdgcn_perm(0u, d01, 0x0C0C0100u ^ (b0 * 0x0D0C0D0Cu));
+  qa.y = __builtin_amdgcn_perm(0u, d01, 0x0C0C0302u ^ (b1 * 0x0F0E0F0Eu));
+  qa.z = __builtin_amdgcn_perm(0u, d23, 0x0C0C0100u ^ (b2 * 0x0D0C0D0Cu));
+  qa.w = __builtin_amdgcn_perm(0u, d23, 0x0C0C0302u ^ (b3 * 0x0F0E0F0Eu));
+  // positions: nibble g = (c_g & 2) | ((c_g & 2) + 1) << 2
+  uint32_t y = cb;
+  y = (y | (y << 4)) & 0x0F0Fu;  // codes 0,1 in byte 0, codes 2,3 in byte 1
+  y = (y | (y << 2)) & 0x3333u;  // code g in bits 4g..4g+1
+  const uint32_t idx = (y & 0x2222u) * 5u + 0x4444u;
+  const h8_t a = __builtin_bit_cast(h8_t, qa);
+  return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, bx, c, (int)idx, 0, 0);
+}
+
+// NK = 2 (2:4) or 1 (1:4).  CPW = 16-unit chunks per wave; waves per block =
+// ceil(units / (16 * CPW)).  SG = units per quantization group (G / 64: 1, 2
+// or 4), so where a group ends inside a block of 4 units is known at compile
+// time.
+template <int NK, int CPW, int SG>
 __global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
     int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
@@ -697,11 +748,13 @@ __global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nwaves = blockDim.x / 64;
   const int li = lane % 16, lq = lane / 16;
   const int row0 = blockIdx.x * 16;
-  const uint32_t nnz_row = (uint32_t)units * 32;
+  const uint32_t nnz_row = (uint32_t)units * 16 * NK;
   const uint32_t ngroups = (uint32_t)units >> sg_shift;
+  typedef typename std::conditional<NK == 2, u32x4_t, u32x2_t>::type vals_t;    // a unit's vals
+  typedef typename std::conditional<NK == 2, u32x2_t, uint32_t>::type codes_t;  // a unit's codes
   uint8_t *wl = lds + wave * kRWaveLds;
-  u32x4_t *lv = reinterpret_cast<u32x4_t *>(wl);                                 // [16 rows][17] vals
-  u32x2_t *lc = reinterpret_cast<u32x2_t *>(wl + kRValsBytes);                   // [16 rows][17] codes
+  vals_t *lv = reinterpret_cast<vals_t *>(wl);                                   // [16 rows][17] vals
+  codes_t *lc = reinterpret_cast<codes_t *>(wl + kRValsBytes);                   // [16 rows][17] codes
   uint16_t *lsc = reinterpret_cast<uint16_t *>(wl + kRValsBytes + kRCodesBytes);  // [16 units][16 rows]
 
   // B fragments: lane (vector li, column quarter lq); vectors past `batch`
@@ -726,22 +779,22 @@ __global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
   u32x4_t bq[2][8];
   load_b(bq[0], 0);
   load_b(bq[1], 1);
-  u32x4_t wv[CPW][4];
-  u32x2_t wc[CPW][4];
+  vals_t wv[CPW][4];
+  codes_t wc[CPW][4];
   uint16_t wsc[CPW][4];
   auto load_w = [&](int c, const uint32_t (&base)[4], bool nt) {
     const int u = min((wave * CPW + c) * kRUnits + li, units - 1);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t e0 = base[k] + (uint32_t)u * 32;
+      const uint32_t e0 = base[k] + (uint32_t)u * 16 * NK;
       const uint32_t si = (uint32_t)wrow[k] * ngroups + ((uint32_t)u >> sg_shift);
       if (nt) {
-        wv[c][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vals + (e0 >> 1)));
-        wc[c][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(codes + (e0 >> 3)));
+        wv[c][k] = __builtin_nontemporal_load(reinterpret_cast<const vals_t *>(vals + (e0 >> 1)));
+        wc[c][k] = __builtin_nontemporal_load(reinterpret_cast<const codes_t *>(codes + (e0 >> 3)));
         wsc[c][k] = __builtin_nontemporal_load(scales + si);
       } else {
-        wv[c][k] = *reinterpret_cast<const u32x4_t *>(vals + (e0 >> 1));
-        wc[c][k] = *reinterpret_cast<const u32x2_t *>(codes + (e0 >> 3));
+        wv[c][k] = *reinterpret_cast<const vals_t *>(vals + (e0 >> 1));
+        wc[c][k] = *reinterpret_cast<const codes_t *>(codes + (e0 >> 3));
         wsc[c][k] = scales[si];
       }
     }
@@ -786,12 +839,25 @@ __global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
       for (int bb = 0; bb < 4; ++bb) {
         const int n = 4 * c + bb;
         u32x4_t (&bx)[8] = bq[n % 2];
-        // the matrix layout: lane (row li, chunk lq) takes unit 4bb + lq
-        const u32x4_t v = lv[li * kRStride + 4 * bb + lq];
-        const u32x2_t cw = lc[li * kRStride + 4 * bb + lq];
-        uint32_t W0 = v.x, W1 = v.y, W2 = v.z, W3 = v.w, P, Q;
-        transpose4(W0, W1, W2, W3);
-        transpose_codes(cw.x, cw.y, P, Q);
+        uint32_t W0, W1, W2, W3, P = 0, Q = 0;
+        if constexpr (NK == 2) {
+          // the matrix layout: lane (row li, chunk lq) takes unit 4bb + lq
+          const u32x4_t v = lv[li * kRStride + 4 * bb + lq];
+          const u32x2_t cw = lc[li * kRStride + 4 * bb + lq];
+          W0 = v.x; W1 = v.y; W2 = v.z; W3 = v.w;
+          transpose4(W0, W1, W2, W3);
+          transpose_codes(cw.x, cw.y, P, Q);
+        } else {
+          // lane (row li, quarter lq) of unit 4bb + s: vals word lq / 2 and
+          // code byte lq, read in place
+          const uint32_t *lvw = reinterpret_cast<const uint32_t *>(lv);
+          const uint8_t *lcb = reinterpret_cast<const uint8_t *>(lc);
+          const int e = li * kRStride + 4 * bb;
+          W0 = lvw[2 * e + (lq >> 1)]; W1 = lvw[2 * (e + 1) + (lq >> 1)];
+          W2 = lvw[2 * (e + 2) + (lq >> 1)]; W3 = lvw[2 * (e + 3) + (lq >> 1)];
+          P = (uint32_t)lcb[4 * e + lq] | ((uint32_t)lcb[4 * (e + 1) + lq] << 8) |
+              ((uint32_t)lcb[4 * (e + 2) + lq] << 16) | ((uint32_t)lcb[4 * (e + 3) + lq] << 24);
+        }
         // the scales of the block's groups (rows 4lq..4lq+3 of each group's
         // last unit), read before the matrix steps
         u32x2_t sv[4 / SG];
@@ -806,10 +872,16 @@ __global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
           const u8_t xv = {bx[2 * s].x, bx[2 * s].y, bx[2 * s].z, bx[2 * s].w,
                            bx[2 * s + 1].x, bx[2 * s + 1].y, bx[2 * s + 1].z, bx[2 * s + 1].w};
           const h16_t hb = __builtin_bit_cast(h16_t, xv);
-          if (s == 0) cg = smfmac_step<0>(W0, hb, cg, P, Q);
-          if (s == 1) cg = smfmac_step<1>(W1, hb, cg, P, Q);
-          if (s == 2) cg = smfmac_step<2>(W2, hb, cg, P, Q);
-          if (s == 3) cg = smfmac_step<3>(W3, hb, cg, P, Q);
+          if constexpr (NK == 2) {
+            if (s == 0) cg = smfmac_step<0>(W0, hb, cg, P, Q);
+            if (s == 1) cg = smfmac_step<1>(W1, hb, cg, P, Q);
+            if (s == 2) cg = smfmac_step<2>(W2, hb, cg, P, Q);
+            if (s == 3) cg = smfmac_step<3>(W3, hb, cg, P, Q);
+          } else {
+            const uint32_t sh = 8u * (uint32_t)(lq & 1);
+            const uint32_t wd = s == 0 ? W0 : (s == 1 ? W1 : (s == 2 ? W2 : W3));
+            cg = smfmac_step_14(wd, (P >> (8 * s)) & 0xFFu, sh, hb, cg);
+          }
           if ((s + 1) % SG == 0) {  // the group ends with this unit (chunks start on 4-unit bounds)
             const u32x2_t g2 = sv[s / SG];
             acc[0] = fmaf(fp16_bits_to_float(g2.x & 0xFFFFu), cg[0], acc[0]);
@@ -870,27 +942,36 @@ bool rows_kernel_enabled() {
   return v;
 }
 
-hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
-                         hipStream_t stream) {
+// The rows kernel covers up to 8 waves of 1 or 2 chunks: K <= 16384.
+bool rows_kernel_fits(const i4s_packed &w) {
+  const int chunks = (w.cols / kSegCols + kRUnits - 1) / kRUnits;
+  return chunks <= 2 * kRMaxWaves;
+}
+
+template <int NK>
+hipError_t launch_rows(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+                       hipStream_t stream) {
   const int units = w.cols / kSegCols;
   const int chunks = (units + kRUnits - 1) / kRUnits;
-  // up to 8 waves of 1 or 2 chunks: K <= 16384
-  if (rows_kernel_enabled() && chunks <= 2 * kRMaxWaves) {
-    const int cpw = chunks > kRMaxWaves ? 2 : 1;
-    const int waves = (chunks + cpw - 1) / cpw;
-    const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
-    const dim3 grid((unsigned)((w.rows + 15) / 16)), block(64 * waves);
-    const size_t lds = (size_t)waves * kRWaveLds;
-#define I4S_ROWS(C, G) hipLaunchKernelGGL((gemv_smfmac_rows_kernel<C, G>), grid, block, lds, stream, w.rows, units, \
-                                          sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, batch, y)
-    if (cpw == 1) {
-      if (sg_shift == 0) I4S_ROWS(1, 1); else if (sg_shift == 1) I4S_ROWS(1, 2); else I4S_ROWS(1, 4);
-    } else {
-      if (sg_shift == 0) I4S_ROWS(2, 1); else if (sg_shift == 1) I4S_ROWS(2, 2); else I4S_ROWS(2, 4);
-    }
-#undef I4S_ROWS
-    return hipGetLastError();
+  const int cpw = chunks > kRMaxWaves ? 2 : 1;
+  const int waves = (chunks + cpw - 1) / cpw;
+  const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
+  const dim3 grid((unsigned)((w.rows + 15) / 16)), block(64 * waves);
+  const size_t lds = (size_t)waves * kRWaveLds;
+#define I4S_ROWS(C, G) hipLaunchKernelGGL((gemv_smfmac_rows_kernel<NK, C, G>), grid, block, lds, stream, w.rows, \
+                                          units, sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, batch, y)
+  if (cpw == 1) {
+    if (sg_shift == 0) I4S_ROWS(1, 1); else if (sg_shift == 1) I4S_ROWS(1, 2); else I4S_ROWS(1, 4);
+  } else {
+    if (sg_shift == 0) I4S_ROWS(2, 1); else if (sg_shift == 1) I4S_ROWS(2, 2); else I4S_ROWS(2, 4);
   }
+#undef I4S_ROWS
+  return hipGetLastError();
+}
+
+hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+                         hipStream_t stream) {
+  if (rows_kernel_enabled() && rows_kernel_fits(w)) return launch_rows<2>(w, x, batch, y, stream);
   const dim3 grid((unsigned)((w.rows + 15) / 16)), block(64 * kMWaves);
   hipLaunchKernelGGL(gemv_smfmac_kernel, grid, block, 0, stream, w.rows, w.cols, w.group_size, w.row_ptr,
                      w.vals, w.codes, w.scales, x, batch, y);
@@ -938,8 +1019,8 @@ hipError_t launch_smfmac_split(const i4s_packed &w, const uint16_t *x, int32_t b
   }
 }
 
-// I4S_BATCH_PATH=valu forces the VALU batch kernel for 2:4 (tuning and
-// cross-checks); read once.
+// I4S_BATCH_PATH=valu forces the VALU batch kernel for 2:4 and 1:4 (tuning
+// and cross-checks); read once.
 bool smfmac_enabled() {
   static const bool v = [] {
     const char *e = getenv("I4S_BATCH_PATH");
@@ -954,9 +1035,11 @@ hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint
   if (NK == 2 && batch >= 2 && smfmac_enabled()) {
     return launch_smfmac(w, x, batch, y, stream);
   }
+  if (NK == 1 && batch >= 2 && smfmac_enabled() && rows_kernel_fits(w)) {
+    return launch_rows<1>(w, x, batch, y, stream);
+  }
   if (batch <= 1) {
-    if constexpr (NK == 2 || NK == 4) return launch_gemv_b1(w, x, y, stream);
-    return launch_t<NK, 1, 4>(w, x, batch, y, stream);
+    return launch_gemv_b1(w, x, y, stream);
   }
   if (batch <= 2) return launch_t<NK, 2, 4>(w, x, batch, y, stream);
   if (batch <= 4) return launch_t<NK, 4, 2>(w, x, batch, y, stream);

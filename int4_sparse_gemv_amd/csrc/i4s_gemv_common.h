@@ -65,6 +65,18 @@ __host__ __device__ constexpr uint32_t pair_selector(uint32_t h) {
   return ((h * 0x808202u) & 0x06060606u) | 0x01000100u;
 }
 
+// 1:4: a pair of stored elements (2k, 2k+1) belongs to groups 2k and 2k+1,
+// each keeping one column; their codes form nibble h = cA | cB << 2.  Two
+// v_perm_b32 selectors move activation cA of group 2k into the low half and
+// activation cB of group 2k+1 into the high half (selector byte 0x0C gives
+// a zero byte), so an OR of the two results is the activation pair.
+__host__ __device__ constexpr uint32_t single_selector_lo(uint32_t c) {
+  return (2 * c) | ((2 * c + 1) << 8) | 0x0C0C0000u;
+}
+__host__ __device__ constexpr uint32_t single_selector_hi(uint32_t c) {
+  return 0x00000C0Cu | ((2 * c) << 16) | ((2 * c + 1) << 24);
+}
+
 __device__ inline float fp16_bits_to_float(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
@@ -137,6 +149,30 @@ __device__ inline void init_selector_table(uint32_t *lut) {
 
 __device__ inline uint32_t lut_read(const uint32_t *lut, uint32_t byte_off) {
   return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lut) + byte_off);
+}
+
+// Fill the 16-entry table of 1:4 selector pairs (32 words, 8-byte aligned);
+// call with threadIdx.x < 16.
+__device__ inline void init_single_table(uint32_t *lut) {
+  lut[2 * threadIdx.x] = single_selector_lo(threadIdx.x & 3u);
+  lut[2 * threadIdx.x + 1] = single_selector_hi(threadIdx.x >> 2);
+}
+
+typedef uint32_t u32x2_lut_t __attribute__((ext_vector_type(2)));
+
+// The selector pair at byte offset 8 * h.
+__device__ inline u32x2_lut_t lut_read2(const uint32_t *lut, uint32_t byte_off) {
+  return *reinterpret_cast<const u32x2_lut_t *>(reinterpret_cast<const char *>(lut) + byte_off);
+}
+
+// Fill whichever selector table pattern NK uses (none for dense).
+template <int NK>
+__device__ inline void init_tables(uint32_t *lut) {
+  if constexpr (NK == 2) {
+    if (threadIdx.x < 16) init_selector_table(lut);
+  } else if constexpr (NK == 1) {
+    if (threadIdx.x < 16) init_single_table(lut);
+  }
 }
 
 // Block barrier that orders LDS only: the fences are restricted to the local

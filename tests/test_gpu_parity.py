@@ -247,13 +247,16 @@ def test_pack_importance_rejects_bad_inputs():
 
 def config_matrices():
     out = []
-    for name in ("c1_512", "c2_4096", "c3_mlp7b", "c5_verify13b"):
+    for name in ("c1_512", "c2_4096", "c3_mlp7b", "c5_verify13b", "x1_4096_1to4"):
         for m in WL.WORKLOADS[name].matrices:
             out.append((name, m))
-    # a sample of the 32-layer stack: a dense and a 2:4 layer, all projections
-    for m in WL.WORKLOADS["c4_stack7b"].matrices:
-        if m.name.startswith(("L0.", "L4.")):
-            out.append(("c4_stack7b", m))
+    # a sample of the 32-layer stacks, all projections: a dense and a 2:4
+    # layer of the first, a 1:4 layer of the mixed one (its 2:4 layers are
+    # shaped like the first stack's)
+    for name, layers in (("c4_stack7b", ("L0.", "L4.")), ("x2_mix_stack7b", ("L4.",))):
+        for m in WL.WORKLOADS[name].matrices:
+            if m.name.startswith(layers):
+                out.append((name, m))
     return out
 
 
@@ -288,7 +291,8 @@ def test_config_pack_and_gemv(name, m):
 
 @pytest.mark.parametrize("rows,cols,n_keep,g", [
     (1, 64, 2, 64), (17, 192, 2, 64), (33, 4160, 2, 64), (100, 8192, 2, 128), (5, 64, 4, 64),
-    (19, 320, 4, 64), (21, 4224, 4, 128), (3, 128, 1, 64), (13, 4352, 1, 256), (16, 16384, 2, 256)])
+    (19, 320, 4, 64), (21, 4224, 4, 128), (3, 128, 1, 64), (13, 4352, 1, 256), (16, 16384, 2, 256),
+    (700, 16384, 1, 128), (9, 20480, 1, 64), (37, 12288, 1, 64)])
 def test_gemv_shapes_and_all_batches(rows, cols, n_keep, g):
     rng = np.random.default_rng(rows + cols)
     w = rand16(rng, (rows, cols))
@@ -378,7 +382,7 @@ def test_run_on_side_stream():
     assert_gemv_close(y.cpu().numpy().astype(np.float64), y_ref, a_ref, "side-stream")
 
 
-@pytest.mark.parametrize("n_keep,batch", [(2, 1), (4, 1), (2, 3), (1, 1), (4, 8)])
+@pytest.mark.parametrize("n_keep,batch", [(2, 1), (4, 1), (2, 3), (1, 1), (4, 8), (1, 6)])
 def test_row_ptr_is_honoured(n_keep, batch):
     """Rows stored in reverse order, described only by row_ptr, give the same y."""
     import int4_sparse_gemv_amd as I

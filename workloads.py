@@ -103,15 +103,17 @@ def make_importance_inputs(rows: int, cols: int, seed: int,
 _PROJ = ("q", "k", "v", "o", "gate", "up", "down")
 
 
-def stack_7b_matrices() -> Tuple[Matrix, ...]:
+def stack_7b_matrices(outer: int = 4, inner: int = 2) -> Tuple[Matrix, ...]:
     """The 224 projections of a 32-layer 7B-shaped decoder, in layer order.
 
-    Layers 0-3 and 28-31 are dense INT4 (n_keep = 4), the others 2:4; each
-    matrix picks its own group size; seed = 100 + 7*layer + projection index.
+    Layers 0-3 and 28-31 take pattern ``outer`` (n_keep; dense INT4 = 4 by
+    default), the others ``inner`` (2:4 by default); each matrix picks its
+    own group size; seed = 100 + 7*layer + projection index, so the weights
+    are the same whatever the patterns.
     """
     out: List[Matrix] = []
     for layer in range(32):
-        n_keep = 4 if (layer < 4 or layer >= 28) else 2
+        n_keep = outer if (layer < 4 or layer >= 28) else inner
         for m, proj in enumerate(_PROJ):
             if proj in ("q", "k", "v", "o"):
                 r, k = 4096, 4096
@@ -147,4 +149,13 @@ WORKLOADS = {
          Matrix("down", 5120, 13824, 2, 128, 2)),
         (4, 8, 16),
         "13B-shaped layers, 2:4, G=128, verification batches of 4, 8 and 16"),
+    # the 1:4 pattern and the layer-wise 2:4/1:4 mix of the page's
+    # "Sparse(Mix)+Quant" setting (which layers count as critical is not
+    # given; here the outer four at each end keep 2:4)
+    "x1_4096_1to4": Workload(
+        "x1_4096_1to4", (Matrix("w", 4096, 4096, 1, 128, 0),), (1, 4, 8, 16),
+        "single 4096x4096 layer, 1:4, G=128, batches 1, 4, 8 and 16"),
+    "x2_mix_stack7b": Workload(
+        "x2_mix_stack7b", stack_7b_matrices(outer=2, inner=1), (1,),
+        "32-layer 7B stack, 2:4 in layers 0-3/28-31, 1:4 elsewhere, adaptive G, batch 1"),
 }
