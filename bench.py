@@ -121,23 +121,27 @@ class Runner:
         return [(d, xp, b, yp, ws.data_ptr() if n else None, ws.numel()) for d, xp, b, yp, n in out]
 
     def timed(self, seq, steps, warmup, trials):
-        """Median (wall ms per step, event ms per step) over trials; seq is visited round-robin."""
+        """Median (wall ms per step, event ms per step) over trials; seq is visited round-robin.
+
+        An item of seq is an i4s_run_ws argument tuple or a callable taking
+        the stream handle and returning a status."""
         import numpy as np
-        torch, run = self.torch, self.lib.i4s_run_ws
+        torch, run_ws = self.torch, self.lib.i4s_run_ws
+
+        def run(item, sh):
+            return item(sh) if callable(item) else run_ws(*item, sh)
         walls, evs = [], []
         if self.args.eager:
             sh = self.stream.cuda_stream
             for i in range(warmup):
-                d, xp, b, yp, wp, wn = seq[i % len(seq)]
-                assert run(d, xp, b, yp, wp, wn, sh) == 0
+                assert run(seq[i % len(seq)], sh) == 0
             for _ in range(trials):
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 t = time.perf_counter()
                 e0.record(self.stream)
                 for i in range(steps):
-                    d, xp, b, yp, wp, wn = seq[i % len(seq)]
-                    run(d, xp, b, yp, wp, wn, sh)
+                    run(seq[i % len(seq)], sh)
                 e1.record(self.stream)
                 torch.cuda.synchronize()
                 walls.append((time.perf_counter() - t) * 1e3 / steps)
@@ -150,8 +154,7 @@ class Runner:
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=cap):
                 for i in range(n):
-                    d, xp, b, yp, wp, wn = seq[i % len(seq)]
-                    st = run(d, xp, b, yp, wp, wn, cap.cuda_stream)
+                    st = run(seq[i % len(seq)], cap.cuda_stream)
                     if st != 0:
                         raise self.B.I4SError(st, "i4s_run")
             graphs.append(g)
@@ -293,13 +296,14 @@ class Runner:
                 "cold_gbs": nbytes / (cold_ev * 1e-3) / 1e9, "hot_gbs": nbytes / (hot_ev * 1e-3) / 1e9,
                 "cold_tflops": flops / (cold_ev * 1e-3) / 1e12}
 
-    def measure_stack(self, trials, name="c4_stack7b"):
-        """The 224 projections of a 32-layer 7B stack, one call each, in layer order."""
+    def measure_stack(self, trials, name="c4_stack7b", fused=False):
+        """The 224 projections of a 32-layer 7B stack in layer order: one call
+        each, or (fused) q/k/v and gate/up as one i4s_run_multi call each, so
+        4 calls per layer.  Fused projections read the same x, as in a model."""
         import workloads as WL
         torch = self.torch
         mats = WL.WORKLOADS[name].matrices
         items, total, groups = [], 0, {}
-        xs = {}
         for m in mats:
             w16, x16 = WL.make_weight_and_x(m, 1)
             p, _ = self.pack(w16, m)
@@ -308,9 +312,25 @@ class Runner:
             items.append((p, x, y, 1))
             total += p.packed_nbytes()
             groups[p.group_size] = groups.get(p.group_size, 0) + 1
-        seq = self.calls(items)
+        if fused:
+            seq = []
+            for layer in range(len(items) // 7):
+                li = items[7 * layer: 7 * layer + 7]  # q, k, v, o, gate, up, down
+                for grp in (li[0:3], li[3:4], li[4:6], li[6:7]):
+                    if len(grp) == 1:
+                        seq.extend(self.calls(grp))
+                        continue
+                    descs = [p.descriptor() for p, _, _, _ in grp]
+                    arr = (self.B.i4s_packed * len(grp))(*descs)
+                    ys = (ctypes.c_void_p * len(grp))(*[y.data_ptr() for _, _, y, _ in grp])
+                    self.keep.extend([descs, arr, ys])
+                    xp = grp[0][1].data_ptr()  # the group shares its first projection's x
+                    seq.append(lambda sh, arr=arr, n=len(grp), xp=xp, ys=ys:
+                               self.lib.i4s_run_multi(arr, n, xp, 1, ys, sh))
+        else:
+            seq = self.calls(items)
         wall, ev = self.timed(seq, len(seq), len(seq), trials)
-        res = {"calls": len(seq), "packed_bytes": total, "us_per_pass": ev * len(seq) * 1e3,
+        res = {"calls": len(seq), "fused": fused, "packed_bytes": total, "us_per_pass": ev * len(seq) * 1e3,
                "us_per_layer": ev * len(seq) * 1e3 / 32, "gbs": total / (ev * len(seq) * 1e-3) / 1e9,
                "group_sizes": groups}
         del items, seq
@@ -446,11 +466,12 @@ def run_suite(R, args):
     for name in stacks:
         if args.no_stack or name not in names:
             continue
-        s = R.measure_stack(3, name)
-        s["workload"] = name + "/all"
-        print(f"suite {name}: {s['us_per_pass']:.1f} us per 224-call pass ({s['gbs']:.0f} GB/s)",
-              file=sys.stderr, flush=True)
-        out.append(s)
+        for fused in (False, True):
+            s = R.measure_stack(3, name, fused)
+            s["workload"] = name + ("/all-fused" if fused else "/all")
+            print(f"suite {s['workload']}: {s['us_per_pass']:.1f} us per {s['calls']}-call pass "
+                  f"({s['gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+            out.append(s)
     return out
 
 

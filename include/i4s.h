@@ -64,6 +64,7 @@ extern "C" {
 
 #define I4S_FORMAT_VERSION 1
 #define I4S_MAX_BATCH 16
+#define I4S_MAX_MULTI 8
 
 typedef enum i4s_status {
   I4S_OK = 0,
@@ -210,6 +211,30 @@ i4s_status i4s_run_workspace_size(const i4s_packed *w /* host */, int32_t batch,
 i4s_status i4s_run_ws(const i4s_packed *w /* host */, const uint16_t *x_fp16,
                       int32_t batch, uint16_t *y_fp16, void *workspace,
                       uint64_t workspace_bytes, void *stream);
+
+/* y_m = W_hat_m x for n layers that read the same activations (the q, k, v
+ * projections of an attention block; the gate and up projections of an MLP),
+ * in one kernel launch where possible: horizontal fusion, which pays the
+ * per-launch cost once instead of n times (the SparseGemv of section 3.3 of
+ * the page, applied to several weights at once).
+ *   w      : host array of n descriptors as for i4s_run; every layer has the
+ *            same cols.
+ *   n      : 1 .. I4S_MAX_MULTI.
+ *   x_fp16 : [batch][cols] fp16 bits, as for i4s_run, shared by all layers.
+ *   y_fp16 : host array of n device pointers; y_fp16[m] is [batch][rows_m]
+ *            fp16 bits, 2-byte aligned, fully overwritten.  The outputs must
+ *            not overlap one another, x, or any layer's packed buffers.
+ * Results are bit-identical to n i4s_run calls.  One launch when the layers
+ * share n_keep and group_size and either batch is 1 and cols <= 16384, or
+ * batch >= 2, n_keep is 1 or 2 and cols <= 16384; otherwise one launch per
+ * layer, in order, on `stream`.  Asynchronous; allocates nothing.
+ * Errors: as i4s_run (reported for the first offending layer), plus
+ * I4S_ERR_INVALID_ARGUMENT for n out of range, NULL arrays, differing cols
+ * or overlapping outputs. */
+i4s_status i4s_run_multi(const i4s_packed *w /* host, n entries */, int32_t n,
+                         const uint16_t *x_fp16, int32_t batch,
+                         uint16_t *const *y_fp16 /* host, n device pointers */,
+                         void *stream);
 
 /* Static text for a status code (never NULL). */
 const char *i4s_status_string(i4s_status s);

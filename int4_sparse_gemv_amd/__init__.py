@@ -20,11 +20,11 @@ import ctypes
 from . import _binding as B
 from ._binding import (  # noqa: F401  (the C names)
     I4SError, i4s_format_version, i4s_last_error, i4s_pack, i4s_pack_ex, i4s_pack_sizes, i4s_run,
-    i4s_run_workspace_size, i4s_run_ws, i4s_status_string, i4s_version,
+    i4s_run_multi, i4s_run_workspace_size, i4s_run_ws, i4s_status_string, i4s_version,
 )
 
-__all__ = ["PackedWeight", "pack", "run", "pack_sizes", "run_workspace_size", "I4SError",
-           "i4s_pack_sizes", "i4s_pack", "i4s_pack_ex", "i4s_run", "i4s_run_workspace_size", "i4s_run_ws",
+__all__ = ["PackedWeight", "pack", "run", "run_multi", "pack_sizes", "run_workspace_size", "I4SError",
+           "i4s_pack_sizes", "i4s_pack", "i4s_pack_ex", "i4s_run", "i4s_run_multi", "i4s_run_workspace_size", "i4s_run_ws",
            "i4s_status_string", "i4s_last_error", "i4s_version", "i4s_format_version"]
 
 
@@ -187,3 +187,26 @@ def run(p: PackedWeight, x, out=None, descriptor: Optional[B.i4s_packed] = None,
     else:
         B.check(B.i4s_run(d, x.data_ptr(), batch, out.data_ptr(), stream), "i4s_run")
     return out[0] if squeeze else out
+
+
+def run_multi(layers, x, outs=None):
+    """y_m = W_hat_m x for layers sharing x, in one launch where possible.
+
+    ``layers``: PackedWeight objects with the same cols.  ``x``: float16
+    [batch][cols] (or [cols]) on the GPU.  Returns a list of outputs (or
+    fills ``outs``).  Calls ``i4s_run_multi``.
+    """
+    torch = _torch()
+    squeeze = x.dim() == 1
+    if squeeze:
+        x = x.unsqueeze(0)
+    if x.dtype != torch.float16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be float16 [batch][cols] on the GPU")
+    x = x.contiguous()
+    batch = x.shape[0]
+    if outs is None:
+        outs = [torch.empty(batch, p.rows, dtype=torch.float16, device=x.device) for p in layers]
+    descs = [p.descriptor() for p in layers]
+    B.check(B.i4s_run_multi(descs, x.data_ptr(), batch, [o.data_ptr() for o in outs], _stream_handle(x.device)),
+            "i4s_run_multi")
+    return [o[0] for o in outs] if squeeze else outs

@@ -21,6 +21,7 @@ I4S_ERR_NONFINITE_WEIGHT = 3
 I4S_ERR_WORKSPACE_TOO_SMALL = 4
 I4S_ERR_DEVICE = 5
 I4S_MAX_BATCH = 16
+I4S_MAX_MULTI = 8
 I4S_FORMAT_VERSION = 1
 
 
@@ -77,6 +78,8 @@ SIGNATURES = {
                                               ctypes.POINTER(ctypes.c_uint64)]),
     "i4s_run_ws": (ctypes.c_int, [ctypes.POINTER(i4s_packed), ctypes.c_void_p, ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
+    "i4s_run_multi": (ctypes.c_int, [ctypes.POINTER(i4s_packed), ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
     "i4s_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "i4s_last_error": (ctypes.c_char_p, []),
     "i4s_version": (ctypes.c_int32, []),
@@ -144,6 +147,14 @@ def i4s_run_workspace_size(packed, batch, out):
 
 def i4s_run_ws(packed, x_ptr, batch, y_ptr, ws_ptr, ws_bytes, stream):
     return load().i4s_run_ws(ctypes.byref(packed), x_ptr, batch, y_ptr, ws_ptr, ws_bytes, stream)
+
+
+def i4s_run_multi(packed_list, x_ptr, batch, y_ptrs, stream):
+    """packed_list: sequence of i4s_packed; y_ptrs: sequence of device addresses."""
+    n = len(packed_list)
+    arr = (i4s_packed * max(n, 1))(*packed_list)
+    ys = (ctypes.c_void_p * max(n, 1))(*y_ptrs)
+    return load().i4s_run_multi(arr, n, x_ptr, batch, ys, stream)
 
 
 def i4s_status_string(status):

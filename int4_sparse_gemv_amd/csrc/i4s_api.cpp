@@ -274,6 +274,40 @@ i4s_status i4s_run_ws(const i4s_packed *w, const uint16_t *x_fp16, int32_t batch
   return I4S_OK;
 }
 
+i4s_status i4s_run_multi(const i4s_packed *w, int32_t n, const uint16_t *x_fp16, int32_t batch,
+                         uint16_t *const *y_fp16, void *stream) {
+  if (!w || !y_fp16) return fail(I4S_ERR_INVALID_ARGUMENT, "w or y_fp16 is NULL");
+  if (n < 1 || n > I4S_MAX_MULTI) return fail(I4S_ERR_INVALID_ARGUMENT, "n=%d must be in [1, %d]", n, I4S_MAX_MULTI);
+  for (int32_t m = 0; m < n; ++m) {
+    i4s_status st = validate_run(&w[m], x_fp16, batch, y_fp16[m]);
+    if (st != I4S_OK) return st;
+    if (w[m].cols != w[0].cols) return fail(I4S_ERR_INVALID_ARGUMENT, "layer %d has cols %d, layer 0 has %d", m,
+                                            w[m].cols, w[0].cols);
+  }
+  // an output must not overlap another output or another layer's packed
+  // buffers: in one launch all layers run at once
+  for (int32_t m = 0; m < n; ++m) {
+    const uint64_t yb = 2ull * batch * w[m].rows;
+    for (int32_t j = 0; j < n; ++j) {
+      if (j == m) continue;
+      const i4s_packed &o = w[j];
+      const int64_t nnz = o.nnz;
+      if (overlap(y_fp16[m], yb, y_fp16[j], 2ull * batch * o.rows))
+        return fail(I4S_ERR_INVALID_ARGUMENT, "outputs %d and %d overlap", m, j);
+      if (overlap(y_fp16[m], yb, o.vals, (uint64_t)nnz / 2) ||
+          overlap(y_fp16[m], yb, o.scales, 2ull * o.rows * (o.cols / o.group_size)) ||
+          overlap(y_fp16[m], yb, o.row_ptr, 4ull * (o.rows + 1)) ||
+          (o.n_keep < 4 && overlap(y_fp16[m], yb, o.codes, (uint64_t)nnz / 4)))
+        return fail(I4S_ERR_INVALID_ARGUMENT, "output %d overlaps the packed buffers of layer %d", m, j);
+    }
+  }
+  i4s_status st = check_device();
+  if (st != I4S_OK) return st;
+  const hipError_t e = i4s::launch_gemv_multi(w, n, x_fp16, batch, y_fp16, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "gemv launch");
+  return I4S_OK;
+}
+
 const char *i4s_status_string(i4s_status s) {
   switch (s) {
     case I4S_OK: return "ok";

@@ -215,18 +215,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
 // are in, which overlaps the decode with the stream.
 
 // units = K / 64; sg_shift = log2(G / 64).  Shapes arrive pre-divided so the
-// prologue before the first load is a handful of scalar shifts.
+// prologue before the first load is a handful of scalar shifts.  `blk` is
+// the block's index within its layer; xs and lut are the block's LDS.
 template <int NK, int RPW, int UPL, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
-    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
+__device__ __forceinline__ void b1_direct_body(
+    int blk, int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
-    uint16_t *__restrict__ y) {
-  extern __shared__ __align__(16) uint16_t xs[];  // [units][kStrideB1]
-  __shared__ __align__(8) uint32_t lut[32];
+    uint16_t *__restrict__ y, uint16_t *xs, uint32_t *lut) {
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
-  const int row0 = (blockIdx.x * WAVES + wave) * RPW;
+  const int row0 = (blk * WAVES + wave) * RPW;
   const int nvec = units * (kSegCols / 8);  // uint4 pieces of x
   const uint32_t nnz_row = (uint32_t)units * 16 * NK;
   const uint32_t ngroups = (uint32_t)units >> sg_shift;
@@ -329,6 +328,34 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
   }
 }
 
+template <int NK, int RPW, int UPL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
+    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
+    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
+    uint16_t *__restrict__ y) {
+  extern __shared__ __align__(16) uint16_t xs[];  // [units][kStrideB1]
+  __shared__ __align__(8) uint32_t lut[32];
+  b1_direct_body<NK, RPW, UPL, WAVES>(blockIdx.x, rows, units, sg_shift, row_ptr, vals, codes, scales, x, y,
+                                      xs, lut);
+}
+
+// Several layers that share x in one launch (horizontal fusion): each block
+// finds its layer from the cumulative block counts (a few scalar compares on
+// preloaded arguments) and runs the single-layer body on it.
+template <int NK, int RPW, int UPL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_multi_kernel(
+    int units, const uint16_t *__restrict__ x, MultiDesc d) {
+  extern __shared__ __align__(16) uint16_t xs[];  // [units][kStrideB1]
+  __shared__ __align__(8) uint32_t lut[32];
+  int m = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxMulti; ++i) m += (i < d.n && (int)blockIdx.x >= d.block_end[i - 1]) ? 1 : 0;
+  const int first = m == 0 ? 0 : d.block_end[m - 1];
+  b1_direct_body<NK, RPW, UPL, WAVES>((int)blockIdx.x - first, d.rows[m], units, d.sg_shift[m], d.row_ptr[m],
+                                      d.vals[m], d.codes[m], d.scales[m], x, d.y[m], xs, lut);
+}
+
 // ---------------------------------------------------------------------------
 // dispatch
 
@@ -345,6 +372,42 @@ hipError_t launch_b1_direct(const i4s_packed &w, const uint16_t *x, uint16_t *y,
   hipLaunchKernelGGL((gemv_b1_direct_kernel<NK, RPW, UPL, kB1Waves>), grid, block, lds, stream, w.rows,
                      units, sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, y);
   return hipGetLastError();
+}
+
+template <int NK, int RPW, int UPL>
+hipError_t launch_b1_direct_multi(const i4s_packed *w, int32_t n, const uint16_t *x, uint16_t *const *y,
+                                  hipStream_t stream) {
+  const int units = w[0].cols / kSegCols;
+  const size_t lds = (size_t)units * kStrideB1 * 2;
+  const int rows_per_block = kB1Waves * RPW;
+  MultiDesc d = {};
+  d.n = n;
+  int blocks = 0;
+  for (int m = 0; m < n; ++m) {
+    blocks += (w[m].rows + rows_per_block - 1) / rows_per_block;
+    d.block_end[m] = blocks;
+    d.rows[m] = w[m].rows;
+    d.sg_shift[m] = w[m].group_size == 64 ? 0 : (w[m].group_size == 128 ? 1 : 2);
+    d.row_ptr[m] = w[m].row_ptr;
+    d.vals[m] = w[m].vals;
+    d.codes[m] = w[m].codes;
+    d.scales[m] = w[m].scales;
+    d.y[m] = y[m];
+  }
+  hipLaunchKernelGGL((gemv_b1_direct_multi_kernel<NK, RPW, UPL, kB1Waves>), dim3((unsigned)blocks),
+                     dim3(64 * kB1Waves), lds, stream, units, x, d);
+  return hipGetLastError();
+}
+
+template <int NK, int RPW>
+hipError_t launch_b1_multi_t(const i4s_packed *w, int32_t n, const uint16_t *x, uint16_t *const *y,
+                             hipStream_t stream) {
+  switch ((w[0].cols / kSegCols + 63) / 64) {
+    case 1: return launch_b1_direct_multi<NK, RPW, 1>(w, n, x, y, stream);
+    case 2: return launch_b1_direct_multi<NK, RPW, 2>(w, n, x, y, stream);
+    case 3: return launch_b1_direct_multi<NK, RPW, 3>(w, n, x, y, stream);
+    default: return launch_b1_direct_multi<NK, RPW, 4>(w, n, x, y, stream);
+  }
 }
 
 // I4S_B1_KERNEL=stream forces the pipelined batch-1 kernel (tuning); read once.
@@ -414,6 +477,24 @@ hipError_t launch_gemv_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, h
     case 2: return launch_b1<4, 2>(w, x, y, stream);
     case 4: return launch_b1<4, 4>(w, x, y, stream);
     default: return launch_b1<4, 1>(w, x, y, stream);
+  }
+}
+
+hipError_t launch_gemv_b1_multi(const i4s_packed *w, int32_t n, const uint16_t *x, uint16_t *const *y,
+                                hipStream_t stream) {
+  const int units = w[0].cols / kSegCols;
+  if (!b1_direct_enabled() || units > 256) return hipErrorNotSupported;
+  int max_rows = 0;
+  for (int m = 0; m < n; ++m) {
+    if (w[m].n_keep != w[0].n_keep || w[m].cols != w[0].cols) return hipErrorNotSupported;
+    max_rows = max_rows > w[m].rows ? max_rows : w[m].rows;
+  }
+  // rows per wave as for the tallest layer alone
+  const int rpw = b1_rows_per_wave(max_rows) >= 2 ? 2 : 1;
+  switch (w[0].n_keep) {
+    case 1: return rpw == 2 ? launch_b1_multi_t<1, 2>(w, n, x, y, stream) : launch_b1_multi_t<1, 1>(w, n, x, y, stream);
+    case 2: return rpw == 2 ? launch_b1_multi_t<2, 2>(w, n, x, y, stream) : launch_b1_multi_t<2, 1>(w, n, x, y, stream);
+    default: return rpw == 2 ? launch_b1_multi_t<4, 2>(w, n, x, y, stream) : launch_b1_multi_t<4, 1>(w, n, x, y, stream);
   }
 }
 

@@ -738,16 +738,17 @@ __device__ inline f4_t smfmac_step_14(uint32_t wd, uint32_t cb, uint32_t sh, con
 // ceil(units / (16 * CPW)).  SG = units per quantization group (G / 64: 1, 2
 // or 4), so where a group ends inside a block of 4 units is known at compile
 // time.
+// `tile` is the block's 16-row tile within its layer; lds is the block's
+// dynamic LDS ([waves][kRWaveLds]).
 template <int NK, int CPW, int SG>
-__global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
-    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
+__device__ __forceinline__ void rows_body(
+    int tile, int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
-    uint16_t *__restrict__ y) {
-  extern __shared__ __align__(16) uint8_t lds[];  // [waves][kRWaveLds]
+    uint16_t *__restrict__ y, uint8_t *lds) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nwaves = blockDim.x / 64;
   const int li = lane % 16, lq = lane / 16;
-  const int row0 = blockIdx.x * 16;
+  const int row0 = tile * 16;
   const uint32_t nnz_row = (uint32_t)units * 16 * NK;
   const uint32_t ngroups = (uint32_t)units >> sg_shift;
   typedef typename std::conditional<NK == 2, u32x4_t, u32x2_t>::type vals_t;    // a unit's vals
@@ -916,6 +917,31 @@ __global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
   }
 }
 
+template <int NK, int CPW, int SG>
+__global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
+    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
+    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
+    uint16_t *__restrict__ y) {
+  extern __shared__ __align__(16) uint8_t lds[];  // [waves][kRWaveLds]
+  rows_body<NK, CPW, SG>(blockIdx.x, rows, units, sg_shift, row_ptr, vals, codes, scales, x, batch, y, lds);
+}
+
+// Several layers that share x (and N, G and K) in one launch: each block
+// finds its layer from the cumulative tile counts and runs the single-layer
+// body on it.
+template <int NK, int CPW, int SG>
+__global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_multi_kernel(
+    int units, const uint16_t *__restrict__ x, int batch, MultiDesc d) {
+  extern __shared__ __align__(16) uint8_t lds[];  // [waves][kRWaveLds]
+  int m = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxMulti; ++i) m += (i < d.n && (int)blockIdx.x >= d.block_end[i - 1]) ? 1 : 0;
+  const int first = m == 0 ? 0 : d.block_end[m - 1];
+  rows_body<NK, CPW, SG>((int)blockIdx.x - first, d.rows[m], units, d.sg_shift[m], d.row_ptr[m], d.vals[m],
+                         d.codes[m], d.scales[m], x, batch, d.y[m], lds);
+}
+
 // ---------------------------------------------------------------------------
 // dispatch
 
@@ -960,6 +986,41 @@ hipError_t launch_rows(const i4s_packed &w, const uint16_t *x, int32_t batch, ui
   const size_t lds = (size_t)waves * kRWaveLds;
 #define I4S_ROWS(C, G) hipLaunchKernelGGL((gemv_smfmac_rows_kernel<NK, C, G>), grid, block, lds, stream, w.rows, \
                                           units, sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, batch, y)
+  if (cpw == 1) {
+    if (sg_shift == 0) I4S_ROWS(1, 1); else if (sg_shift == 1) I4S_ROWS(1, 2); else I4S_ROWS(1, 4);
+  } else {
+    if (sg_shift == 0) I4S_ROWS(2, 1); else if (sg_shift == 1) I4S_ROWS(2, 2); else I4S_ROWS(2, 4);
+  }
+#undef I4S_ROWS
+  return hipGetLastError();
+}
+
+template <int NK>
+hipError_t launch_rows_multi(const i4s_packed *w, int32_t n, const uint16_t *x, int32_t batch,
+                             uint16_t *const *y, hipStream_t stream) {
+  const int units = w[0].cols / kSegCols;
+  const int chunks = (units + kRUnits - 1) / kRUnits;
+  const int cpw = chunks > kRMaxWaves ? 2 : 1;
+  const int waves = (chunks + cpw - 1) / cpw;
+  const int sg_shift = w[0].group_size == 64 ? 0 : (w[0].group_size == 128 ? 1 : 2);
+  MultiDesc d = {};
+  d.n = n;
+  int tiles = 0;
+  for (int m = 0; m < n; ++m) {
+    tiles += (w[m].rows + 15) / 16;
+    d.block_end[m] = tiles;
+    d.rows[m] = w[m].rows;
+    d.sg_shift[m] = sg_shift;
+    d.row_ptr[m] = w[m].row_ptr;
+    d.vals[m] = w[m].vals;
+    d.codes[m] = w[m].codes;
+    d.scales[m] = w[m].scales;
+    d.y[m] = y[m];
+  }
+  const dim3 grid((unsigned)tiles), block(64 * waves);
+  const size_t lds = (size_t)waves * kRWaveLds;
+#define I4S_ROWS(C, G) hipLaunchKernelGGL((gemv_smfmac_rows_multi_kernel<NK, C, G>), grid, block, lds, stream, \
+                                          units, x, batch, d)
   if (cpw == 1) {
     if (sg_shift == 0) I4S_ROWS(1, 1); else if (sg_shift == 1) I4S_ROWS(1, 2); else I4S_ROWS(1, 4);
   } else {
@@ -1097,6 +1158,28 @@ hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch, ui
     case 2: return launch_nk<2>(w, x, batch, y, stream);
     default: return launch_nk<4>(w, x, batch, y, stream);
   }
+}
+
+hipError_t launch_gemv_multi(const i4s_packed *w, int32_t n, const uint16_t *x, int32_t batch,
+                             uint16_t *const *y, hipStream_t stream) {
+  bool same = true;  // one pattern, one group size, one K
+  for (int m = 1; m < n; ++m)
+    same &= w[m].n_keep == w[0].n_keep && w[m].group_size == w[0].group_size && w[m].cols == w[0].cols;
+  if (n > 1 && same) {
+    if (batch == 1) {
+      const hipError_t e = launch_gemv_b1_multi(w, n, x, y, stream);
+      if (e != hipErrorNotSupported) return e;
+    } else if ((w[0].n_keep == 2 || w[0].n_keep == 1) && smfmac_enabled() && rows_kernel_enabled() &&
+               rows_kernel_fits(w[0])) {
+      return w[0].n_keep == 2 ? launch_rows_multi<2>(w, n, x, batch, y, stream)
+                              : launch_rows_multi<1>(w, n, x, batch, y, stream);
+    }
+  }
+  for (int m = 0; m < n; ++m) {
+    const hipError_t e = launch_gemv(w[m], x, batch, y[m], stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace i4s

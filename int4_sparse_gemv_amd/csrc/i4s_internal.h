@@ -47,9 +47,33 @@ hipError_t launch_pack_emit(const uint16_t *w, const float *col_norm, const uint
                             int32_t rows, int32_t cols, int32_t n_keep, int32_t group_size,
                             const i4s_packed &out, hipStream_t stream);
 
+// Layers of one fused launch (i4s_run_multi): block b belongs to the first
+// layer m with b < block_end[m]; its blocks are numbered from the previous
+// layer's block_end.  Passed by value as a kernel argument.
+constexpr int kMaxMulti = I4S_MAX_MULTI;
+struct MultiDesc {
+  int32_t n;
+  int32_t block_end[kMaxMulti];
+  int32_t rows[kMaxMulti];
+  int32_t sg_shift[kMaxMulti];
+  const int32_t *row_ptr[kMaxMulti];
+  const uint8_t *vals[kMaxMulti];
+  const uint16_t *codes[kMaxMulti];
+  const uint16_t *scales[kMaxMulti];
+  uint16_t *y[kMaxMulti];
+};
+
 // GEMV kernels.  launch_gemv (i4s_gemv_batch.hip) dispatches every call;
 // launch_gemv_b1 (i4s_gemv_b1.hip) runs batch 1 for n_keep 2 and 4.
 hipError_t launch_gemv_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream);
+// Fused batch-1 launch of n layers with one n_keep and K <= 16384; returns
+// hipErrorNotSupported (launching nothing) when the layers do not fit it.
+hipError_t launch_gemv_b1_multi(const i4s_packed *w, int32_t n, const uint16_t *x, uint16_t *const *y,
+                                hipStream_t stream);
+// Every layer of an i4s_run_multi call: one launch when a fused kernel
+// covers them, else one launch per layer in order.
+hipError_t launch_gemv_multi(const i4s_packed *w, int32_t n, const uint16_t *x, int32_t batch,
+                             uint16_t *const *y, hipStream_t stream);
 hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch,
                        uint16_t *y, hipStream_t stream);
 

@@ -34,6 +34,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["i4s_pack_sizes", "i4s_pack", "i4s_pack_ex", "i4s_run", "i4s_run_workspace_size", "i4s_run_ws",
+         "i4s_run_multi",
          "i4s_status_string", "i4s_last_error", "i4s_version", "i4s_format_version"])
 
 
@@ -136,6 +137,25 @@ def test_run_rejects_overlap_and_misalignment(lib):
     assert B.i4s_run(d, (1 << 30) + 2, 1, 1 << 31, None) == B.I4S_ERR_INVALID_ARGUMENT   # x misaligned
     assert B.i4s_run(d, 1 << 30, 1, (1 << 20) + (1 << 16), None) == B.I4S_ERR_INVALID_ARGUMENT  # y on vals
     assert lib.i4s_run(None, 1 << 30, 1, 1 << 31, None) == B.I4S_ERR_INVALID_ARGUMENT
+
+
+def test_run_multi_validation_fails_before_any_device_call(lib):
+    x = 1 << 30
+    a, b = _desc(base=1 << 20), _desc(base=1 << 24)
+    y0, y1 = 1 << 31, (1 << 31) + (1 << 20)
+    E = B.I4S_ERR_INVALID_ARGUMENT
+    assert B.i4s_run_multi([], x, 1, [], None) == E                         # n = 0
+    assert B.i4s_run_multi([a] * 9, x, 1, [y0 + (k << 20) for k in range(9)], None) == E  # n > 8
+    assert lib.i4s_run_multi(None, 1, x, 1, None, None) == E
+    c = _desc(cols=512, base=1 << 24)
+    assert B.i4s_run_multi([a, c], x, 1, [y0, y1], None) == E               # cols differ
+    assert B.i4s_run_multi([a, b], x, 1, [y0, y0 + 64], None) == E          # outputs overlap
+    assert B.i4s_run_multi([a, b], x, 1, [y0, (1 << 20) + (1 << 16)], None) == E  # y1 on layer 0's vals
+    assert B.i4s_run_multi([a, b], x, 17, [y0, y1], None) == E              # batch out of range
+    bad = _desc(base=1 << 24)
+    bad.nnz = 5
+    assert B.i4s_run_multi([a, bad], x, 1, [y0, y1], None) == E             # a bad descriptor
+    assert "layer" in B.i4s_last_error() or B.i4s_last_error()
 
 
 def test_pack_validation_fails_before_any_device_call(lib):

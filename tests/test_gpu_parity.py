@@ -363,6 +363,45 @@ def test_batch_rows_match_single_calls(n_keep):
         np.testing.assert_array_equal(gpu_run(p, x[:nb]), y16[:nb])
 
 
+# layers of one fused call: (rows, n_keep, G) per layer, K, batch
+MULTI_CASES = [
+    ([(512, 2, 128), (1000, 2, 128), (777, 2, 128)], 4096, 1),     # q/k/v-like, fused batch-1
+    ([(8200, 4, 64), (300, 4, 64)], 1024, 1),                     # dense, two rows per wave
+    ([(100, 1, 64), (33, 1, 64), (257, 1, 64)], 2048, 1),         # 1:4, fused batch-1
+    ([(512, 2, 128), (1000, 2, 128), (777, 2, 128)], 4096, 5),     # fused matrix-core batch
+    ([(200, 1, 256), (70, 1, 256)], 3072, 16),                    # 1:4 fused matrix-core batch
+    ([(96, 4, 64), (50, 4, 64)], 1024, 8),                        # dense batch: one launch per layer
+    ([(64, 2, 64), (80, 2, 128)], 1024, 1),                       # group sizes differ: per layer
+    ([(40, 2, 64)] * 8, 512, 3),                                  # the most layers
+    ([(24, 2, 64), (40, 2, 64)], 20480, 1),                       # K > 16384: per layer
+]
+
+
+@pytest.mark.parametrize("layers,cols,batch", MULTI_CASES)
+def test_run_multi_equals_single_calls(layers, cols, batch):
+    import int4_sparse_gemv_amd as I
+    rng = np.random.default_rng(cols + batch + len(layers))
+    say(f"case run-multi {layers} K={cols} b={batch}")
+    packs, refs = [], []
+    for rows, n_keep, g in layers:
+        w = rand16(rng, (rows, cols))
+        ref = O.pack(w, n_keep, g)
+        p = gpu_pack(w, n_keep, g)
+        assert_pack_equal(p, ref, "multi pack")
+        packs.append(p)
+        refs.append(ref)
+    x16 = rng.standard_normal((batch, cols)).astype(np.float16)
+    x = torch.from_numpy(x16.view(np.int16)).cuda().view(torch.float16)
+    outs = I.run_multi(packs, x)
+    singles = [I.run(p, x, use_workspace=False) for p in packs]
+    torch.cuda.synchronize()
+    for m, (o, s1, ref) in enumerate(zip(outs, singles, refs)):
+        got = o.cpu().numpy()
+        assert np.array_equal(got.view(np.uint16), s1.cpu().numpy().view(np.uint16)), f"layer {m} differs from i4s_run"
+        y_ref, a_ref = O.gemv(O.reconstruct(ref), x16)
+        assert_gemv_close(got.astype(np.float64), y_ref, a_ref, f"multi layer {m}")
+
+
 def test_run_on_side_stream():
     import int4_sparse_gemv_amd as I
     rng = np.random.default_rng(79)
