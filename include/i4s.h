@@ -184,8 +184,9 @@ i4s_status i4s_run(const i4s_packed *w /* host */, const uint16_t *x_fp16,
                    int32_t batch, uint16_t *y_fp16, void *stream);
 
 /* Bytes of device workspace i4s_run_ws needs for this layer and batch; 0
- * when the call needs none (batch 1, a pattern other than 2:4, or a layer
- * whose K split has a single slice).  Host-only and pure.  Errors:
+ * when the call needs none: batch 1, a pattern other than 2:4, K <= 16384
+ * (the one-launch batch kernel covers those rows whole), or a layer whose K
+ * split has a single slice.  Host-only and pure.  Errors:
  * I4S_ERR_INVALID_ARGUMENT (descriptor inconsistent, batch out of range,
  * bytes == NULL). */
 i4s_status i4s_run_workspace_size(const i4s_packed *w /* host */, int32_t batch,

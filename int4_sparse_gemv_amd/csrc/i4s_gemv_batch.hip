@@ -15,6 +15,7 @@
 // the 8-byte reads of 64 lanes fall in distinct banks.  When the staged
 // activations exceed the LDS budget the K axis is processed in chunks.
 
+#include <atomic>
 #include <type_traits>
 
 #include "i4s_gemv_common.h"
@@ -738,25 +739,31 @@ __device__ inline f4_t smfmac_step_14(uint32_t wd, uint32_t cb, uint32_t sh, con
 // ceil(units / (16 * CPW)).  SG = units per quantization group (G / 64: 1, 2
 // or 4), so where a group ends inside a block of 4 units is known at compile
 // time.
-// `tile` is the block's 16-row tile within its layer; lds is the block's
-// dynamic LDS ([waves][kRWaveLds]).
-template <int NK, int CPW, int SG>
+// `blk` is the block's index within its layer: it covers the TPW 16-row
+// tiles from row 16 * TPW * blk.  lds is the block's dynamic LDS
+// ([waves][TPW][kRWaveLds]).  Each B fragment a wave loads feeds the matrix
+// steps of its TPW tiles (measured on the 13824x5120 layer: the B-fragment
+// loads from L2, not the weight stream, bound the one-tile form; two tiles
+// per wave take 14.8 -> 10.6 us at batch 4 and 23.4 -> 14.6 us at batch 16).
+template <int NK, int CPW, int SG, int TPW>
 __device__ __forceinline__ void rows_body(
-    int tile, int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
+    int blk, int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
     uint16_t *__restrict__ y, uint8_t *lds) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nwaves = blockDim.x / 64;
   const int li = lane % 16, lq = lane / 16;
-  const int row0 = tile * 16;
+  const int row0 = blk * 16 * TPW;
   const uint32_t nnz_row = (uint32_t)units * 16 * NK;
   const uint32_t ngroups = (uint32_t)units >> sg_shift;
   typedef typename std::conditional<NK == 2, u32x4_t, u32x2_t>::type vals_t;    // a unit's vals
   typedef typename std::conditional<NK == 2, u32x2_t, uint32_t>::type codes_t;  // a unit's codes
-  uint8_t *wl = lds + wave * kRWaveLds;
-  vals_t *lv = reinterpret_cast<vals_t *>(wl);                                   // [16 rows][17] vals
-  codes_t *lc = reinterpret_cast<codes_t *>(wl + kRValsBytes);                   // [16 rows][17] codes
-  uint16_t *lsc = reinterpret_cast<uint16_t *>(wl + kRValsBytes + kRCodesBytes);  // [16 units][16 rows]
+  uint8_t *wl = lds + wave * TPW * kRWaveLds;  // the wave's areas, one per tile
+  auto lv_of = [&](int t) { return reinterpret_cast<vals_t *>(wl + t * kRWaveLds); };        // [16 rows][17]
+  auto lc_of = [&](int t) { return reinterpret_cast<codes_t *>(wl + t * kRWaveLds + kRValsBytes); };
+  auto lsc_of = [&](int t) {                                                                  // [16 units][16 rows]
+    return reinterpret_cast<uint16_t *>(wl + t * kRWaveLds + kRValsBytes + kRCodesBytes);
+  };
 
   // B fragments: lane (vector li, column quarter lq); vectors past `batch`
   // read the last real one (their output columns are never stored).  Block
@@ -773,123 +780,155 @@ __device__ __forceinline__ void rows_body(
     }
   };
 
-  // every weight load of the wave: lane (unit li, row lq): row 4k + lq
-  int wrow[4];
+  // every weight load of the wave: lane (unit li, row lq): row 16t + 4k + lq
+  int wrow[TPW][4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) wrow[k] = min(row0 + 4 * k + lq, rows - 1);
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wrow[t][k] = min(row0 + 16 * t + 4 * k + lq, rows - 1);
   u32x4_t bq[2][8];
   load_b(bq[0], 0);
   load_b(bq[1], 1);
-  vals_t wv[CPW][4];
-  codes_t wc[CPW][4];
-  uint16_t wsc[CPW][4];
-  auto load_w = [&](int c, const uint32_t (&base)[4], bool nt) {
+  vals_t wv[CPW][TPW][4];
+  codes_t wc[CPW][TPW][4];
+  uint16_t wsc[CPW][TPW][4];
+  auto load_w = [&](int c, const uint32_t (&base)[TPW][4], bool nt) {
     const int u = min((wave * CPW + c) * kRUnits + li, units - 1);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t e0 = base[k] + (uint32_t)u * 16 * NK;
-      const uint32_t si = (uint32_t)wrow[k] * ngroups + ((uint32_t)u >> sg_shift);
-      if (nt) {
-        wv[c][k] = __builtin_nontemporal_load(reinterpret_cast<const vals_t *>(vals + (e0 >> 1)));
-        wc[c][k] = __builtin_nontemporal_load(reinterpret_cast<const codes_t *>(codes + (e0 >> 3)));
-        wsc[c][k] = __builtin_nontemporal_load(scales + si);
-      } else {
-        wv[c][k] = *reinterpret_cast<const vals_t *>(vals + (e0 >> 1));
-        wc[c][k] = *reinterpret_cast<const codes_t *>(codes + (e0 >> 3));
-        wsc[c][k] = scales[si];
-      }
-    }
-  };
-  uint32_t base[4];
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-  for (int k = 0; k < 4; ++k) base[k] = (uint32_t)wrow[k] * nnz_row;  // the format's offsets
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t e0 = base[t][k] + (uint32_t)u * 16 * NK;
+        const uint32_t si = (uint32_t)wrow[t][k] * ngroups + ((uint32_t)u >> sg_shift);
+        if (nt) {
+          wv[c][t][k] = __builtin_nontemporal_load(reinterpret_cast<const vals_t *>(vals + (e0 >> 1)));
+          wc[c][t][k] = __builtin_nontemporal_load(reinterpret_cast<const codes_t *>(codes + (e0 >> 3)));
+          wsc[c][t][k] = __builtin_nontemporal_load(scales + si);
+        } else {
+          wv[c][t][k] = *reinterpret_cast<const vals_t *>(vals + (e0 >> 1));
+          wc[c][t][k] = *reinterpret_cast<const codes_t *>(codes + (e0 >> 3));
+          wsc[c][t][k] = scales[si];
+        }
+      }
+  };
+  uint32_t base[TPW][4];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) base[t][k] = (uint32_t)wrow[t][k] * nnz_row;  // the format's offsets
 #pragma unroll
   for (int c = 0; c < CPW; ++c) load_w(c, base, true);
-  int32_t rp[4];
+  int32_t rp[TPW][4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) rp[k] = row_ptr[wrow[k]];
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rp[t][k] = row_ptr[wrow[t][k]];
 
   // row_ptr check before the pass: row_ptr is the wave's last load and loads
   // retire in order, so this waits for little beyond the weights the pass
-  // needs anyway.  A tile with a row stored away from the format's offset
+  // needs anyway.  A block with a row stored away from the format's offset
   // fetches its weights again from row_ptr's offsets (every wave of the
   // block sees the same rows, so each decides alone).
   bool moved = false;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) moved |= (uint32_t)rp[k] != base[k];
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) moved |= (uint32_t)rp[t][k] != base[t][k];
   if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) base[k] = (uint32_t)rp[k];
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) base[t][k] = (uint32_t)rp[t][k];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) load_w(c, base, false);
   }
 
   // one pass over the wave's chunks; B fragments two blocks ahead
-  f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  f4_t acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
   {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      // chunk c to the wave's LDS area, in the load layout
+      // chunk c of every tile to the wave's LDS areas, in the load layout.
+      // A unit past the row's end (only the last chunk can hold one; it read
+      // the last unit again) is staged with every nibble 8, i.e. q = 0, so its
+      // matrix steps add exact zeros and the loop below needs no branch.  It
+      // never shares a quantization group with a real unit (K % G == 0).
+      const bool real = (wave * CPW + c) * kRUnits + li < units;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        lv[(4 * k + lq) * kRStride + li] = wv[c][k];
-        lc[(4 * k + lq) * kRStride + li] = wc[c][k];
-        lsc[li * 16 + 4 * k + lq] = wsc[c][k];
+      for (int t = 0; t < TPW; ++t) {
+        vals_t *lv = lv_of(t);
+        codes_t *lc = lc_of(t);
+        uint16_t *lsc = lsc_of(t);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          vals_t zv;
+          if constexpr (NK == 2) zv = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+          else zv = u32x2_t{0x88888888u, 0x88888888u};
+          lv[(4 * k + lq) * kRStride + li] = real ? wv[c][t][k] : zv;
+          lc[(4 * k + lq) * kRStride + li] = wc[c][t][k];
+          lsc[li * 16 + 4 * k + lq] = wsc[c][t][k];
+        }
       }
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const int n = 4 * c + bb;
         u32x4_t (&bx)[8] = bq[n % 2];
-        uint32_t W0, W1, W2, W3, P = 0, Q = 0;
-        if constexpr (NK == 2) {
-          // the matrix layout: lane (row li, chunk lq) takes unit 4bb + lq
-          const u32x4_t v = lv[li * kRStride + 4 * bb + lq];
-          const u32x2_t cw = lc[li * kRStride + 4 * bb + lq];
-          W0 = v.x; W1 = v.y; W2 = v.z; W3 = v.w;
-          transpose4(W0, W1, W2, W3);
-          transpose_codes(cw.x, cw.y, P, Q);
-        } else {
-          // lane (row li, quarter lq) of unit 4bb + s: vals word lq / 2 and
-          // code byte lq, read in place
-          const uint32_t *lvw = reinterpret_cast<const uint32_t *>(lv);
-          const uint8_t *lcb = reinterpret_cast<const uint8_t *>(lc);
-          const int e = li * kRStride + 4 * bb;
-          W0 = lvw[2 * e + (lq >> 1)]; W1 = lvw[2 * (e + 1) + (lq >> 1)];
-          W2 = lvw[2 * (e + 2) + (lq >> 1)]; W3 = lvw[2 * (e + 3) + (lq >> 1)];
-          P = (uint32_t)lcb[4 * e + lq] | ((uint32_t)lcb[4 * (e + 1) + lq] << 8) |
-              ((uint32_t)lcb[4 * (e + 2) + lq] << 16) | ((uint32_t)lcb[4 * (e + 3) + lq] << 24);
-        }
-        // the scales of the block's groups (rows 4lq..4lq+3 of each group's
-        // last unit), read before the matrix steps
-        u32x2_t sv[4 / SG];
 #pragma unroll
-        for (int g = 0; g < 4 / SG; ++g)
-          sv[g] = *reinterpret_cast<const u32x2_t *>(&lsc[(4 * bb + SG * g + SG - 1) * 16 + 4 * lq]);
-        f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int u = unit_of(n, s);
-          if (u >= units) break;  // only the last chunk of a row can end early, on a group bound
-          const u8_t xv = {bx[2 * s].x, bx[2 * s].y, bx[2 * s].z, bx[2 * s].w,
-                           bx[2 * s + 1].x, bx[2 * s + 1].y, bx[2 * s + 1].z, bx[2 * s + 1].w};
-          const h16_t hb = __builtin_bit_cast(h16_t, xv);
+        for (int t = 0; t < TPW; ++t) {
+          const vals_t *lv = lv_of(t);
+          const codes_t *lc = lc_of(t);
+          const uint16_t *lsc = lsc_of(t);
+          uint32_t W0, W1, W2, W3, P = 0, Q = 0;
           if constexpr (NK == 2) {
-            if (s == 0) cg = smfmac_step<0>(W0, hb, cg, P, Q);
-            if (s == 1) cg = smfmac_step<1>(W1, hb, cg, P, Q);
-            if (s == 2) cg = smfmac_step<2>(W2, hb, cg, P, Q);
-            if (s == 3) cg = smfmac_step<3>(W3, hb, cg, P, Q);
+            // the matrix layout: lane (row li, chunk lq) takes unit 4bb + lq
+            const u32x4_t v = lv[li * kRStride + 4 * bb + lq];
+            const u32x2_t cw = lc[li * kRStride + 4 * bb + lq];
+            W0 = v.x; W1 = v.y; W2 = v.z; W3 = v.w;
+            transpose4(W0, W1, W2, W3);
+            transpose_codes(cw.x, cw.y, P, Q);
           } else {
-            const uint32_t sh = 8u * (uint32_t)(lq & 1);
-            const uint32_t wd = s == 0 ? W0 : (s == 1 ? W1 : (s == 2 ? W2 : W3));
-            cg = smfmac_step_14(wd, (P >> (8 * s)) & 0xFFu, sh, hb, cg);
+            // lane (row li, quarter lq) of unit 4bb + s: vals word lq / 2 and
+            // code byte lq, read in place
+            const uint32_t *lvw = reinterpret_cast<const uint32_t *>(lv);
+            const uint8_t *lcb = reinterpret_cast<const uint8_t *>(lc);
+            const int e = li * kRStride + 4 * bb;
+            W0 = lvw[2 * e + (lq >> 1)]; W1 = lvw[2 * (e + 1) + (lq >> 1)];
+            W2 = lvw[2 * (e + 2) + (lq >> 1)]; W3 = lvw[2 * (e + 3) + (lq >> 1)];
+            P = (uint32_t)lcb[4 * e + lq] | ((uint32_t)lcb[4 * (e + 1) + lq] << 8) |
+                ((uint32_t)lcb[4 * (e + 2) + lq] << 16) | ((uint32_t)lcb[4 * (e + 3) + lq] << 24);
           }
-          if ((s + 1) % SG == 0) {  // the group ends with this unit (chunks start on 4-unit bounds)
-            const u32x2_t g2 = sv[s / SG];
-            acc[0] = fmaf(fp16_bits_to_float(g2.x & 0xFFFFu), cg[0], acc[0]);
-            acc[1] = fmaf(fp16_bits_to_float(g2.x >> 16), cg[1], acc[1]);
-            acc[2] = fmaf(fp16_bits_to_float(g2.y & 0xFFFFu), cg[2], acc[2]);
-            acc[3] = fmaf(fp16_bits_to_float(g2.y >> 16), cg[3], acc[3]);
-            cg = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          // the scales of the block's groups (rows 4lq..4lq+3 of each group's
+          // last unit), read before the matrix steps
+          u32x2_t sv[4 / SG];
+#pragma unroll
+          for (int g = 0; g < 4 / SG; ++g)
+            sv[g] = *reinterpret_cast<const u32x2_t *>(&lsc[(4 * bb + SG * g + SG - 1) * 16 + 4 * lq]);
+          f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const u8_t xv = {bx[2 * s].x, bx[2 * s].y, bx[2 * s].z, bx[2 * s].w,
+                             bx[2 * s + 1].x, bx[2 * s + 1].y, bx[2 * s + 1].z, bx[2 * s + 1].w};
+            const h16_t hb = __builtin_bit_cast(h16_t, xv);
+            if constexpr (NK == 2) {
+              if (s == 0) cg = smfmac_step<0>(W0, hb, cg, P, Q);
+              if (s == 1) cg = smfmac_step<1>(W1, hb, cg, P, Q);
+              if (s == 2) cg = smfmac_step<2>(W2, hb, cg, P, Q);
+              if (s == 3) cg = smfmac_step<3>(W3, hb, cg, P, Q);
+            } else {
+              const uint32_t sh = 8u * (uint32_t)(lq & 1);
+              const uint32_t wd = s == 0 ? W0 : (s == 1 ? W1 : (s == 2 ? W2 : W3));
+              cg = smfmac_step_14(wd, (P >> (8 * s)) & 0xFFu, sh, hb, cg);
+            }
+            if ((s + 1) % SG == 0) {  // the group ends with this unit (chunks start on 4-unit bounds)
+              const u32x2_t g2 = sv[s / SG];
+              acc[t][0] = fmaf(fp16_bits_to_float(g2.x & 0xFFFFu), cg[0], acc[t][0]);
+              acc[t][1] = fmaf(fp16_bits_to_float(g2.x >> 16), cg[1], acc[t][1]);
+              acc[t][2] = fmaf(fp16_bits_to_float(g2.y & 0xFFFFu), cg[2], acc[t][2]);
+              acc[t][3] = fmaf(fp16_bits_to_float(g2.y >> 16), cg[3], acc[t][3]);
+              cg = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
           }
         }
         // the buffer just used takes block n + 2; the scheduling barriers keep
@@ -904,42 +943,47 @@ __device__ __forceinline__ void rows_body(
   // sum the waves' partial tiles (each wave writes into its own area, which
   // it no longer reads) and store y
   f4_t *red = reinterpret_cast<f4_t *>(wl);
-  red[lane] = acc;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) red[64 * t + lane] = acc[t];
   lds_barrier();
   if (wave == 0) {
-    f4_t sum = acc;
-    for (int w = 1; w < nwaves; ++w) sum += reinterpret_cast<const f4_t *>(lds + w * kRWaveLds)[lane];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + 4 * lq + r;
-      if (li < batch && row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(sum[r]);
+    for (int t = 0; t < TPW; ++t) {
+      f4_t sum = acc[t];
+      for (int w = 1; w < nwaves; ++w)
+        sum += reinterpret_cast<const f4_t *>(lds + w * TPW * kRWaveLds)[64 * t + lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 16 * t + 4 * lq + r;
+        if (li < batch && row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(sum[r]);
+      }
     }
   }
 }
 
-template <int NK, int CPW, int SG>
+template <int NK, int CPW, int SG, int TPW>
 __global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
     int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
     uint16_t *__restrict__ y) {
-  extern __shared__ __align__(16) uint8_t lds[];  // [waves][kRWaveLds]
-  rows_body<NK, CPW, SG>(blockIdx.x, rows, units, sg_shift, row_ptr, vals, codes, scales, x, batch, y, lds);
+  extern __shared__ __align__(16) uint8_t lds[];  // [waves][TPW][kRWaveLds]
+  rows_body<NK, CPW, SG, TPW>(blockIdx.x, rows, units, sg_shift, row_ptr, vals, codes, scales, x, batch, y, lds);
 }
 
 // Several layers that share x (and N, G and K) in one launch: each block
-// finds its layer from the cumulative tile counts and runs the single-layer
+// finds its layer from the cumulative block counts and runs the single-layer
 // body on it.
-template <int NK, int CPW, int SG>
+template <int NK, int CPW, int SG, int TPW>
 __global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_multi_kernel(
     int units, const uint16_t *__restrict__ x, int batch, MultiDesc d) {
-  extern __shared__ __align__(16) uint8_t lds[];  // [waves][kRWaveLds]
+  extern __shared__ __align__(16) uint8_t lds[];  // [waves][TPW][kRWaveLds]
   int m = 0;
 #pragma unroll
   for (int i = 1; i < kMaxMulti; ++i) m += (i < d.n && (int)blockIdx.x >= d.block_end[i - 1]) ? 1 : 0;
   const int first = m == 0 ? 0 : d.block_end[m - 1];
-  rows_body<NK, CPW, SG>((int)blockIdx.x - first, d.rows[m], units, d.sg_shift[m], d.row_ptr[m], d.vals[m],
-                         d.codes[m], d.scales[m], x, batch, d.y[m], lds);
+  rows_body<NK, CPW, SG, TPW>((int)blockIdx.x - first, d.rows[m], units, d.sg_shift[m], d.row_ptr[m], d.vals[m],
+                              d.codes[m], d.scales[m], x, batch, d.y[m], lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -974,41 +1018,114 @@ bool rows_kernel_fits(const i4s_packed &w) {
   return chunks <= 2 * kRMaxWaves;
 }
 
+// Shape of a rows-kernel launch: chunks per wave, waves per block, tiles
+// per wave.  Two tiles per wave halve the B-fragment loads per weight byte;
+// one tile per wave keeps twice the blocks for layers with few rows.
+// Measured on MI355X: two tiles win from 320 tiles up (5120 rows: 7.7 / 8.0 /
+// 8.8 us against 7.8 / 9.0 / 12.3 at batch 4 / 8 / 16), one tile wins at 256
+// (4096 rows, 1:4: 5.2 / 5.5 / 6.7 against 6.9 / 7.1 / 7.9).  I4S_ROWS_TPW=1
+// or 2 forces the choice (tuning); read once.
+struct RowsShape {
+  int cpw, waves, tpw;
+  size_t lds;
+};
+
+RowsShape rows_shape(int units, int total_tiles) {
+  static const int forced = [] {
+    const char *e = getenv("I4S_ROWS_TPW");
+    const int v = e ? atoi(e) : 0;
+    return (v == 1 || v == 2) ? v : 0;
+  }();
+  RowsShape r;
+  const int chunks = (units + kRUnits - 1) / kRUnits;
+  r.cpw = chunks > kRMaxWaves ? 2 : 1;
+  r.waves = (chunks + r.cpw - 1) / r.cpw;
+  r.tpw = forced ? forced : (total_tiles >= 300 ? 2 : 1);
+  r.lds = (size_t)r.waves * r.tpw * kRWaveLds;
+  return r;
+}
+
+// Dynamic LDS above 64 KB needs the kernel's limit raised (once per kernel;
+// gfx950 allows 160 KB per workgroup).
+template <typename Tag>
+hipError_t allow_lds(const void *kernel, size_t bytes) {
+  static std::atomic<size_t> granted{64 * 1024};
+  if (bytes <= granted.load(std::memory_order_relaxed)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) granted.store(bytes, std::memory_order_relaxed);
+  return e;
+}
+template <int NK, int C, int G, int T> struct RowsTag {};
+template <int NK, int C, int G, int T> struct RowsMultiTag {};
+
+template <int NK, int C, int G, int T>
+hipError_t launch_rows_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y, const RowsShape &r,
+                         int sg_shift, hipStream_t stream) {
+  const void *k = reinterpret_cast<const void *>(&gemv_smfmac_rows_kernel<NK, C, G, T>);
+  hipError_t e = allow_lds<RowsTag<NK, C, G, T>>(k, r.lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((w.rows + 16 * T - 1) / (16 * T))), block(64 * r.waves);
+  hipLaunchKernelGGL((gemv_smfmac_rows_kernel<NK, C, G, T>), grid, block, r.lds, stream, w.rows, w.cols / kSegCols,
+                     sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, batch, y);
+  return hipGetLastError();
+}
+
+template <int NK, int C, int G, int T>
+hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, const MultiDesc &d, int blocks,
+                               const RowsShape &r, hipStream_t stream) {
+  const void *k = reinterpret_cast<const void *>(&gemv_smfmac_rows_multi_kernel<NK, C, G, T>);
+  hipError_t e = allow_lds<RowsMultiTag<NK, C, G, T>>(k, r.lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemv_smfmac_rows_multi_kernel<NK, C, G, T>), dim3((unsigned)blocks), dim3(64 * r.waves), r.lds,
+                     stream, units, x, batch, d);
+  return hipGetLastError();
+}
+
+// Run F<NK, cpw, SG, tpw>::go(args...) for the shape's run-time values.
+#define I4S_ROWS_DISPATCH(FN, ...)                                                      \
+  do {                                                                                  \
+    const int sgv = sg_shift == 0 ? 1 : (sg_shift == 1 ? 2 : 4);                        \
+    if (r.cpw == 1 && r.tpw == 1) {                                                     \
+      if (sgv == 1) return FN<NK, 1, 1, 1>(__VA_ARGS__);                                \
+      if (sgv == 2) return FN<NK, 1, 2, 1>(__VA_ARGS__);                                \
+      return FN<NK, 1, 4, 1>(__VA_ARGS__);                                              \
+    } else if (r.cpw == 1) {                                                            \
+      if (sgv == 1) return FN<NK, 1, 1, 2>(__VA_ARGS__);                                \
+      if (sgv == 2) return FN<NK, 1, 2, 2>(__VA_ARGS__);                                \
+      return FN<NK, 1, 4, 2>(__VA_ARGS__);                                              \
+    } else if (r.tpw == 1) {                                                            \
+      if (sgv == 1) return FN<NK, 2, 1, 1>(__VA_ARGS__);                                \
+      if (sgv == 2) return FN<NK, 2, 2, 1>(__VA_ARGS__);                                \
+      return FN<NK, 2, 4, 1>(__VA_ARGS__);                                              \
+    } else {                                                                            \
+      if (sgv == 1) return FN<NK, 2, 1, 2>(__VA_ARGS__);                                \
+      if (sgv == 2) return FN<NK, 2, 2, 2>(__VA_ARGS__);                                \
+      return FN<NK, 2, 4, 2>(__VA_ARGS__);                                              \
+    }                                                                                   \
+  } while (0)
+
 template <int NK>
 hipError_t launch_rows(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                        hipStream_t stream) {
-  const int units = w.cols / kSegCols;
-  const int chunks = (units + kRUnits - 1) / kRUnits;
-  const int cpw = chunks > kRMaxWaves ? 2 : 1;
-  const int waves = (chunks + cpw - 1) / cpw;
+  const RowsShape r = rows_shape(w.cols / kSegCols, (w.rows + 15) / 16);
   const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
-  const dim3 grid((unsigned)((w.rows + 15) / 16)), block(64 * waves);
-  const size_t lds = (size_t)waves * kRWaveLds;
-#define I4S_ROWS(C, G) hipLaunchKernelGGL((gemv_smfmac_rows_kernel<NK, C, G>), grid, block, lds, stream, w.rows, \
-                                          units, sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, batch, y)
-  if (cpw == 1) {
-    if (sg_shift == 0) I4S_ROWS(1, 1); else if (sg_shift == 1) I4S_ROWS(1, 2); else I4S_ROWS(1, 4);
-  } else {
-    if (sg_shift == 0) I4S_ROWS(2, 1); else if (sg_shift == 1) I4S_ROWS(2, 2); else I4S_ROWS(2, 4);
-  }
-#undef I4S_ROWS
-  return hipGetLastError();
+  I4S_ROWS_DISPATCH(launch_rows_t, w, x, batch, y, r, sg_shift, stream);
 }
 
 template <int NK>
 hipError_t launch_rows_multi(const i4s_packed *w, int32_t n, const uint16_t *x, int32_t batch,
                              uint16_t *const *y, hipStream_t stream) {
   const int units = w[0].cols / kSegCols;
-  const int chunks = (units + kRUnits - 1) / kRUnits;
-  const int cpw = chunks > kRMaxWaves ? 2 : 1;
-  const int waves = (chunks + cpw - 1) / cpw;
+  int total_tiles = 0;
+  for (int m = 0; m < n; ++m) total_tiles += (w[m].rows + 15) / 16;
+  const RowsShape r = rows_shape(units, total_tiles);
   const int sg_shift = w[0].group_size == 64 ? 0 : (w[0].group_size == 128 ? 1 : 2);
   MultiDesc d = {};
   d.n = n;
-  int tiles = 0;
+  int blocks = 0;
   for (int m = 0; m < n; ++m) {
-    tiles += (w[m].rows + 15) / 16;
-    d.block_end[m] = tiles;
+    blocks += (w[m].rows + 16 * r.tpw - 1) / (16 * r.tpw);
+    d.block_end[m] = blocks;
     d.rows[m] = w[m].rows;
     d.sg_shift[m] = sg_shift;
     d.row_ptr[m] = w[m].row_ptr;
@@ -1017,18 +1134,9 @@ hipError_t launch_rows_multi(const i4s_packed *w, int32_t n, const uint16_t *x, 
     d.scales[m] = w[m].scales;
     d.y[m] = y[m];
   }
-  const dim3 grid((unsigned)tiles), block(64 * waves);
-  const size_t lds = (size_t)waves * kRWaveLds;
-#define I4S_ROWS(C, G) hipLaunchKernelGGL((gemv_smfmac_rows_multi_kernel<NK, C, G>), grid, block, lds, stream, \
-                                          units, x, batch, d)
-  if (cpw == 1) {
-    if (sg_shift == 0) I4S_ROWS(1, 1); else if (sg_shift == 1) I4S_ROWS(1, 2); else I4S_ROWS(1, 4);
-  } else {
-    if (sg_shift == 0) I4S_ROWS(2, 1); else if (sg_shift == 1) I4S_ROWS(2, 2); else I4S_ROWS(2, 4);
-  }
-#undef I4S_ROWS
-  return hipGetLastError();
+  I4S_ROWS_DISPATCH(launch_rows_multi_t, units, x, batch, d, blocks, r, stream);
 }
+#undef I4S_ROWS_DISPATCH
 
 hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                          hipStream_t stream) {
@@ -1128,17 +1236,17 @@ SplitPlan split_plan(const i4s_packed &w, int32_t batch) {
   if (ups > max_ups) ups = max_ups;
   pl.ups = ups;
   pl.ksplit = (units + ups - 1) / ups;
-  // When the split pays (measured on the 13B-shaped layers): the one-tile
-  // kernel reads its B fragments from L2, 32 loads per 16 units per wave at
-  // any batch, while the split kernel shares an LDS copy of x among 16 tiles.
-  // The split wins at batch > 8 and on long rows (K > 8192); below that the
-  // one-tile kernel (no workspace) is faster.  I4S_SPLIT=0 / 1 forces it off
+  // When the split pays: only where the rows kernel does not fit (K > 16384).
+  // Measured on the 13B-shaped layers with two tiles per wave in the rows
+  // kernel, the rows kernel is as fast or faster at every batch (5120x13824
+  // at batch 16: 19.5 us both; everywhere else 5-40 % faster), and it needs
+  // no workspace and no second launch.  I4S_SPLIT=0 / 1 forces the split off
   // or on (tuning and cross-checks).
   static const int split_env = [] {
     const char *e = getenv("I4S_SPLIT");
     return e ? (e[0] == '0' ? 0 : 1) : -1;
   }();
-  const bool wanted = split_env >= 0 ? split_env == 1 : (batch > 8 || units > 128);
+  const bool wanted = split_env >= 0 ? split_env == 1 : units > 2 * kRMaxWaves * kRUnits;
   if (!wanted) return SplitPlan{};
   if (pl.ksplit > 1) pl.partial_bytes = (size_t)pl.ksplit * pl.row_groups * kSWaves * kSTiles * 64 * sizeof(f4_t);
   pl.workspace_bytes = pl.partial_bytes;

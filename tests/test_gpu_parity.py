@@ -292,7 +292,7 @@ def test_config_pack_and_gemv(name, m):
 @pytest.mark.parametrize("rows,cols,n_keep,g", [
     (1, 64, 2, 64), (17, 192, 2, 64), (33, 4160, 2, 64), (100, 8192, 2, 128), (5, 64, 4, 64),
     (19, 320, 4, 64), (21, 4224, 4, 128), (3, 128, 1, 64), (13, 4352, 1, 256), (16, 16384, 2, 256),
-    (700, 16384, 1, 128), (9, 20480, 1, 64), (37, 12288, 1, 64)])
+    (700, 16384, 1, 128), (9, 20480, 1, 64), (37, 12288, 1, 64), (8200, 1024, 1, 64), (8210, 1024, 2, 128)])
 def test_gemv_shapes_and_all_batches(rows, cols, n_keep, g):
     rng = np.random.default_rng(rows + cols)
     w = rand16(rng, (rows, cols))
@@ -336,9 +336,8 @@ def test_batch_rows_match_single_calls(n_keep):
     """Row b of a batch call matches the batch-1 call on x_b (within the
     tolerance: batch 1 and batch >= 2 run different kernels), and a row does
     not depend on the other vectors of its batch: bit-identical across every
-    batch size that runs the same kernel (the no-workspace path for every
-    batch >= 2; the workspace path, which splits K at batch > 8, for batch
-    9..16)."""
+    batch size that runs the same kernel (batch >= 2, with or without a
+    workspace: at this K the workspace path runs the same kernel)."""
     rng = np.random.default_rng(78)
     rows, cols = 64, 2048
     w = rand16(rng, (rows, cols))
@@ -374,6 +373,8 @@ MULTI_CASES = [
     ([(64, 2, 64), (80, 2, 128)], 1024, 1),                       # group sizes differ: per layer
     ([(40, 2, 64)] * 8, 512, 3),                                  # the most layers
     ([(24, 2, 64), (40, 2, 64)], 20480, 1),                       # K > 16384: per layer
+    ([(4100, 2, 64), (4200, 2, 64)], 1024, 6),                    # two tiles per wave, ragged
+    ([(4100, 1, 128), (4200, 1, 128)], 2048, 9),                  # the same for 1:4
 ]
 
 
@@ -447,7 +448,9 @@ def test_row_ptr_is_honoured(n_keep, batch):
 @pytest.mark.parametrize("rows,cols,batch,g", [
     (200, 2048, 3, 64), (5120, 1024, 16, 64), (128, 13824, 16, 64), (777, 4352, 8, 64), (8200, 1024, 4, 64),
     (300, 8192, 8, 64), (8193, 2048, 16, 64), (64, 5120, 4, 128), (48, 2048, 2, 128), (40, 16384, 8, 128),
-    (64, 5120, 4, 256), (33, 13824, 16, 256), (16, 1024, 5, 128)])
+    (64, 5120, 4, 256), (33, 13824, 16, 256), (16, 1024, 5, 128),
+    # K > 16384: the workspace path splits K across blocks
+    (96, 20480, 5, 64), (300, 24576, 16, 128), (40, 32768, 9, 256)])
 def test_batch_paths_with_and_without_workspace(rows, cols, batch, g):
     """i4s_run (no workspace) and i4s_run_ws (K split across blocks where the
     layer's plan uses it) both meet the tolerance for every group size; the
@@ -476,7 +479,7 @@ def test_shared_workspace_across_layers_and_graph_replay():
     entry, also when the calls are replayed from a graph."""
     import int4_sparse_gemv_amd as I
     rng = np.random.default_rng(91)
-    shapes = [(640, 8192), (1536, 1024), (96, 8192), (8320, 512)]
+    shapes = [(640, 20480), (1536, 1024), (96, 24576), (8320, 512)]  # two of them split K
     packs, xs, refs = [], [], []
     for r, c in shapes:
         w = rand16(rng, (r, c))
@@ -487,6 +490,7 @@ def test_shared_workspace_across_layers_and_graph_replay():
         refs.append(O.gemv(O.reconstruct(ref), x16))
     say("case shared-workspace")
     need = max(I.run_workspace_size(p, 16) for p in packs)
+    assert need > 0
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bytes: must not matter
     outs = [torch.empty(16, r, dtype=torch.float16, device="cuda") for r, _ in shapes]
     for _ in range(2):
