@@ -789,59 +789,38 @@ __device__ __forceinline__ void rows_body(
   u32x4_t bq[2][8];
   load_b(bq[0], 0);
   load_b(bq[1], 1);
-  vals_t wv[CPW][TPW][4];
-  codes_t wc[CPW][TPW][4];
-  uint16_t wsc[CPW][TPW][4];
-  auto load_w = [&](int c, const uint32_t (&base)[TPW][4], bool nt) {
+  vals_t wv[TPW][4];  // one chunk; the next chunk reuses them once it is staged
+  codes_t wc[TPW][4];
+  uint16_t wsc[TPW][4];
+  // The weights are fetched at the format's offsets (row * K * N / 4)
+  // without waiting for row_ptr, which is read last and checked after the
+  // pass.  The pass uses these loads on every path, so the compiler cannot
+  // sink them below the check (an earlier arrangement that reloaded into the
+  // same registers when a row had moved let it do exactly that, and the
+  // weight stream then waited for row_ptr).
+  // One chunk's weights at a time (two chunks at once would also exceed the
+  // 63 vector loads a wave can have in flight): the next chunk is loaded
+  // into the same registers as soon as the current one sits in LDS, and
+  // streams in while it is multiplied.
+  auto load_chunk = [&](int c) {
     const int u = min((wave * CPW + c) * kRUnits + li, units - 1);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t e0 = base[t][k] + (uint32_t)u * 16 * NK;
+        const uint32_t e0 = (uint32_t)wrow[t][k] * nnz_row + (uint32_t)u * 16 * NK;
         const uint32_t si = (uint32_t)wrow[t][k] * ngroups + ((uint32_t)u >> sg_shift);
-        if (nt) {
-          wv[c][t][k] = __builtin_nontemporal_load(reinterpret_cast<const vals_t *>(vals + (e0 >> 1)));
-          wc[c][t][k] = __builtin_nontemporal_load(reinterpret_cast<const codes_t *>(codes + (e0 >> 3)));
-          wsc[c][t][k] = __builtin_nontemporal_load(scales + si);
-        } else {
-          wv[c][t][k] = *reinterpret_cast<const vals_t *>(vals + (e0 >> 1));
-          wc[c][t][k] = *reinterpret_cast<const codes_t *>(codes + (e0 >> 3));
-          wsc[c][t][k] = scales[si];
-        }
+        wv[t][k] = __builtin_nontemporal_load(reinterpret_cast<const vals_t *>(vals + (e0 >> 1)));
+        wc[t][k] = __builtin_nontemporal_load(reinterpret_cast<const codes_t *>(codes + (e0 >> 3)));
+        wsc[t][k] = __builtin_nontemporal_load(scales + si);
       }
   };
-  uint32_t base[TPW][4];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) base[t][k] = (uint32_t)wrow[t][k] * nnz_row;  // the format's offsets
-#pragma unroll
-  for (int c = 0; c < CPW; ++c) load_w(c, base, true);
+  load_chunk(0);
   int32_t rp[TPW][4];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int k = 0; k < 4; ++k) rp[t][k] = row_ptr[wrow[t][k]];
-
-  // row_ptr check before the pass: row_ptr is the wave's last load and loads
-  // retire in order, so this waits for little beyond the weights the pass
-  // needs anyway.  A block with a row stored away from the format's offset
-  // fetches its weights again from row_ptr's offsets (every wave of the
-  // block sees the same rows, so each decides alone).
-  bool moved = false;
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) moved |= (uint32_t)rp[t][k] != base[t][k];
-  if (__builtin_amdgcn_ballot_w64(moved) != 0) {
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) base[t][k] = (uint32_t)rp[t][k];
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) load_w(c, base, false);
-  }
 
   // one pass over the wave's chunks; B fragments two blocks ahead
   f4_t acc[TPW];
@@ -851,25 +830,40 @@ __device__ __forceinline__ void rows_body(
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       // chunk c of every tile to the wave's LDS areas, in the load layout.
-      // A unit past the row's end (only the last chunk can hold one; it read
-      // the last unit again) is staged with every nibble 8, i.e. q = 0, so its
-      // matrix steps add exact zeros and the loop below needs no branch.  It
-      // never shares a quantization group with a real unit (K % G == 0).
-      const bool real = (wave * CPW + c) * kRUnits + li < units;
+      // A unit past the row's end (only a row's last chunk can hold one; its
+      // lane read the last unit again) must add nothing: every lane first
+      // writes vals whose nibbles are all 8, i.e. q = 0, and a lane past the
+      // end then sends its loaded vals to the row's padding column (never
+      // read) instead of its own slot.  Its codes and scale stay those of the
+      // last unit (a valid index pattern and a finite scale), and its unit
+      // never shares a quantization group with a real one (K % G == 0).  Only
+      // addresses depend on the lane, so the loads are used on every path and
+      // stay where they were issued; and there is no branch (even a
+      // wave-uniform one here split the body and made the compiler spill).
+      const int vcol = (wave * CPW + c) * kRUnits + li < units ? li : kRStride - 1;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         vals_t *lv = lv_of(t);
         codes_t *lc = lc_of(t);
         uint16_t *lsc = lsc_of(t);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        {
           vals_t zv;
           if constexpr (NK == 2) zv = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
           else zv = u32x2_t{0x88888888u, 0x88888888u};
-          lv[(4 * k + lq) * kRStride + li] = real ? wv[c][t][k] : zv;
-          lc[(4 * k + lq) * kRStride + li] = wc[c][t][k];
-          lsc[li * 16 + 4 * k + lq] = wsc[c][t][k];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) lv[(4 * k + lq) * kRStride + li] = zv;
         }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          lv[(4 * k + lq) * kRStride + vcol] = wv[t][k];
+          lc[(4 * k + lq) * kRStride + li] = wc[t][k];
+          lsc[li * 16 + 4 * k + lq] = wsc[t][k];
+        }
+      }
+      if (c + 1 < CPW) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_chunk(c + 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
@@ -936,6 +930,46 @@ __device__ __forceinline__ void rows_body(
         __builtin_amdgcn_sched_barrier(0);
         if (n + 2 < 4 * CPW) load_b(bx, n + 2);
         __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // row_ptr check (wave-uniform; every wave of the block sees the same
+  // rows).  A row stored away from the format's offset is rare: the wave
+  // then recomputes its share of every tile from row_ptr's offsets with a
+  // plain per-lane loop (lane (vector li, quarter lq) owns rows 4lq..4lq+3 of
+  // each tile, as in the matrix accumulator), within the same tolerance.
+  bool moved = false;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) moved |= (uint32_t)rp[t][k] != (uint32_t)wrow[t][k] * nnz_row;
+  if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+    const uint16_t *xv = x + (int64_t)min(li, batch - 1) * cols;
+    for (int t = 0; t < TPW; ++t) {
+      for (int r = 0; r < 4; ++r) {
+        const int row = min(row0 + 16 * t + 4 * lq + r, rows - 1);
+        const uint32_t rs = (uint32_t)row_ptr[row];
+        float sum = 0.0f;
+        for (int c = 0; c < CPW; ++c) {
+          for (int uu = 0; uu < kRUnits; ++uu) {
+            const int u = (wave * CPW + c) * kRUnits + uu;
+            if (u >= units) break;
+            float g = 0.0f;
+            for (int e = 0; e < 16 * NK; ++e) {
+              const uint32_t el = rs + (uint32_t)u * 16 * NK + (uint32_t)e;
+              const uint32_t word = reinterpret_cast<const uint32_t *>(vals)[el >> 3];
+              const uint32_t k8 = el & 7u;
+              const uint32_t slot = (k8 & 1u) ? 4u + (k8 >> 1) : (k8 >> 1);
+              const int q = (int)((word >> (4 * slot)) & 0xFu) - 8;
+              const uint32_t code = (codes[el >> 3] >> (2 * (el & 7u))) & 3u;
+              const int col = u * kSegCols + 4 * (e / NK) + (int)code;
+              g = fmaf((float)q, fp16_bits_to_float(xv[col]), g);
+            }
+            sum = fmaf(fp16_bits_to_float(scales[(uint32_t)row * ngroups + ((uint32_t)u >> sg_shift)]), g, sum);
+          }
+        }
+        acc[t][r] = sum;
       }
     }
   }
