@@ -698,12 +698,29 @@ __global__ __launch_bounds__(256) void gemv_split_reduce_kernel(
 // no transposes are needed.  The multiply count per unit is that of 2:4;
 // the bytes are half.
 
-constexpr int kRUnits = 16;                  // units per chunk
-constexpr int kRMaxWaves = 8;                // 8 x 7040 bytes of LDS; 2 waves per SIMD
-constexpr int kRStride = kRUnits + 1;        // LDS row stride in elements (bank spread)
-constexpr int kRValsBytes = 16 * kRStride * 16;
-constexpr int kRCodesBytes = 16 * kRStride * 8;
-constexpr int kRWaveLds = kRValsBytes + kRCodesBytes + kRUnits * 16 * 2;  // 7040 bytes
+constexpr int kRUnits = 16;                  // units per chunk (the wide form)
+constexpr int kRMaxWaves = 8;                // waves per block (the wide form)
+
+// Geometry of a chunk of U units (16 or 8) in a wave's LDS area for one
+// tile: vals [16 rows][U + 1] (the extra column spreads the banks and takes
+// the vals of units past a row's end), codes [16 rows][U + 1], scales
+// [U units][16 rows].  One load instruction covers 64 / U rows of U units
+// (4 rows x 256 bytes or 8 rows x 128 bytes of vals).
+template <int U>
+struct RowsGeom {
+  static constexpr int kStride = U + 1;
+  static constexpr int kValsBytes = 16 * kStride * 16;
+  static constexpr int kCodesBytes = 16 * kStride * 8;
+  static constexpr int kTileLds = kValsBytes + kCodesBytes + U * 16 * 2;  // 7040 / 3712 bytes
+  static constexpr int kRowsPerLoad = 64 / U;
+  static constexpr int kLoads = 16 / kRowsPerLoad;  // load instructions per tile and chunk
+  static constexpr int kBlocks = U / 4;             // 4-unit blocks per chunk
+  static constexpr int kMaxWaves = U == 8 ? 16 : 8;
+};
+constexpr int kRStride = kRUnits + 1;        // LDS row stride in elements (the wide form)
+constexpr int kRValsBytes = RowsGeom<16>::kValsBytes;
+constexpr int kRCodesBytes = RowsGeom<16>::kCodesBytes;
+constexpr int kRWaveLds = RowsGeom<16>::kTileLds;  // 7040 bytes
 
 // The matrix-step operands of one 1:4 unit for lane (row, kq): the unit's
 // vals word kq / 2 and code byte kq (groups 4kq..4kq+3).  `sh` is 8 * (kq & 1):
@@ -741,28 +758,31 @@ __device__ inline f4_t smfmac_step_14(uint32_t wd, uint32_t cb, uint32_t sh, con
 // time.
 // `blk` is the block's index within its layer: it covers the TPW 16-row
 // tiles from row 16 * TPW * blk.  lds is the block's dynamic LDS
-// ([waves][TPW][kRWaveLds]).  Each B fragment a wave loads feeds the matrix
+// ([waves][TPW][RowsGeom<U>::kTileLds]).  Each B fragment a wave loads feeds the matrix
 // steps of its TPW tiles (measured on the 13824x5120 layer: the B-fragment
 // loads from L2, not the weight stream, bound the one-tile form; two tiles
 // per wave take 14.8 -> 10.6 us at batch 4 and 23.4 -> 14.6 us at batch 16).
-template <int NK, int CPW, int SG, int TPW>
+template <int NK, int CPW, int SG, int TPW, int U>
 __device__ __forceinline__ void rows_body(
     int blk, int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
     uint16_t *__restrict__ y, uint8_t *lds) {
+  typedef RowsGeom<U> Geo;
+  constexpr int RL = Geo::kRowsPerLoad, NL = Geo::kLoads, NBK = Geo::kBlocks, ST = Geo::kStride;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nwaves = blockDim.x / 64;
-  const int li = lane % 16, lq = lane / 16;
+  const int li = lane % 16, lq = lane / 16;  // the matrix layout
+  const int lu = lane % U, lr = lane / U;     // the load layout: unit lu of row RL * k + lr
   const int row0 = blk * 16 * TPW;
   const uint32_t nnz_row = (uint32_t)units * 16 * NK;
   const uint32_t ngroups = (uint32_t)units >> sg_shift;
   typedef typename std::conditional<NK == 2, u32x4_t, u32x2_t>::type vals_t;    // a unit's vals
   typedef typename std::conditional<NK == 2, u32x2_t, uint32_t>::type codes_t;  // a unit's codes
-  uint8_t *wl = lds + wave * TPW * kRWaveLds;  // the wave's areas, one per tile
-  auto lv_of = [&](int t) { return reinterpret_cast<vals_t *>(wl + t * kRWaveLds); };        // [16 rows][17]
-  auto lc_of = [&](int t) { return reinterpret_cast<codes_t *>(wl + t * kRWaveLds + kRValsBytes); };
-  auto lsc_of = [&](int t) {                                                                  // [16 units][16 rows]
-    return reinterpret_cast<uint16_t *>(wl + t * kRWaveLds + kRValsBytes + kRCodesBytes);
+  uint8_t *wl = lds + wave * TPW * Geo::kTileLds;  // the wave's areas, one per tile
+  auto lv_of = [&](int t) { return reinterpret_cast<vals_t *>(wl + t * Geo::kTileLds); };  // [16 rows][ST]
+  auto lc_of = [&](int t) { return reinterpret_cast<codes_t *>(wl + t * Geo::kTileLds + Geo::kValsBytes); };
+  auto lsc_of = [&](int t) {                                                                // [U units][16 rows]
+    return reinterpret_cast<uint16_t *>(wl + t * Geo::kTileLds + Geo::kValsBytes + Geo::kCodesBytes);
   };
 
   // B fragments: lane (vector li, column quarter lq); vectors past `batch`
@@ -770,7 +790,7 @@ __device__ __forceinline__ void rows_body(
   // n of the wave = units 4n..4n+3 of its chunks, in order.
   const int cols = units * kSegCols;
   const uint16_t *xrow = x + (int64_t)min(li, batch - 1) * cols + 8 * lq;
-  auto unit_of = [&](int n, int s) { return (wave * CPW + n / 4) * kRUnits + 4 * (n % 4) + s; };
+  auto unit_of = [&](int n, int s) { return (wave * CPW + n / NBK) * U + 4 * (n % NBK) + s; };
   auto load_b = [&](u32x4_t (&bx)[8], int n) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -780,18 +800,18 @@ __device__ __forceinline__ void rows_body(
     }
   };
 
-  // every weight load of the wave: lane (unit li, row lq): row 16t + 4k + lq
-  int wrow[TPW][4];
+  // every weight load of the wave: lane (unit lu, row lr): row 16t + RL k + lr
+  int wrow[TPW][NL];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) wrow[t][k] = min(row0 + 16 * t + 4 * k + lq, rows - 1);
+    for (int k = 0; k < NL; ++k) wrow[t][k] = min(row0 + 16 * t + RL * k + lr, rows - 1);
   u32x4_t bq[2][8];
   load_b(bq[0], 0);
   load_b(bq[1], 1);
-  vals_t wv[TPW][4];  // one chunk; the next chunk reuses them once it is staged
-  codes_t wc[TPW][4];
-  uint16_t wsc[TPW][4];
+  vals_t wv[TPW][NL];  // one chunk; the next chunk reuses them once it is staged
+  codes_t wc[TPW][NL];
+  uint16_t wsc[TPW][NL];
   // The weights are fetched at the format's offsets (row * K * N / 4)
   // without waiting for row_ptr, which is read last and checked after the
   // pass.  The pass uses these loads on every path, so the compiler cannot
@@ -803,11 +823,11 @@ __device__ __forceinline__ void rows_body(
   // into the same registers as soon as the current one sits in LDS, and
   // streams in while it is multiplied.
   auto load_chunk = [&](int c) {
-    const int u = min((wave * CPW + c) * kRUnits + li, units - 1);
+    const int u = min((wave * CPW + c) * U + lu, units - 1);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < NL; ++k) {
         const uint32_t e0 = (uint32_t)wrow[t][k] * nnz_row + (uint32_t)u * 16 * NK;
         const uint32_t si = (uint32_t)wrow[t][k] * ngroups + ((uint32_t)u >> sg_shift);
         wv[t][k] = __builtin_nontemporal_load(reinterpret_cast<const vals_t *>(vals + (e0 >> 1)));
@@ -816,11 +836,11 @@ __device__ __forceinline__ void rows_body(
       }
   };
   load_chunk(0);
-  int32_t rp[TPW][4];
+  int32_t rp[TPW][NL];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) rp[t][k] = row_ptr[wrow[t][k]];
+    for (int k = 0; k < NL; ++k) rp[t][k] = row_ptr[wrow[t][k]];
 
   // one pass over the wave's chunks; B fragments two blocks ahead
   f4_t acc[TPW];
@@ -840,7 +860,7 @@ __device__ __forceinline__ void rows_body(
       // addresses depend on the lane, so the loads are used on every path and
       // stay where they were issued; and there is no branch (even a
       // wave-uniform one here split the body and made the compiler spill).
-      const int vcol = (wave * CPW + c) * kRUnits + li < units ? li : kRStride - 1;
+      const int vcol = (wave * CPW + c) * U + lu < units ? lu : ST - 1;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         vals_t *lv = lv_of(t);
@@ -851,13 +871,13 @@ __device__ __forceinline__ void rows_body(
           if constexpr (NK == 2) zv = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
           else zv = u32x2_t{0x88888888u, 0x88888888u};
 #pragma unroll
-          for (int k = 0; k < 4; ++k) lv[(4 * k + lq) * kRStride + li] = zv;
+          for (int k = 0; k < NL; ++k) lv[(RL * k + lr) * ST + lu] = zv;
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          lv[(4 * k + lq) * kRStride + vcol] = wv[t][k];
-          lc[(4 * k + lq) * kRStride + li] = wc[t][k];
-          lsc[li * 16 + 4 * k + lq] = wsc[t][k];
+        for (int k = 0; k < NL; ++k) {
+          lv[(RL * k + lr) * ST + vcol] = wv[t][k];
+          lc[(RL * k + lr) * ST + lu] = wc[t][k];
+          lsc[lu * 16 + RL * k + lr] = wsc[t][k];
         }
       }
       if (c + 1 < CPW) {
@@ -866,8 +886,8 @@ __device__ __forceinline__ void rows_body(
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int n = 4 * c + bb;
+      for (int bb = 0; bb < NBK; ++bb) {
+        const int n = NBK * c + bb;
         u32x4_t (&bx)[8] = bq[n % 2];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
@@ -877,8 +897,8 @@ __device__ __forceinline__ void rows_body(
           uint32_t W0, W1, W2, W3, P = 0, Q = 0;
           if constexpr (NK == 2) {
             // the matrix layout: lane (row li, chunk lq) takes unit 4bb + lq
-            const u32x4_t v = lv[li * kRStride + 4 * bb + lq];
-            const u32x2_t cw = lc[li * kRStride + 4 * bb + lq];
+            const u32x4_t v = lv[li * ST + 4 * bb + lq];
+            const u32x2_t cw = lc[li * ST + 4 * bb + lq];
             W0 = v.x; W1 = v.y; W2 = v.z; W3 = v.w;
             transpose4(W0, W1, W2, W3);
             transpose_codes(cw.x, cw.y, P, Q);
@@ -887,7 +907,7 @@ __device__ __forceinline__ void rows_body(
             // code byte lq, read in place
             const uint32_t *lvw = reinterpret_cast<const uint32_t *>(lv);
             const uint8_t *lcb = reinterpret_cast<const uint8_t *>(lc);
-            const int e = li * kRStride + 4 * bb;
+            const int e = li * ST + 4 * bb;
             W0 = lvw[2 * e + (lq >> 1)]; W1 = lvw[2 * (e + 1) + (lq >> 1)];
             W2 = lvw[2 * (e + 2) + (lq >> 1)]; W3 = lvw[2 * (e + 3) + (lq >> 1)];
             P = (uint32_t)lcb[4 * e + lq] | ((uint32_t)lcb[4 * (e + 1) + lq] << 8) |
@@ -928,7 +948,7 @@ __device__ __forceinline__ void rows_body(
         // the buffer just used takes block n + 2; the scheduling barriers keep
         // the loads here, so only two buffers are ever live
         __builtin_amdgcn_sched_barrier(0);
-        if (n + 2 < 4 * CPW) load_b(bx, n + 2);
+        if (n + 2 < NBK * CPW) load_b(bx, n + 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -943,7 +963,7 @@ __device__ __forceinline__ void rows_body(
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) moved |= (uint32_t)rp[t][k] != (uint32_t)wrow[t][k] * nnz_row;
+    for (int k = 0; k < NL; ++k) moved |= (uint32_t)rp[t][k] != (uint32_t)wrow[t][k] * nnz_row;
   if (__builtin_amdgcn_ballot_w64(moved) != 0) {
     const uint16_t *xv = x + (int64_t)min(li, batch - 1) * cols;
     for (int t = 0; t < TPW; ++t) {
@@ -952,8 +972,8 @@ __device__ __forceinline__ void rows_body(
         const uint32_t rs = (uint32_t)row_ptr[row];
         float sum = 0.0f;
         for (int c = 0; c < CPW; ++c) {
-          for (int uu = 0; uu < kRUnits; ++uu) {
-            const int u = (wave * CPW + c) * kRUnits + uu;
+          for (int uu = 0; uu < U; ++uu) {
+            const int u = (wave * CPW + c) * U + uu;
             if (u >= units) break;
             float g = 0.0f;
             for (int e = 0; e < 16 * NK; ++e) {
@@ -985,7 +1005,7 @@ __device__ __forceinline__ void rows_body(
     for (int t = 0; t < TPW; ++t) {
       f4_t sum = acc[t];
       for (int w = 1; w < nwaves; ++w)
-        sum += reinterpret_cast<const f4_t *>(lds + w * TPW * kRWaveLds)[64 * t + lane];
+        sum += reinterpret_cast<const f4_t *>(lds + w * TPW * Geo::kTileLds)[64 * t + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + 16 * t + 4 * lq + r;
@@ -995,29 +1015,29 @@ __device__ __forceinline__ void rows_body(
   }
 }
 
-template <int NK, int CPW, int SG, int TPW>
-__global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_kernel(
+template <int NK, int CPW, int SG, int TPW, int U>
+__global__ __launch_bounds__(64 * RowsGeom<U>::kMaxWaves) void gemv_smfmac_rows_kernel(
     int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
     uint16_t *__restrict__ y) {
-  extern __shared__ __align__(16) uint8_t lds[];  // [waves][TPW][kRWaveLds]
-  rows_body<NK, CPW, SG, TPW>(blockIdx.x, rows, units, sg_shift, row_ptr, vals, codes, scales, x, batch, y, lds);
+  extern __shared__ __align__(16) uint8_t lds[];  // [waves][TPW][RowsGeom<U>::kTileLds]
+  rows_body<NK, CPW, SG, TPW, U>(blockIdx.x, rows, units, sg_shift, row_ptr, vals, codes, scales, x, batch, y, lds);
 }
 
 // Several layers that share x (and N, G and K) in one launch: each block
 // finds its layer from the cumulative block counts and runs the single-layer
 // body on it.
-template <int NK, int CPW, int SG, int TPW>
-__global__ __launch_bounds__(64 * kRMaxWaves) void gemv_smfmac_rows_multi_kernel(
+template <int NK, int CPW, int SG, int TPW, int U>
+__global__ __launch_bounds__(64 * RowsGeom<U>::kMaxWaves) void gemv_smfmac_rows_multi_kernel(
     int units, const uint16_t *__restrict__ x, int batch, MultiDesc d) {
-  extern __shared__ __align__(16) uint8_t lds[];  // [waves][TPW][kRWaveLds]
+  extern __shared__ __align__(16) uint8_t lds[];  // [waves][TPW][RowsGeom<U>::kTileLds]
   int m = 0;
 #pragma unroll
   for (int i = 1; i < kMaxMulti; ++i) m += (i < d.n && (int)blockIdx.x >= d.block_end[i - 1]) ? 1 : 0;
   const int first = m == 0 ? 0 : d.block_end[m - 1];
-  rows_body<NK, CPW, SG, TPW>((int)blockIdx.x - first, d.rows[m], units, d.sg_shift[m], d.row_ptr[m], d.vals[m],
-                              d.codes[m], d.scales[m], x, batch, d.y[m], lds);
+  rows_body<NK, CPW, SG, TPW, U>((int)blockIdx.x - first, d.rows[m], units, d.sg_shift[m], d.row_ptr[m],
+                                 d.vals[m], d.codes[m], d.scales[m], x, batch, d.y[m], lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1060,22 +1080,38 @@ bool rows_kernel_fits(const i4s_packed &w) {
 // (4096 rows, 1:4: 5.2 / 5.5 / 6.7 against 6.9 / 7.1 / 7.9).  I4S_ROWS_TPW=1
 // or 2 forces the choice (tuning); read once.
 struct RowsShape {
-  int cpw, waves, tpw;
+  int u, cpw, waves, tpw;
   size_t lds;
 };
 
-RowsShape rows_shape(int units, int total_tiles) {
-  static const int forced = [] {
+// Chunk width: 16 units (4 rows x 256 bytes per load) by default; 8 units
+// (8 rows x 128 bytes, twice the waves per block, half the work each) when
+// two-tile blocks are fewer than the compute units and the batch is at most
+// 8.  Measured: 5120x5120 at batch 4 / 8 / 16: 7.45 / 7.76 / 8.90 us with 16,
+// 6.63 / 7.32 / 9.01 with 8; 13824x5120 (432 blocks): 10.8 / 11.5 / 14.4 with
+// 16, 11.6 / 12.9 / 16.5 with 8.  I4S_ROWS_UNITS=8 or 16 forces it (tuning).
+RowsShape rows_shape(int units, int total_tiles, int batch) {
+  static const int forced_tpw = [] {
     const char *e = getenv("I4S_ROWS_TPW");
     const int v = e ? atoi(e) : 0;
     return (v == 1 || v == 2) ? v : 0;
   }();
+  static const int forced_u = [] {
+    const char *e = getenv("I4S_ROWS_UNITS");
+    const int v = e ? atoi(e) : 0;
+    return (v == 8 || v == 16) ? v : 0;
+  }();
   RowsShape r;
-  const int chunks = (units + kRUnits - 1) / kRUnits;
-  r.cpw = chunks > kRMaxWaves ? 2 : 1;
+  r.tpw = forced_tpw ? forced_tpw : (total_tiles >= 300 ? 2 : 1);
+  r.u = forced_u ? forced_u : ((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) ? 8 : 16);
+  // 8-unit chunks only with one chunk per wave (K <= 8192): two chunks per
+  // wave of the 16-wave form would not fit its 128 registers
+  if ((units + 7) / 8 > RowsGeom<8>::kMaxWaves) r.u = 16;
+  const int maxw = r.u == 8 ? RowsGeom<8>::kMaxWaves : RowsGeom<16>::kMaxWaves;
+  const int chunks = (units + r.u - 1) / r.u;
+  r.cpw = chunks > maxw ? 2 : 1;
   r.waves = (chunks + r.cpw - 1) / r.cpw;
-  r.tpw = forced ? forced : (total_tiles >= 300 ? 2 : 1);
-  r.lds = (size_t)r.waves * r.tpw * kRWaveLds;
+  r.lds = (size_t)r.waves * r.tpw * (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);
   return r;
 }
 
@@ -1089,59 +1125,55 @@ hipError_t allow_lds(const void *kernel, size_t bytes) {
   if (e == hipSuccess) granted.store(bytes, std::memory_order_relaxed);
   return e;
 }
-template <int NK, int C, int G, int T> struct RowsTag {};
-template <int NK, int C, int G, int T> struct RowsMultiTag {};
+template <int NK, int C, int G, int T, int U> struct RowsTag {};
+template <int NK, int C, int G, int T, int U> struct RowsMultiTag {};
 
-template <int NK, int C, int G, int T>
+template <int NK, int C, int G, int T, int U>
 hipError_t launch_rows_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y, const RowsShape &r,
                          int sg_shift, hipStream_t stream) {
-  const void *k = reinterpret_cast<const void *>(&gemv_smfmac_rows_kernel<NK, C, G, T>);
-  hipError_t e = allow_lds<RowsTag<NK, C, G, T>>(k, r.lds);
+  const void *k = reinterpret_cast<const void *>(&gemv_smfmac_rows_kernel<NK, C, G, T, U>);
+  hipError_t e = allow_lds<RowsTag<NK, C, G, T, U>>(k, r.lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((w.rows + 16 * T - 1) / (16 * T))), block(64 * r.waves);
-  hipLaunchKernelGGL((gemv_smfmac_rows_kernel<NK, C, G, T>), grid, block, r.lds, stream, w.rows, w.cols / kSegCols,
-                     sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, batch, y);
+  hipLaunchKernelGGL((gemv_smfmac_rows_kernel<NK, C, G, T, U>), grid, block, r.lds, stream, w.rows,
+                     w.cols / kSegCols, sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, batch, y);
   return hipGetLastError();
 }
 
-template <int NK, int C, int G, int T>
+template <int NK, int C, int G, int T, int U>
 hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, const MultiDesc &d, int blocks,
                                const RowsShape &r, hipStream_t stream) {
-  const void *k = reinterpret_cast<const void *>(&gemv_smfmac_rows_multi_kernel<NK, C, G, T>);
-  hipError_t e = allow_lds<RowsMultiTag<NK, C, G, T>>(k, r.lds);
+  const void *k = reinterpret_cast<const void *>(&gemv_smfmac_rows_multi_kernel<NK, C, G, T, U>);
+  hipError_t e = allow_lds<RowsMultiTag<NK, C, G, T, U>>(k, r.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemv_smfmac_rows_multi_kernel<NK, C, G, T>), dim3((unsigned)blocks), dim3(64 * r.waves), r.lds,
-                     stream, units, x, batch, d);
+  hipLaunchKernelGGL((gemv_smfmac_rows_multi_kernel<NK, C, G, T, U>), dim3((unsigned)blocks), dim3(64 * r.waves),
+                     r.lds, stream, units, x, batch, d);
   return hipGetLastError();
 }
 
-// Run F<NK, cpw, SG, tpw>::go(args...) for the shape's run-time values.
-#define I4S_ROWS_DISPATCH(FN, ...)                                                      \
-  do {                                                                                  \
-    const int sgv = sg_shift == 0 ? 1 : (sg_shift == 1 ? 2 : 4);                        \
-    if (r.cpw == 1 && r.tpw == 1) {                                                     \
-      if (sgv == 1) return FN<NK, 1, 1, 1>(__VA_ARGS__);                                \
-      if (sgv == 2) return FN<NK, 1, 2, 1>(__VA_ARGS__);                                \
-      return FN<NK, 1, 4, 1>(__VA_ARGS__);                                              \
-    } else if (r.cpw == 1) {                                                            \
-      if (sgv == 1) return FN<NK, 1, 1, 2>(__VA_ARGS__);                                \
-      if (sgv == 2) return FN<NK, 1, 2, 2>(__VA_ARGS__);                                \
-      return FN<NK, 1, 4, 2>(__VA_ARGS__);                                              \
-    } else if (r.tpw == 1) {                                                            \
-      if (sgv == 1) return FN<NK, 2, 1, 1>(__VA_ARGS__);                                \
-      if (sgv == 2) return FN<NK, 2, 2, 1>(__VA_ARGS__);                                \
-      return FN<NK, 2, 4, 1>(__VA_ARGS__);                                              \
-    } else {                                                                            \
-      if (sgv == 1) return FN<NK, 2, 1, 2>(__VA_ARGS__);                                \
-      if (sgv == 2) return FN<NK, 2, 2, 2>(__VA_ARGS__);                                \
-      return FN<NK, 2, 4, 2>(__VA_ARGS__);                                              \
-    }                                                                                   \
+// Call FN<NK, cpw, SG, tpw, U>(args...) for the shape's run-time values.
+#define I4S_ROWS_SG(FN, C, T, U, ...)                                                    \
+  do {                                                                                   \
+    if (sg_shift == 0) return FN<NK, C, 1, T, U>(__VA_ARGS__);                           \
+    if (sg_shift == 1) return FN<NK, C, 2, T, U>(__VA_ARGS__);                           \
+    return FN<NK, C, 4, T, U>(__VA_ARGS__);                                              \
+  } while (0)
+#define I4S_ROWS_DISPATCH(FN, ...)                                                       \
+  do {                                                                                   \
+    if (r.u == 16) {                                                                     \
+      if (r.cpw == 1 && r.tpw == 1) I4S_ROWS_SG(FN, 1, 1, 16, __VA_ARGS__);             \
+      if (r.cpw == 1) I4S_ROWS_SG(FN, 1, 2, 16, __VA_ARGS__);                           \
+      if (r.tpw == 1) I4S_ROWS_SG(FN, 2, 1, 16, __VA_ARGS__);                           \
+      I4S_ROWS_SG(FN, 2, 2, 16, __VA_ARGS__);                                           \
+    }                                                                                    \
+    if (r.tpw == 1) I4S_ROWS_SG(FN, 1, 1, 8, __VA_ARGS__);                              \
+    I4S_ROWS_SG(FN, 1, 2, 8, __VA_ARGS__);                                              \
   } while (0)
 
 template <int NK>
 hipError_t launch_rows(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                        hipStream_t stream) {
-  const RowsShape r = rows_shape(w.cols / kSegCols, (w.rows + 15) / 16);
+  const RowsShape r = rows_shape(w.cols / kSegCols, (w.rows + 15) / 16, batch);
   const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
   I4S_ROWS_DISPATCH(launch_rows_t, w, x, batch, y, r, sg_shift, stream);
 }
@@ -1152,7 +1184,7 @@ hipError_t launch_rows_multi(const i4s_packed *w, int32_t n, const uint16_t *x, 
   const int units = w[0].cols / kSegCols;
   int total_tiles = 0;
   for (int m = 0; m < n; ++m) total_tiles += (w[m].rows + 15) / 16;
-  const RowsShape r = rows_shape(units, total_tiles);
+  const RowsShape r = rows_shape(units, total_tiles, batch);
   const int sg_shift = w[0].group_size == 64 ? 0 : (w[0].group_size == 128 ? 1 : 2);
   MultiDesc d = {};
   d.n = n;
@@ -1171,6 +1203,7 @@ hipError_t launch_rows_multi(const i4s_packed *w, int32_t n, const uint16_t *x, 
   I4S_ROWS_DISPATCH(launch_rows_multi_t, units, x, batch, d, blocks, r, stream);
 }
 #undef I4S_ROWS_DISPATCH
+#undef I4S_ROWS_SG
 
 hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                          hipStream_t stream) {

@@ -449,6 +449,8 @@ def test_row_ptr_is_honoured(n_keep, batch):
     (200, 2048, 3, 64), (5120, 1024, 16, 64), (128, 13824, 16, 64), (777, 4352, 8, 64), (8200, 1024, 4, 64),
     (300, 8192, 8, 64), (8193, 2048, 16, 64), (64, 5120, 4, 128), (48, 2048, 2, 128), (40, 16384, 8, 128),
     (64, 5120, 4, 256), (33, 13824, 16, 256), (16, 1024, 5, 128),
+    # two-tile blocks fewer than the compute units at batch <= 8: 8-unit chunks
+    (6000, 2048, 6, 128), (5000, 3072, 3, 64),
     # K > 16384: the workspace path splits K across blocks
     (96, 20480, 5, 64), (300, 24576, 16, 128), (40, 32768, 9, 256)])
 def test_batch_paths_with_and_without_workspace(rows, cols, batch, g):
