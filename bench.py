@@ -58,6 +58,7 @@ def parse():
     ap.add_argument("--suite", default=None, help="also measure every workload and write a table here")
     ap.add_argument("--no-stack", action="store_true", help="with --suite: skip the 224-matrix 7B stack")
     ap.add_argument("--only", default=None, help="with --suite: comma-separated workloads to measure")
+    ap.add_argument("--suite-steps", type=int, default=1000, help="with --suite: timed calls per layer and trial")
     ap.add_argument("--no-floors", action="store_true",
                     help="skip the read-only and latency floor measurements")
     return ap.parse_args()
@@ -458,7 +459,7 @@ def run_suite(R, args):
             mats = [m for m in mats if m.name.startswith(("L0.", "L4."))]
         for m in mats:
             for b in wl.batches:
-                r = R.measure_layer(m, b, 1000, 100, 3)
+                r = R.measure_layer(m, b, args.suite_steps, max(1, args.suite_steps // 10), 3)
                 r["workload"] = name
                 print(f"suite {name}/{m.name} b{b}: cold {r['cold_us']:.2f} us ({r['cold_gbs']:.0f} GB/s), "
                       f"hot {r['hot_us']:.2f} us", file=sys.stderr, flush=True)
