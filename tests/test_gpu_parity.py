@@ -518,3 +518,96 @@ def test_shared_workspace_across_layers_and_graph_replay():
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert torch.equal(o, e)
+
+
+def _decode_layer(I, packs, xs, outs):
+    """One decoder layer's calls: q/k/v fused, o, gate/up fused, down."""
+    q, k, v, o, g, u, d = packs
+    I.run_multi([q, k, v], xs[0], outs=outs[0:3])
+    I.run(o, xs[1], out=outs[3], use_workspace=False)
+    I.run_multi([g, u], xs[2], outs=outs[4:6])
+    I.run(d, xs[3], out=outs[6], use_workspace=False)
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_decode_layer_graph_replay(batch):
+    """A layer's sequence of calls captured in a HIP graph replays to the
+    eager result, bit for bit, with eager work between the replays."""
+    import int4_sparse_gemv_amd as I
+    rng = np.random.default_rng(300 + batch)
+    shapes = [(512, 1024, 2)] * 4 + [(1536, 1024, 2), (1536, 1024, 2), (1024, 1536, 1)]  # q k v o gate up down
+    packs, refs = [], []
+    for r, c, nk in shapes:
+        w = rand16(rng, (r, c))
+        ref = O.pack(w, nk, 64)
+        packs.append(gpu_pack(w, nk, 64))
+        refs.append(ref)
+    x16 = [rng.standard_normal((batch, c)).astype(np.float16) for c in (1024, 1024, 1024, 1536)]
+    xs = [torch.from_numpy(a.view(np.int16)).cuda().view(torch.float16) for a in x16]
+    outs = [torch.empty(batch, r, dtype=torch.float16, device="cuda") for r, _, _ in shapes]
+    say(f"case decode-layer-graph b{batch}")
+    _decode_layer(I, packs, xs, outs)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    xin = [x16[0]] * 3 + [x16[1]] + [x16[2]] * 2 + [x16[3]]
+    for m, (e, ref) in enumerate(zip(eager, refs)):
+        y_ref, a_ref = O.gemv(O.reconstruct(ref), xin[m])
+        assert_gemv_close(e.cpu().numpy().astype(np.float64), y_ref, a_ref, f"layer call {m}")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            _decode_layer(I, packs, xs, outs)
+    for _ in range(3):
+        for o in outs:
+            o.fill_(7)
+        _decode_layer(I, packs, xs, [torch.empty_like(o) for o in outs])  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e)
+
+
+_FIRST_LAUNCH_IN_CAPTURE = r"""
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+import int4_sparse_gemv_amd as I
+rng = np.random.default_rng(5)
+# 5120 x 5120 at batch 4: the two-tile, 8-unit batch kernel with 10 waves,
+# whose 74 KB of LDS needs the per-kernel limit raised; its first launch is
+# the captured one
+w = torch.from_numpy((0.02 * rng.standard_normal((5120, 5120))).astype(np.float16).view(np.int16)).cuda().view(torch.float16)
+p = I.pack(w, 2, 64)
+x = torch.from_numpy(rng.standard_normal((4, 5120)).astype(np.float16).view(np.int16)).cuda().view(torch.float16)
+out = torch.empty(4, 5120, dtype=torch.float16, device="cuda")
+d = p.descriptor()
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+side = torch.cuda.Stream()
+with torch.cuda.stream(side):
+    with torch.cuda.graph(g, stream=side):
+        I.run(p, x, out=out, descriptor=d, use_workspace=False)
+out.zero_()
+g.replay()
+torch.cuda.synchronize()
+ref = I.run(p, x, use_workspace=False)
+torch.cuda.synchronize()
+assert torch.equal(out, ref), "captured first launch differs from the eager call"
+print("ok", flush=True)
+"""
+
+
+def test_first_launch_of_a_kernel_inside_graph_capture():
+    """The first launch of a batch kernel that needs more than 64 KB of LDS
+    may happen inside a graph capture (a fresh process makes it the first)."""
+    import os
+    import subprocess
+    say("case first-launch-in-capture (subprocess)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_LAUNCH_IN_CAPTURE, root], capture_output=True, text=True,
+                       timeout=110)
+    assert r.returncode == 0 and "ok" in r.stdout, (r.returncode, r.stdout[-2000:], r.stderr[-2000:])
