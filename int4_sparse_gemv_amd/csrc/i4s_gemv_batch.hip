@@ -1107,22 +1107,35 @@ RowsShape rows_shape(int units, int total_tiles, int batch) {
   // 8-unit chunks only with one chunk per wave (K <= 8192): two chunks per
   // wave of the 16-wave form would not fit its 128 registers
   if ((units + 7) / 8 > RowsGeom<8>::kMaxWaves) r.u = 16;
+  static const int forced_cpw = [] {
+    const char *e = getenv("I4S_ROWS_CPW");
+    const int v = e ? atoi(e) : 0;
+    return (v == 1 || v == 2) ? v : 0;
+  }();
+  if (forced_cpw == 2) r.u = 16;  // the 8-unit form has one chunk per wave
   const int maxw = r.u == 8 ? RowsGeom<8>::kMaxWaves : RowsGeom<16>::kMaxWaves;
   const int chunks = (units + r.u - 1) / r.u;
-  r.cpw = chunks > maxw ? 2 : 1;
+  r.cpw = chunks > maxw ? 2 : (forced_cpw ? forced_cpw : 1);
   r.waves = (chunks + r.cpw - 1) / r.cpw;
   r.lds = (size_t)r.waves * r.tpw * (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);
   return r;
 }
 
-// Dynamic LDS above 64 KB needs the kernel's limit raised (once per kernel;
-// gfx950 allows 160 KB per workgroup).
+// Dynamic LDS above 64 KB needs the kernel's limit raised (once per kernel
+// and device; gfx950 allows 160 KB per workgroup).  Setting it again is
+// harmless, so concurrent first calls need no lock.
+constexpr int kMaxDevices = 64;
 template <typename Tag>
 hipError_t allow_lds(const void *kernel, size_t bytes) {
-  static std::atomic<size_t> granted{64 * 1024};
-  if (bytes <= granted.load(std::memory_order_relaxed)) return hipSuccess;
-  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) granted.store(bytes, std::memory_order_relaxed);
+  if (bytes <= 64 * 1024) return hipSuccess;
+  static std::atomic<size_t> granted[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::atomic<size_t> *g = (dev >= 0 && dev < kMaxDevices) ? &granted[dev] : nullptr;
+  if (g && bytes <= g->load(std::memory_order_relaxed)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && g) g->store(bytes, std::memory_order_relaxed);
   return e;
 }
 template <int NK, int C, int G, int T, int U> struct RowsTag {};
