@@ -41,8 +41,10 @@ __device__ inline float unit_dot_b1(const UnitRegs<NK> &u, const uint32_t (&xr)[
   if constexpr (NK == 2) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {  // code dword c: groups 8c..8c+7
-      const uint32_t me = (u.c[c] << 2) & 0x3C3C3C3Cu;  // byte k: 4 * code nibble of group 8c+2k
-      const uint32_t mo = (u.c[c] >> 2) & 0x3C3C3C3Cu;  // byte k: 4 * code nibble of group 8c+2k+1
+      uint32_t me = (u.c[c] << 2) & 0x3C3C3C3Cu;  // byte k: 4 * code nibble of group 8c+2k
+      uint32_t mo = (u.c[c] >> 2) & 0x3C3C3C3Cu;  // byte k: 4 * code nibble of group 8c+2k+1
+      opaque(me);
+      opaque(mo);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {  // vals word j = 2c + half: groups 8c+4half .. +3
         h2_t q[4];
@@ -86,6 +88,16 @@ __device__ inline float unit_dot_b1(const UnitRegs<NK> &u, const uint32_t (&xr)[
     }
   }
   return g;
+}
+
+// The 64 activations of unit u from the block's LDS copy (eight 16-byte reads).
+__device__ inline void lds_unit_x(const uint16_t *xs, int u, uint32_t (&xr)[32]) {
+  const uint4 *xv = reinterpret_cast<const uint4 *>(xs + u * kStrideB1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 t = xv[i];
+    xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
+  }
 }
 
 template <int NK, int RPW, int WAVES>
@@ -230,17 +242,18 @@ __device__ __forceinline__ void b1_direct_body(
   const uint32_t nnz_row = (uint32_t)units * 16 * NK;
   const uint32_t ngroups = (uint32_t)units >> sg_shift;
 
-  // 1. activations (nvec <= 64 * WAVES * UPL, so UPL pieces per thread cover
-  // them).  Every load below is unconditional, at a clamped index, so the
-  // wait before the LDS write counts exactly the loads issued after it.
-  uint4 xg[UPL];
-  int xi[UPL];
+  // 1. activations (nvec <= 512 * UPL, so XP pieces per thread cover them).
+  // Every load below is unconditional, at a clamped index, so the wait before
+  // the LDS write counts exactly the loads issued after it.
+  constexpr int XP = (8 * UPL + WAVES - 1) / WAVES;
+  u32x4_t xg[XP];  // a vector type: a plain load, not an aggregate copy the optimizer may re-place
+  int xi[XP];
 #pragma unroll
-  for (int j = 0; j < UPL; ++j) {
+  for (int j = 0; j < XP; ++j) {
     xi[j] = min((int)threadIdx.x + j * 64 * WAVES, nvec - 1);
-    xg[j] = reinterpret_cast<const uint4 *>(x)[xi[j]];
+    xg[j] = reinterpret_cast<const u32x4_t *>(x)[xi[j]];
   }
-  __builtin_amdgcn_sched_barrier(0);
+  issue_fence();
 
   // 2. weights: rows past the end re-read the last row (never stored)
   uint32_t rstart[RPW], srow[RPW];
@@ -252,6 +265,8 @@ __device__ __forceinline__ void b1_direct_body(
     rstart[r] = (uint32_t)rr * nnz_row;
     srow[r] = (uint32_t)rr * ngroups;
   }
+  // In the order the decode consumes them: unit by unit, the rows of a unit
+  // together.
   UnitRegs<NK> wr[UPL][RPW];
 #pragma unroll
   for (int k = 0; k < UPL; ++k) {
@@ -260,6 +275,7 @@ __device__ __forceinline__ void b1_direct_body(
     for (int r = 0; r < RPW; ++r)
       load_unit_nt<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
                        srow[r] + ((uint32_t)u >> sg_shift));
+    issue_fence();
   }
   // row_ptr: a vector load, issued last and needed only after decoding.  (A
   // scalar load would share its counter with LDS and, returning out of
@@ -272,50 +288,59 @@ __device__ __forceinline__ void b1_direct_body(
   // 3. stage x in LDS (threads with a clamped index write the same piece
   // to the same place again)
 #pragma unroll
-  for (int j = 0; j < UPL; ++j)
-    *reinterpret_cast<uint4 *>(xs + (xi[j] >> 3) * kStrideB1 + 8 * (xi[j] & 7)) = xg[j];
+  for (int j = 0; j < XP; ++j)
+    *reinterpret_cast<u32x4_t *>(xs + (xi[j] >> 3) * kStrideB1 + 8 * (xi[j] & 7)) = xg[j];
   init_tables<NK>(lut);
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
-  // 4. decode and accumulate.  The row_ptr check comes after the first pass,
-  // so the common case never waits for row_ptr before decoding; a row stored
-  // away from the format's offset (wave-uniform) is re-fetched and decoded
-  // again.
+  // 4. decode and accumulate.  The activations of the lane's first unit are
+  // read from LDS before the first wait for weights, so those reads overlap
+  // the stream; each unit's activations then feed all RPW rows.
+  uint32_t xr0[32];
+  lds_unit_x(xs, min(lane, units - 1), xr0);
+  __builtin_amdgcn_sched_barrier(0);
   float acc[RPW];
-  for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
 #pragma unroll
-    for (int k = 0; k < UPL; ++k) {
-      const int u = lane + 64 * k;
-      if (u < units) {
-        uint32_t xr[32];
-        const uint4 *xv = reinterpret_cast<const uint4 *>(xs + u * kStrideB1);
+  for (int k = 0; k < UPL; ++k) {
+    const int u = lane + 64 * k;
+    if (u < units) {
+      uint32_t xr[32];
+      if (k == 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint4 t = xv[i];
-          xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
-        }
+        for (int i = 0; i < 32; ++i) xr[i] = xr0[i];
+      } else {
+        lds_unit_x(xs, u, xr);
+      }
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          const float gsum = unit_dot_b1<NK>(wr[k][r], xr, lut);
-          acc[r] = fmaf(fp16_bits_to_float(wr[k][r].s), gsum, acc[r]);
-        }
+      for (int r = 0; r < RPW; ++r) {
+        const float gsum = unit_dot_b1<NK>(wr[k][r], xr, lut);
+        acc[r] = fmaf(fp16_bits_to_float(wr[k][r].s), gsum, acc[r]);
       }
     }
-    bool moved = false;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The row_ptr check comes after the decode, so the common case never waits
+  // for row_ptr; a row stored away from the format's offset (wave-uniform) is
+  // fetched from row_ptr's offset into registers of its own and decoded again.
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) moved |= (uint32_t)rp[r] != rstart[r];
-    if (pass == 1 || !moved) break;
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      rstart[r] = (uint32_t)rp[r];
+  for (int r = 0; r < RPW; ++r) {
+    if ((uint32_t)rp[r] != rstart[r]) {
+      acc[r] = 0.0f;
 #pragma unroll
       for (int k = 0; k < UPL; ++k) {
         const int u = min(lane + 64 * k, units - 1);
-        load_unit<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+        UnitRegs<NK> t;
+        load_unit<NK>(t, vals, codes, scales, (uint32_t)rp[r] + (uint32_t)u * 16 * NK,
                       srow[r] + ((uint32_t)u >> sg_shift));
+        if (lane + 64 * k < units) {
+          uint32_t xr[32];
+          lds_unit_x(xs, u, xr);
+          acc[r] = fmaf(fp16_bits_to_float(t.s), unit_dot_b1<NK>(t, xr, lut), acc[r]);
+        }
       }
     }
   }

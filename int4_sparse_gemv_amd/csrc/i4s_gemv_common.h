@@ -77,6 +77,21 @@ __host__ __device__ constexpr uint32_t single_selector_hi(uint32_t c) {
   return 0x00000C0Cu | ((2 * c) << 16) | ((2 * c + 1) << 24);
 }
 
+// Hides a value's origin from the optimizer.  Selector-table offsets are
+// built once per code dword as four byte lanes and then taken out one byte at
+// a time (one v_bfe_u32 each); without this the compiler folds the masks back
+// into every extraction and spends a shift and an AND per group.
+__device__ inline void opaque(uint32_t &v) { asm("" : "+v"(v)); }
+
+// Keeps the loads issued before it ahead of those issued after it: the empty
+// asm with a memory clobber stops the IR passes from sinking loads towards
+// their first use, and the scheduling barrier does the same for the machine
+// scheduler.  (No wait is implied: nothing reads the loaded registers.)
+__device__ inline void issue_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ inline float fp16_bits_to_float(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
