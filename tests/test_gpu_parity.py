@@ -422,14 +422,17 @@ def test_run_on_side_stream():
     assert_gemv_close(y.cpu().numpy().astype(np.float64), y_ref, a_ref, "side-stream")
 
 
-@pytest.mark.parametrize("n_keep,batch", [(2, 1), (4, 1), (2, 3), (1, 1), (4, 8), (1, 6)])
-def test_row_ptr_is_honoured(n_keep, batch):
+@pytest.mark.parametrize("n_keep,batch,rows,cols", [
+    (2, 1, 37, 5120), (4, 1, 37, 5120), (2, 3, 37, 5120), (1, 1, 37, 5120), (4, 8, 37, 5120), (1, 6, 37, 5120),
+    # more than 8192 rows: two rows per wave at batch 1
+    (2, 1, 8200, 1024), (1, 1, 8200, 1024), (4, 1, 8200, 2048)])
+def test_row_ptr_is_honoured(n_keep, batch, rows, cols):
     """Rows stored in reverse order, described only by row_ptr, give the same y."""
     import int4_sparse_gemv_amd as I
     rng = np.random.default_rng(80 + n_keep)
-    rows, cols, g = 37, 4096 + 1024, 128
+    g = 128
     w = rand16(rng, (rows, cols))
-    say(f"case row-ptr-reversed n={n_keep} b={batch}")
+    say(f"case row-ptr-reversed n={n_keep} b={batch} {rows}x{cols}")
     p = gpu_pack(w, n_keep, g)
     x16 = rng.standard_normal((batch, cols)).astype(np.float16)
     y0 = gpu_run(p, x16)
