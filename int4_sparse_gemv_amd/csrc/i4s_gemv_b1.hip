@@ -303,10 +303,25 @@ __device__ __forceinline__ void b1_direct_body(
   float acc[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
+  // One row per wave: lanes past the row's end compute on its last unit and
+  // discard the result (a select, not a branch: behind a branch the compiler
+  // moved the dense weight loads down into the decode block, after the
+  // barrier).  Two or more rows keep the branch: without it their register
+  // count rose from ~75 to ~120, too many for three blocks per CU.
 #pragma unroll
   for (int k = 0; k < UPL; ++k) {
     const int u = lane + 64 * k;
-    if (u < units) {
+    if constexpr (RPW == 1) {
+      uint32_t xr[32];
+      if (k == 0) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) xr[i] = xr0[i];
+      } else {
+        lds_unit_x(xs, min(u, units - 1), xr);
+      }
+      const float a = fmaf(fp16_bits_to_float(wr[k][0].s), unit_dot_b1<NK>(wr[k][0], xr, lut), acc[0]);
+      acc[0] = u < units ? a : acc[0];
+    } else if (u < units) {
       uint32_t xr[32];
       if (k == 0) {
 #pragma unroll
