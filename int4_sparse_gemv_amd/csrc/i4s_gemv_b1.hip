@@ -92,7 +92,7 @@ __device__ inline float unit_dot_b1(const UnitRegs<NK> &u, const uint32_t (&xr)[
 
 // The 64 activations of unit u from the block's LDS copy (eight 16-byte reads).
 __device__ inline void lds_unit_x(const uint16_t *xs, int u, uint32_t (&xr)[32]) {
-  const uint4 *xv = reinterpret_cast<const uint4 *>(xs + u * kStrideB1);
+  const uint4 *xv = reinterpret_cast<const uint4 *>(xs + __umul24((uint32_t)u, kStrideB1));
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint4 t = xv[i];
@@ -236,7 +236,9 @@ __device__ __forceinline__ void b1_direct_body(
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
     uint16_t *__restrict__ y, uint16_t *xs, uint32_t *lut) {
   const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
+  // The wave index is uniform: row offsets are then scalar arithmetic, and
+  // the weight loads take a scalar base plus a 32-bit per-lane offset.
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
   const int row0 = (blk * WAVES + wave) * RPW;
   const int nvec = units * (kSegCols / 8);  // uint4 pieces of x
   const uint32_t nnz_row = (uint32_t)units * 16 * NK;
@@ -247,11 +249,11 @@ __device__ __forceinline__ void b1_direct_body(
   // the LDS write counts exactly the loads issued after it.
   constexpr int XP = (8 * UPL + WAVES - 1) / WAVES;
   u32x4_t xg[XP];  // a vector type: a plain load, not an aggregate copy the optimizer may re-place
-  int xi[XP];
+  uint32_t xi[XP];
 #pragma unroll
   for (int j = 0; j < XP; ++j) {
-    xi[j] = min((int)threadIdx.x + j * 64 * WAVES, nvec - 1);
-    xg[j] = reinterpret_cast<const u32x4_t *>(x)[xi[j]];
+    xi[j] = (uint32_t)min((int)threadIdx.x + j * 64 * WAVES, nvec - 1);
+    xg[j] = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const char *>(x) + 16u * xi[j]);
   }
   issue_fence();
 
@@ -280,16 +282,19 @@ __device__ __forceinline__ void b1_direct_body(
   // row_ptr: a vector load, issued last and needed only after decoding.  (A
   // scalar load would share its counter with LDS and, returning out of
   // order, hold up the block barrier and the first LDS reads.)
+  // (The index is formed from the per-lane wave number so that it stays a
+  // vector load.)
+  const int row0_v = (blk * WAVES + (int)threadIdx.x / 64) * RPW;
   int32_t rp[RPW];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) rp[r] = row_ptr[min(row0 + r, rows - 1)];
+  for (int r = 0; r < RPW; ++r) rp[r] = row_ptr[min(row0_v + r, rows - 1)];
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. stage x in LDS (threads with a clamped index write the same piece
   // to the same place again)
 #pragma unroll
   for (int j = 0; j < XP; ++j)
-    *reinterpret_cast<u32x4_t *>(xs + (xi[j] >> 3) * kStrideB1 + 8 * (xi[j] & 7)) = xg[j];
+    *reinterpret_cast<u32x4_t *>(xs + __umul24(xi[j] >> 3, kStrideB1) + 8 * (xi[j] & 7)) = xg[j];
   init_tables<NK>(lut);
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -321,19 +326,25 @@ __device__ __forceinline__ void b1_direct_body(
       }
       const float a = fmaf(fp16_bits_to_float(wr[k][0].s), unit_dot_b1<NK>(wr[k][0], xr, lut), acc[0]);
       acc[0] = u < units ? a : acc[0];
-    } else if (u < units) {
-      uint32_t xr[32];
-      if (k == 0) {
+    } else {
+      auto decode = [&]() {
+        uint32_t xr[32];
+        if (k == 0) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) xr[i] = xr0[i];
-      } else {
-        lds_unit_x(xs, u, xr);
-      }
+          for (int i = 0; i < 32; ++i) xr[i] = xr0[i];
+        } else {
+          lds_unit_x(xs, u, xr);
+        }
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const float gsum = unit_dot_b1<NK>(wr[k][r], xr, lut);
-        acc[r] = fmaf(fp16_bits_to_float(wr[k][r].s), gsum, acc[r]);
-      }
+        for (int r = 0; r < RPW; ++r) {
+          const float gsum = unit_dot_b1<NK>(wr[k][r], xr, lut);
+          acc[r] = fmaf(fp16_bits_to_float(wr[k][r].s), gsum, acc[r]);
+        }
+      };
+      // a wave-uniform test first: the loads then have uses in two blocks
+      // and stay where they were issued
+      if (64 * (k + 1) <= units) decode();
+      else if (u < units) decode();
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -369,15 +380,18 @@ __device__ __forceinline__ void b1_direct_body(
 }
 
 template <int NK, int RPW, int UPL, int WAVES>
+// shape = units | sg_shift << 16: with the two sizes in one dword the
+// arguments fit the 14 preloaded SGPRs, y included, so no wave loads an
+// argument from memory (the store of y used to wait for one).
 __global__ __launch_bounds__(64 * WAVES) void gemv_b1_direct_kernel(
-    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
+    int rows, int shape, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
     uint16_t *__restrict__ y) {
   extern __shared__ __align__(16) uint16_t xs[];  // [units][kStrideB1]
   __shared__ __align__(8) uint32_t lut[32];
-  b1_direct_body<NK, RPW, UPL, WAVES>(blockIdx.x, rows, units, sg_shift, row_ptr, vals, codes, scales, x, y,
-                                      xs, lut);
+  b1_direct_body<NK, RPW, UPL, WAVES>(blockIdx.x, rows, shape & 0xFFFF, shape >> 16, row_ptr, vals, codes, scales,
+                                      x, y, xs, lut);
 }
 
 // Several layers that share x in one launch (horizontal fusion): each block
@@ -410,7 +424,7 @@ hipError_t launch_b1_direct(const i4s_packed &w, const uint16_t *x, uint16_t *y,
   const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kB1Waves);
   const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
   hipLaunchKernelGGL((gemv_b1_direct_kernel<NK, RPW, UPL, kB1Waves>), grid, block, lds, stream, w.rows,
-                     units, sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, y);
+                     units | (sg_shift << 16), w.row_ptr, w.vals, w.codes, w.scales, x, y);
   return hipGetLastError();
 }
 

@@ -154,7 +154,7 @@ __device__ inline void load_unit(UnitRegs<NK> &r, const uint8_t *__restrict__ va
     const uint2 c = *reinterpret_cast<const uint2 *>(codes + (elem0 >> 3));
     r.c[0] = c.x; r.c[1] = c.y;
   }
-  r.s = scales[scale_idx];
+  r.s = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(scales) + 2u * scale_idx);
 }
 
 // Fill the 16-entry selector table (2:4 only); call with threadIdx.x < 16.
@@ -225,7 +225,8 @@ __device__ inline void load_unit_nt(UnitRegs<NK> &r, const uint8_t *__restrict__
     const u32x2_t c = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(codes + (elem0 >> 3)));
     r.c[0] = c.x; r.c[1] = c.y;
   }
-  r.s = __builtin_nontemporal_load(scales + scale_idx);
+  r.s = __builtin_nontemporal_load(
+      reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(scales) + 2u * scale_idx));
 }
 
 }  // namespace
