@@ -1281,6 +1281,10 @@ bool smfmac_enabled() {
 template <int NK>
 hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                      hipStream_t stream) {
+  if (batch == 2) {
+    const hipError_t e = launch_gemv_bv(w, x, batch, y, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (NK == 2 && batch >= 2 && smfmac_enabled()) {
     return launch_smfmac(w, x, batch, y, stream);
   }

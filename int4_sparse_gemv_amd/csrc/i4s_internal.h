@@ -66,6 +66,11 @@ struct MultiDesc {
 // GEMV kernels.  launch_gemv (i4s_gemv_batch.hip) dispatches every call;
 // launch_gemv_b1 (i4s_gemv_b1.hip) runs batch 1 for n_keep 2 and 4.
 hipError_t launch_gemv_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream);
+// Batch 2 on the VALU for layers of at most 8192 rows and K <= 8192 (each
+// unit decoded once, then multiplied with both vectors); returns
+// hipErrorNotSupported (launching nothing) where it does not apply.
+hipError_t launch_gemv_bv(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+                          hipStream_t stream);
 // Fused batch-1 launch of n layers with one n_keep and K <= 16384; returns
 // hipErrorNotSupported (launching nothing) when the layers do not fit it.
 hipError_t launch_gemv_b1_multi(const i4s_packed *w, int32_t n, const uint16_t *x, uint16_t *const *y,

@@ -334,10 +334,10 @@ def test_gemv_zero_x_and_unit_vectors():
 @pytest.mark.parametrize("n_keep", [1, 2, 4])
 def test_batch_rows_match_single_calls(n_keep):
     """Row b of a batch call matches the batch-1 call on x_b (within the
-    tolerance: batch 1 and batch >= 2 run different kernels), and a row does
-    not depend on the other vectors of its batch: bit-identical across every
-    batch size that runs the same kernel (batch >= 2, with or without a
-    workspace: at this K the workspace path runs the same kernel)."""
+    tolerance: batch 1, batch 2 and batch >= 3 run different kernels here),
+    and a row does not depend on the other vectors of its batch: bit-identical
+    across every batch size that runs the same kernel (batch >= 3, with or
+    without a workspace: at this K the workspace path runs the same kernel)."""
     rng = np.random.default_rng(78)
     rows, cols = 64, 2048
     w = rand16(rng, (rows, cols))
@@ -356,7 +356,11 @@ def test_batch_rows_match_single_calls(n_keep):
     for b in range(16):
         y_ref, a_ref = O.gemv(w_hat, x[b:b + 1])
         assert_gemv_close(plain16[b][None], y_ref, a_ref, f"no-workspace batch row {b}")
-    for nb in range(2, 16):
+    y2 = gpu_run(p, x[:2], use_workspace=False)
+    for b in range(2):
+        y_ref, a_ref = O.gemv(w_hat, x[b:b + 1])
+        assert_gemv_close(y2[b][None], y_ref, a_ref, f"batch-2 row {b}")
+    for nb in range(3, 16):
         np.testing.assert_array_equal(gpu_run(p, x[:nb], use_workspace=False), plain16[:nb])
     for nb in range(9, 16):
         np.testing.assert_array_equal(gpu_run(p, x[:nb]), y16[:nb])
@@ -424,6 +428,8 @@ def test_run_on_side_stream():
 
 @pytest.mark.parametrize("n_keep,batch,rows,cols", [
     (2, 1, 37, 5120), (4, 1, 37, 5120), (2, 3, 37, 5120), (1, 1, 37, 5120), (4, 8, 37, 5120), (1, 6, 37, 5120),
+    # batch 2 on the VALU kernel (each unit decoded once for both vectors)
+    (2, 2, 37, 5120), (1, 2, 37, 5120), (4, 2, 37, 5120),
     # more than 8192 rows: two rows per wave at batch 1
     (2, 1, 8200, 1024), (1, 1, 8200, 1024), (4, 1, 8200, 2048)])
 def test_row_ptr_is_honoured(n_keep, batch, rows, cols):
