@@ -439,8 +439,12 @@ def kernel_label(m, batch):
         if units <= 256:
             return f"gemv_b1_direct_kernel<{m.n_keep},{rpw},{(units + 63) // 64},8>"
         return f"gemv_b1_kernel<{m.n_keep},{rpw},8>"
-    if m.n_keep == 2 and batch >= 2:
-        return "gemv_smfmac_rows_kernel / gemv_smfmac_split_kernel"
+    if batch == 2 and m.rows <= 8192 and units <= 128:
+        return f"gemv_bv_direct_kernel<{m.n_keep},2,{(units + 63) // 64}>"
+    if units <= 256:
+        return f"gemv_smfmac_rows_kernel<{m.n_keep},...>"
+    if m.n_keep == 2:
+        return "gemv_smfmac_split_kernel + gemv_split_reduce_kernel"
     return f"gemv_kernel<{m.n_keep},BT>=" + str(batch)
 
 

@@ -706,12 +706,18 @@ constexpr int kRMaxWaves = 8;                // waves per block (the wide form)
 // the vals of units past a row's end), codes [16 rows][U + 1], scales
 // [U units][16 rows].  One load instruction covers 64 / U rows of U units
 // (4 rows x 256 bytes or 8 rows x 128 bytes of vals).
-template <int U>
+// A dense unit-row: 64 nibbles, 32 bytes.
+struct DenseVals {
+  u32x4_t lo, hi;
+};
+
+template <int U, int NK = 2>
 struct RowsGeom {
   static constexpr int kStride = U + 1;
-  static constexpr int kValsBytes = 16 * kStride * 16;
-  static constexpr int kCodesBytes = 16 * kStride * 8;
-  static constexpr int kTileLds = kValsBytes + kCodesBytes + U * 16 * 2;  // 7040 / 3712 bytes
+  // vals per unit-row: 16 bytes (2:4), 8 (1:4: the 2:4 layout, half used), 32 (dense)
+  static constexpr int kValsBytes = 16 * kStride * (NK == 4 ? 32 : 16);
+  static constexpr int kCodesBytes = NK == 4 ? 0 : 16 * kStride * 8;
+  static constexpr int kTileLds = kValsBytes + kCodesBytes + U * 16 * 2;  // 2:4 and 1:4: 7040 / 3712 bytes
   static constexpr int kRowsPerLoad = 64 / U;
   static constexpr int kLoads = 16 / kRowsPerLoad;  // load instructions per tile and chunk
   static constexpr int kBlocks = U / 4;             // 4-unit blocks per chunk
@@ -768,7 +774,7 @@ __device__ __forceinline__ void rows_body(
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
     uint16_t *__restrict__ y, uint8_t *lds) {
-  typedef RowsGeom<U> Geo;
+  typedef RowsGeom<U, NK> Geo;
   constexpr int RL = Geo::kRowsPerLoad, NL = Geo::kLoads, NBK = Geo::kBlocks, ST = Geo::kStride;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, nwaves = blockDim.x / 64;
   const int li = lane % 16, lq = lane / 16;  // the matrix layout
@@ -776,8 +782,10 @@ __device__ __forceinline__ void rows_body(
   const int row0 = blk * 16 * TPW;
   const uint32_t nnz_row = (uint32_t)units * 16 * NK;
   const uint32_t ngroups = (uint32_t)units >> sg_shift;
-  typedef typename std::conditional<NK == 2, u32x4_t, u32x2_t>::type vals_t;    // a unit's vals
-  typedef typename std::conditional<NK == 2, u32x2_t, uint32_t>::type codes_t;  // a unit's codes
+  // a unit-row's vals (dense: two 16-byte halves) and codes (none when dense)
+  typedef typename std::conditional<NK == 4, DenseVals,
+                                    typename std::conditional<NK == 2, u32x4_t, u32x2_t>::type>::type vals_t;
+  typedef typename std::conditional<NK == 2, u32x2_t, uint32_t>::type codes_t;
   uint8_t *wl = lds + wave * TPW * Geo::kTileLds;  // the wave's areas, one per tile
   auto lv_of = [&](int t) { return reinterpret_cast<vals_t *>(wl + t * Geo::kTileLds); };  // [16 rows][ST]
   auto lc_of = [&](int t) { return reinterpret_cast<codes_t *>(wl + t * Geo::kTileLds + Geo::kValsBytes); };
@@ -830,8 +838,14 @@ __device__ __forceinline__ void rows_body(
       for (int k = 0; k < NL; ++k) {
         const uint32_t e0 = (uint32_t)wrow[t][k] * nnz_row + (uint32_t)u * 16 * NK;
         const uint32_t si = (uint32_t)wrow[t][k] * ngroups + ((uint32_t)u >> sg_shift);
-        wv[t][k] = __builtin_nontemporal_load(reinterpret_cast<const vals_t *>(vals + (e0 >> 1)));
-        wc[t][k] = __builtin_nontemporal_load(reinterpret_cast<const codes_t *>(codes + (e0 >> 3)));
+        if constexpr (NK == 4) {
+          const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(vals + (e0 >> 1));
+          wv[t][k].lo = __builtin_nontemporal_load(vp);
+          wv[t][k].hi = __builtin_nontemporal_load(vp + 1);
+        } else {
+          wv[t][k] = __builtin_nontemporal_load(reinterpret_cast<const vals_t *>(vals + (e0 >> 1)));
+          wc[t][k] = __builtin_nontemporal_load(reinterpret_cast<const codes_t *>(codes + (e0 >> 3)));
+        }
         wsc[t][k] = __builtin_nontemporal_load(scales + si);
       }
   };
@@ -868,15 +882,21 @@ __device__ __forceinline__ void rows_body(
         uint16_t *lsc = lsc_of(t);
         {
           vals_t zv;
-          if constexpr (NK == 2) zv = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-          else zv = u32x2_t{0x88888888u, 0x88888888u};
+          if constexpr (NK == 4) {
+            zv.lo = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+            zv.hi = zv.lo;
+          } else if constexpr (NK == 2) {
+            zv = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+          } else {
+            zv = u32x2_t{0x88888888u, 0x88888888u};
+          }
 #pragma unroll
           for (int k = 0; k < NL; ++k) lv[(RL * k + lr) * ST + lu] = zv;
         }
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
           lv[(RL * k + lr) * ST + vcol] = wv[t][k];
-          lc[(RL * k + lr) * ST + lu] = wc[t][k];
+          if constexpr (NK != 4) lc[(RL * k + lr) * ST + lu] = wc[t][k];
           lsc[lu * 16 + RL * k + lr] = wsc[t][k];
         }
       }
@@ -894,8 +914,10 @@ __device__ __forceinline__ void rows_body(
           const vals_t *lv = lv_of(t);
           const codes_t *lc = lc_of(t);
           const uint16_t *lsc = lsc_of(t);
-          uint32_t W0, W1, W2, W3, P = 0, Q = 0;
-          if constexpr (NK == 2) {
+          uint32_t W0 = 0, W1 = 0, W2 = 0, W3 = 0, P = 0, Q = 0;
+          if constexpr (NK == 4) {
+            // read per unit below (two words per lane and unit)
+          } else if constexpr (NK == 2) {
             // the matrix layout: lane (row li, chunk lq) takes unit 4bb + lq
             const u32x4_t v = lv[li * ST + 4 * bb + lq];
             const u32x2_t cw = lc[li * ST + 4 * bb + lq];
@@ -925,7 +947,21 @@ __device__ __forceinline__ void rows_body(
             const u8_t xv = {bx[2 * s].x, bx[2 * s].y, bx[2 * s].z, bx[2 * s].w,
                              bx[2 * s + 1].x, bx[2 * s + 1].y, bx[2 * s + 1].z, bx[2 * s + 1].w};
             const h16_t hb = __builtin_bit_cast(h16_t, xv);
-            if constexpr (NK == 2) {
+            if constexpr (NK == 4) {
+              // dense: two 16x16x32 steps per unit; lane (row li, quarter lq)
+              // takes vals words lq and 4 + lq (columns 8lq.. and 32 + 8lq..)
+              // of its row's unit, the B fragment's two halves are exactly
+              // those columns of the vectors
+              const uint32_t *lvw = reinterpret_cast<const uint32_t *>(lv);
+              const int e = (li * ST + 4 * bb + s) * 8;
+              h2_t qa[4], qb[4];
+              dequant_word(lvw[e + lq], qa);
+              dequant_word(lvw[e + 4 + lq], qb);
+              const h8_t a0 = {qa[0].x, qa[0].y, qa[1].x, qa[1].y, qa[2].x, qa[2].y, qa[3].x, qa[3].y};
+              const h8_t a1 = {qb[0].x, qb[0].y, qb[1].x, qb[1].y, qb[2].x, qb[2].y, qb[3].x, qb[3].y};
+              cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, __builtin_bit_cast(h8_t, bx[2 * s]), cg, 0, 0, 0);
+              cg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, __builtin_bit_cast(h8_t, bx[2 * s + 1]), cg, 0, 0, 0);
+            } else if constexpr (NK == 2) {
               if (s == 0) cg = smfmac_step<0>(W0, hb, cg, P, Q);
               if (s == 1) cg = smfmac_step<1>(W1, hb, cg, P, Q);
               if (s == 2) cg = smfmac_step<2>(W2, hb, cg, P, Q);
@@ -982,7 +1018,7 @@ __device__ __forceinline__ void rows_body(
               const uint32_t k8 = el & 7u;
               const uint32_t slot = (k8 & 1u) ? 4u + (k8 >> 1) : (k8 >> 1);
               const int q = (int)((word >> (4 * slot)) & 0xFu) - 8;
-              const uint32_t code = (codes[el >> 3] >> (2 * (el & 7u))) & 3u;
+              const uint32_t code = NK == 4 ? (uint32_t)(e & 3) : (codes[el >> 3] >> (2 * (el & 7u))) & 3u;
               const int col = u * kSegCols + 4 * (e / NK) + (int)code;
               g = fmaf((float)q, fp16_bits_to_float(xv[col]), g);
             }
@@ -1090,7 +1126,7 @@ struct RowsShape {
 // 8.  Measured: 5120x5120 at batch 4 / 8 / 16: 7.45 / 7.76 / 8.90 us with 16,
 // 6.63 / 7.32 / 9.01 with 8; 13824x5120 (432 blocks): 10.8 / 11.5 / 14.4 with
 // 16, 11.6 / 12.9 / 16.5 with 8.  I4S_ROWS_UNITS=8 or 16 forces it (tuning).
-RowsShape rows_shape(int units, int total_tiles, int batch) {
+RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep) {
   static const int forced_tpw = [] {
     const char *e = getenv("I4S_ROWS_TPW");
     const int v = e ? atoi(e) : 0;
@@ -1116,8 +1152,12 @@ RowsShape rows_shape(int units, int total_tiles, int batch) {
   const int maxw = r.u == 8 ? RowsGeom<8>::kMaxWaves : RowsGeom<16>::kMaxWaves;
   const int chunks = (units + r.u - 1) / r.u;
   r.cpw = chunks > maxw ? 2 : (forced_cpw ? forced_cpw : 1);
+  // dense rows are twice the bytes: two chunks of two tiles would spill
+  if (n_keep == 4 && r.cpw == 2) r.tpw = 1;
   r.waves = (chunks + r.cpw - 1) / r.cpw;
-  r.lds = (size_t)r.waves * r.tpw * (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);
+  const int tile_lds = n_keep == 4 ? (r.u == 8 ? RowsGeom<8, 4>::kTileLds : RowsGeom<16, 4>::kTileLds)
+                                    : (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);
+  r.lds = (size_t)r.waves * r.tpw * tile_lds;
   return r;
 }
 
@@ -1186,7 +1226,7 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
 template <int NK>
 hipError_t launch_rows(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                        hipStream_t stream) {
-  const RowsShape r = rows_shape(w.cols / kSegCols, (w.rows + 15) / 16, batch);
+  const RowsShape r = rows_shape(w.cols / kSegCols, (w.rows + 15) / 16, batch, NK);
   const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
   I4S_ROWS_DISPATCH(launch_rows_t, w, x, batch, y, r, sg_shift, stream);
 }
@@ -1197,7 +1237,7 @@ hipError_t launch_rows_multi(const i4s_packed *w, int32_t n, const uint16_t *x, 
   const int units = w[0].cols / kSegCols;
   int total_tiles = 0;
   for (int m = 0; m < n; ++m) total_tiles += (w[m].rows + 15) / 16;
-  const RowsShape r = rows_shape(units, total_tiles, batch);
+  const RowsShape r = rows_shape(units, total_tiles, batch, NK);
   const int sg_shift = w[0].group_size == 64 ? 0 : (w[0].group_size == 128 ? 1 : 2);
   MultiDesc d = {};
   d.n = n;
@@ -1288,8 +1328,8 @@ hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint
   if (NK == 2 && batch >= 2 && smfmac_enabled()) {
     return launch_smfmac(w, x, batch, y, stream);
   }
-  if (NK == 1 && batch >= 2 && smfmac_enabled() && rows_kernel_fits(w)) {
-    return launch_rows<1>(w, x, batch, y, stream);
+  if ((NK == 1 || NK == 4) && batch >= 2 && smfmac_enabled() && rows_kernel_fits(w)) {
+    return launch_rows<NK>(w, x, batch, y, stream);
   }
   if (batch <= 1) {
     return launch_gemv_b1(w, x, y, stream);
@@ -1361,10 +1401,10 @@ hipError_t launch_gemv_multi(const i4s_packed *w, int32_t n, const uint16_t *x, 
     if (batch == 1) {
       const hipError_t e = launch_gemv_b1_multi(w, n, x, y, stream);
       if (e != hipErrorNotSupported) return e;
-    } else if ((w[0].n_keep == 2 || w[0].n_keep == 1) && smfmac_enabled() && rows_kernel_enabled() &&
-               rows_kernel_fits(w[0])) {
-      return w[0].n_keep == 2 ? launch_rows_multi<2>(w, n, x, batch, y, stream)
-                              : launch_rows_multi<1>(w, n, x, batch, y, stream);
+    } else if (smfmac_enabled() && rows_kernel_enabled() && rows_kernel_fits(w[0])) {
+      if (w[0].n_keep == 2) return launch_rows_multi<2>(w, n, x, batch, y, stream);
+      if (w[0].n_keep == 1) return launch_rows_multi<1>(w, n, x, batch, y, stream);
+      return launch_rows_multi<4>(w, n, x, batch, y, stream);
     }
   }
   for (int m = 0; m < n; ++m) {

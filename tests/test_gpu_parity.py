@@ -433,7 +433,8 @@ def test_run_on_side_stream():
     # more than 8192 rows: two rows per wave at batch 1
     (2, 1, 8200, 1024), (1, 1, 8200, 1024), (4, 1, 8200, 2048)])
 def test_row_ptr_is_honoured(n_keep, batch, rows, cols):
-    """Rows stored in reverse order, described only by row_ptr, give the same y."""
+    """Rows stored in reverse order, described only by row_ptr, give the same y
+    (bit for bit on the VALU kernels, within the tolerance on the matrix cores)."""
     import int4_sparse_gemv_amd as I
     rng = np.random.default_rng(80 + n_keep)
     g = 128
@@ -451,7 +452,15 @@ def test_row_ptr_is_honoured(n_keep, batch, rows, cols):
                            dtype=torch.int32, device=p.vals.device)
     q = I.PackedWeight(rows, cols, n_keep, p.group_size, row_ptr, vals, codes, p.scales)
     y1 = gpu_run(q, x16)
-    np.testing.assert_array_equal(y0, y1)
+    if batch <= 2:
+        # the VALU kernels recompute a moved row with the same arithmetic
+        np.testing.assert_array_equal(y0, y1)
+    else:
+        # the matrix-core kernel recomputes it with a per-lane loop: within
+        # the tolerance, not necessarily the same bits
+        ref = O.pack(w, n_keep, g)
+        y_ref, a_ref = O.gemv(O.reconstruct(ref), x16)
+        assert_gemv_close(y1, y_ref, a_ref, f"row-ptr-reversed n={n_keep} b={batch}")
 
 
 @pytest.mark.parametrize("rows,cols,batch,g", [
