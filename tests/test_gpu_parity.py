@@ -292,7 +292,9 @@ def test_config_pack_and_gemv(name, m):
 @pytest.mark.parametrize("rows,cols,n_keep,g", [
     (1, 64, 2, 64), (17, 192, 2, 64), (33, 4160, 2, 64), (100, 8192, 2, 128), (5, 64, 4, 64),
     (19, 320, 4, 64), (21, 4224, 4, 128), (3, 128, 1, 64), (13, 4352, 1, 256), (16, 16384, 2, 256),
-    (700, 16384, 1, 128), (9, 20480, 1, 64), (37, 12288, 1, 64), (8200, 1024, 1, 64), (8210, 1024, 2, 128)])
+    (700, 16384, 1, 128), (9, 20480, 1, 64), (37, 12288, 1, 64), (8200, 1024, 1, 64), (8210, 1024, 2, 128),
+    # dense on the matrix cores: two tiles per wave (>= 300 tiles), and two chunks per wave
+    (4900, 2048, 4, 64), (40, 13824, 4, 128)])
 def test_gemv_shapes_and_all_batches(rows, cols, n_keep, g):
     rng = np.random.default_rng(rows + cols)
     w = rand16(rng, (rows, cols))
@@ -373,7 +375,7 @@ MULTI_CASES = [
     ([(100, 1, 64), (33, 1, 64), (257, 1, 64)], 2048, 1),         # 1:4, fused batch-1
     ([(512, 2, 128), (1000, 2, 128), (777, 2, 128)], 4096, 5),     # fused matrix-core batch
     ([(200, 1, 256), (70, 1, 256)], 3072, 16),                    # 1:4 fused matrix-core batch
-    ([(96, 4, 64), (50, 4, 64)], 1024, 8),                        # dense batch: one launch per layer
+    ([(96, 4, 64), (50, 4, 64)], 1024, 8),                        # dense batch: fused on the matrix cores
     ([(64, 2, 64), (80, 2, 128)], 1024, 1),                       # group sizes differ: per layer
     ([(40, 2, 64)] * 8, 512, 3),                                  # the most layers
     ([(24, 2, 64), (40, 2, 64)], 20480, 1),                       # K > 16384: per layer
