@@ -441,7 +441,8 @@ def kernel_label(m, batch):
         return f"gemv_b1_kernel<{m.n_keep},{rpw},8>"
     if batch == 2 and m.rows <= 8192 and units <= 128:
         return f"gemv_bv_direct_kernel<{m.n_keep},2,{(units + 63) // 64}>"
-    if units <= 256:
+    long_split = units > 256 and batch > 8 and m.rows <= 4096
+    if units <= 512 and not (m.n_keep == 2 and long_split):
         return f"gemv_smfmac_rows_kernel<{m.n_keep},...>"
     if m.n_keep == 2:
         return "gemv_smfmac_split_kernel + gemv_split_reduce_kernel"

@@ -184,9 +184,10 @@ i4s_status i4s_run(const i4s_packed *w /* host */, const uint16_t *x_fp16,
                    int32_t batch, uint16_t *y_fp16, void *stream);
 
 /* Bytes of device workspace i4s_run_ws needs for this layer and batch; 0
- * when the call needs none: batch 1, a pattern other than 2:4, K <= 16384
- * (the one-launch batch kernel covers those rows whole), or a layer whose K
- * split has a single slice.  Host-only and pure.  Errors:
+ * when the call needs none: batch 1, a pattern other than 2:4, K <= 16384,
+ * K <= 32768 unless the batch exceeds 8 on at most 4096 rows (the one-launch
+ * batch kernel covers those rows whole), or a layer whose K split has a
+ * single slice.  Host-only and pure.  Errors:
  * I4S_ERR_INVALID_ARGUMENT (descriptor inconsistent, batch out of range,
  * bytes == NULL). */
 i4s_status i4s_run_workspace_size(const i4s_packed *w /* host */, int32_t batch,
@@ -227,8 +228,9 @@ i4s_status i4s_run_ws(const i4s_packed *w /* host */, const uint16_t *x_fp16,
  *            not overlap one another, x, or any layer's packed buffers.
  * Results are bit-identical to n i4s_run calls.  One launch when the layers
  * share n_keep and group_size and either batch is 1 and cols <= 16384, or
- * batch >= 2, n_keep is 1 or 2 and cols <= 16384; otherwise one launch per
- * layer, in order, on `stream`.  Asynchronous; allocates nothing.
+ * batch >= 2 and cols <= 32768 (except batch 2 with cols <= 8192 and a layer
+ * of at most 8192 rows, which single calls run on another kernel); otherwise
+ * one launch per layer, in order, on `stream`.  Asynchronous; allocates nothing.
  * Errors: as i4s_run (reported for the first offending layer), plus
  * I4S_ERR_INVALID_ARGUMENT for n out of range, NULL arrays, differing cols
  * or overlapping outputs. */

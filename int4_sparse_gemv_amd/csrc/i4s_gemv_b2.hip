@@ -234,9 +234,12 @@ bool bv_enabled() {
 // stages both vectors, and tall layers have many blocks), and at batch 3 and
 // 4 the matrix cores win everywhere (5120x5120 b4: 10.2 against 6.7).  So:
 // batch 2, at most 8192 rows, K <= 8192.
+bool gemv_bv_applies(const i4s_packed &w, int32_t batch) {
+  return bv_enabled() && batch == 2 && w.rows <= 8192 && w.cols / kSegCols <= 128;
+}
+
 hipError_t launch_gemv_bv(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y, hipStream_t stream) {
-  const int units = w.cols / kSegCols;
-  if (!bv_enabled() || batch != 2 || w.rows > 8192 || units > 128) return hipErrorNotSupported;
+  if (!gemv_bv_applies(w, batch)) return hipErrorNotSupported;
   switch (w.n_keep) {
     case 1: return launch_bv_u<1, 2>(w, x, batch, y, stream);
     case 2: return launch_bv_u<2, 2>(w, x, batch, y, stream);

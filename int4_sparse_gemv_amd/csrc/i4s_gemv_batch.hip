@@ -1102,10 +1102,10 @@ bool rows_kernel_enabled() {
   return v;
 }
 
-// The rows kernel covers up to 8 waves of 1 or 2 chunks: K <= 16384.
+// The rows kernel covers up to 8 waves of 1, 2 or 4 chunks: K <= 32768.
 bool rows_kernel_fits(const i4s_packed &w) {
   const int chunks = (w.cols / kSegCols + kRUnits - 1) / kRUnits;
-  return chunks <= 2 * kRMaxWaves;
+  return chunks <= 4 * kRMaxWaves;
 }
 
 // Shape of a rows-kernel launch: chunks per wave, waves per block, tiles
@@ -1151,9 +1151,10 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep) {
   if (forced_cpw == 2) r.u = 16;  // the 8-unit form has one chunk per wave
   const int maxw = r.u == 8 ? RowsGeom<8>::kMaxWaves : RowsGeom<16>::kMaxWaves;
   const int chunks = (units + r.u - 1) / r.u;
-  r.cpw = chunks > maxw ? 2 : (forced_cpw ? forced_cpw : 1);
-  // dense rows are twice the bytes: two chunks of two tiles would spill
-  if (n_keep == 4 && r.cpw == 2) r.tpw = 1;
+  r.cpw = chunks > 2 * maxw ? 4 : (chunks > maxw ? 2 : (forced_cpw ? forced_cpw : 1));
+  // dense rows are twice the bytes: two chunks of two tiles would spill; four
+  // chunks per wave (K > 16384) always take one tile per wave
+  if ((n_keep == 4 && r.cpw == 2) || r.cpw == 4) r.tpw = 1;
   r.waves = (chunks + r.cpw - 1) / r.cpw;
   const int tile_lds = n_keep == 4 ? (r.u == 8 ? RowsGeom<8, 4>::kTileLds : RowsGeom<16, 4>::kTileLds)
                                     : (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);
@@ -1214,6 +1215,7 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
 #define I4S_ROWS_DISPATCH(FN, ...)                                                       \
   do {                                                                                   \
     if (r.u == 16) {                                                                     \
+      if (r.cpw == 4) I4S_ROWS_SG(FN, 4, 1, 16, __VA_ARGS__);                           \
       if (r.cpw == 1 && r.tpw == 1) I4S_ROWS_SG(FN, 1, 1, 16, __VA_ARGS__);             \
       if (r.cpw == 1) I4S_ROWS_SG(FN, 1, 2, 16, __VA_ARGS__);                           \
       if (r.tpw == 1) I4S_ROWS_SG(FN, 2, 1, 16, __VA_ARGS__);                           \
@@ -1328,7 +1330,7 @@ hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint
   if (NK == 2 && batch >= 2 && smfmac_enabled()) {
     return launch_smfmac(w, x, batch, y, stream);
   }
-  if ((NK == 1 || NK == 4) && batch >= 2 && smfmac_enabled() && rows_kernel_fits(w)) {
+  if ((NK == 1 || NK == 4) && batch >= 2 && smfmac_enabled() && rows_kernel_enabled() && rows_kernel_fits(w)) {
     return launch_rows<NK>(w, x, batch, y, stream);
   }
   if (batch <= 1) {
@@ -1360,17 +1362,23 @@ SplitPlan split_plan(const i4s_packed &w, int32_t batch) {
   if (ups > max_ups) ups = max_ups;
   pl.ups = ups;
   pl.ksplit = (units + ups - 1) / ups;
-  // When the split pays: only where the rows kernel does not fit (K > 16384).
-  // Measured on the 13B-shaped layers with two tiles per wave in the rows
-  // kernel, the rows kernel is as fast or faster at every batch (5120x13824
-  // at batch 16: 19.5 us both; everywhere else 5-40 % faster), and it needs
-  // no workspace and no second launch.  I4S_SPLIT=0 / 1 forces the split off
-  // or on (tuning and cross-checks).
+  // When the split pays: where the rows kernel does not fit (K > 32768), and
+  // for K > 16384 at batch > 8 on at most 4096 rows.  Measured on MI355X: on
+  // the 13B-shaped layers the rows kernel is as fast or faster at every batch
+  // (5120x13824 at batch 16: 19.5 us both; everywhere else 5-40 % faster);
+  // with four chunks per wave (K > 16384), hot, us at b4 / b8 / b16:
+  // 4096x28672 rows 17.4 / 20.8 / 29.9 against split 23.3 / 23.1 / 24.7,
+  // 8192x20480 rows 25.5 / 30.6 / 43.3 against split 47.3 / 47.5 / 46.6.
+  // The rows kernel needs no workspace and no second launch.  I4S_SPLIT=0 /
+  // 1 forces the split off or on (tuning and cross-checks).
   static const int split_env = [] {
     const char *e = getenv("I4S_SPLIT");
     return e ? (e[0] == '0' ? 0 : 1) : -1;
   }();
-  const bool wanted = split_env >= 0 ? split_env == 1 : units > 2 * kRMaxWaves * kRUnits;
+  const bool wanted =
+      split_env >= 0 ? split_env == 1
+                     : (units > 4 * kRMaxWaves * kRUnits ||
+                        (units > 2 * kRMaxWaves * kRUnits && batch > 8 && w.rows <= 4096));
   if (!wanted) return SplitPlan{};
   if (pl.ksplit > 1) pl.partial_bytes = (size_t)pl.ksplit * pl.row_groups * kSWaves * kSTiles * 64 * sizeof(f4_t);
   pl.workspace_bytes = pl.partial_bytes;
@@ -1395,13 +1403,18 @@ hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch, ui
 hipError_t launch_gemv_multi(const i4s_packed *w, int32_t n, const uint16_t *x, int32_t batch,
                              uint16_t *const *y, hipStream_t stream) {
   bool same = true;  // one pattern, one group size, one K
-  for (int m = 1; m < n; ++m)
+  // a layer that a single call runs on the batch-2 VALU kernel keeps that
+  // kernel, so that fused results stay those of single calls bit for bit
+  bool valu_b2 = gemv_bv_applies(w[0], batch);
+  for (int m = 1; m < n; ++m) {
     same &= w[m].n_keep == w[0].n_keep && w[m].group_size == w[0].group_size && w[m].cols == w[0].cols;
+    valu_b2 |= gemv_bv_applies(w[m], batch);
+  }
   if (n > 1 && same) {
     if (batch == 1) {
       const hipError_t e = launch_gemv_b1_multi(w, n, x, y, stream);
       if (e != hipErrorNotSupported) return e;
-    } else if (smfmac_enabled() && rows_kernel_enabled() && rows_kernel_fits(w[0])) {
+    } else if (!valu_b2 && smfmac_enabled() && rows_kernel_enabled() && rows_kernel_fits(w[0])) {
       if (w[0].n_keep == 2) return launch_rows_multi<2>(w, n, x, batch, y, stream);
       if (w[0].n_keep == 1) return launch_rows_multi<1>(w, n, x, batch, y, stream);
       return launch_rows_multi<4>(w, n, x, batch, y, stream);

@@ -71,6 +71,7 @@ hipError_t launch_gemv_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, h
 // hipErrorNotSupported (launching nothing) where it does not apply.
 hipError_t launch_gemv_bv(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                           hipStream_t stream);
+bool gemv_bv_applies(const i4s_packed &w, int32_t batch);
 // Fused batch-1 launch of n layers with one n_keep and K <= 16384; returns
 // hipErrorNotSupported (launching nothing) when the layers do not fit it.
 hipError_t launch_gemv_b1_multi(const i4s_packed *w, int32_t n, const uint16_t *x, uint16_t *const *y,

@@ -200,16 +200,21 @@ def test_run_workspace_size_is_host_only_and_planned(lib):
     for batch in (2, 4, 8, 16):
         assert B.i4s_run_workspace_size(_desc(13824, 5120, 2, 128), batch, n) == B.I4S_OK and n.value == 0
         assert B.i4s_run_workspace_size(_desc(5120, 13824, 2, 128), batch, n) == B.I4S_OK and n.value == 0
-    # longer rows split K: fp32 partial tiles, 16 tiles x 64 lanes x 16 bytes
+    # 16384 < K <= 32768: whole rows too, except batch > 8 on at most 4096 rows
+    assert B.i4s_run_workspace_size(_desc(5120, 20480, 2, 128), 16, n) == B.I4S_OK and n.value == 0
+    assert B.i4s_run_workspace_size(_desc(4096, 20480, 2, 128), 8, n) == B.I4S_OK and n.value == 0
+    # the others split K: fp32 partial tiles, 16 tiles x 64 lanes x 16 bytes
     # per (256-row group, K slice)
-    assert B.i4s_run_workspace_size(_desc(5120, 20480, 2, 128), 16, n) == B.I4S_OK
+    assert B.i4s_run_workspace_size(_desc(4096, 20480, 2, 128), 16, n) == B.I4S_OK
+    assert n.value > 0 and n.value % (16 * 64 * 16) == 0
+    assert B.i4s_run_workspace_size(_desc(5120, 40960, 2, 128), 4, n) == B.I4S_OK
     assert n.value > 0 and n.value % (16 * 64 * 16) == 0
     assert B.i4s_run_workspace_size(_desc(), 0, n) == B.I4S_ERR_INVALID_ARGUMENT
     assert lib.i4s_run_workspace_size(ctypes.byref(_desc()), 2, None) == B.I4S_ERR_INVALID_ARGUMENT
 
 
 def test_run_ws_validation_fails_before_any_device_call(lib):
-    d = _desc(5120, 20480, 2, 128)
+    d = _desc(4096, 20480, 2, 128)
     n = ctypes.c_uint64()
     assert B.i4s_run_workspace_size(d, 16, n) == B.I4S_OK
     x, y, ws = 1 << 34, 1 << 35, 1 << 36

@@ -294,7 +294,9 @@ def test_config_pack_and_gemv(name, m):
     (19, 320, 4, 64), (21, 4224, 4, 128), (3, 128, 1, 64), (13, 4352, 1, 256), (16, 16384, 2, 256),
     (700, 16384, 1, 128), (9, 20480, 1, 64), (37, 12288, 1, 64), (8200, 1024, 1, 64), (8210, 1024, 2, 128),
     # dense on the matrix cores: two tiles per wave (>= 300 tiles), and two chunks per wave
-    (4900, 2048, 4, 64), (40, 13824, 4, 128)])
+    (4900, 2048, 4, 64), (40, 13824, 4, 128),
+    # K > 16384 on the matrix cores: four chunks per wave
+    (24, 20480, 4, 128), (17, 32768, 4, 64), (33, 32768, 1, 256)])
 def test_gemv_shapes_and_all_batches(rows, cols, n_keep, g):
     rng = np.random.default_rng(rows + cols)
     w = rand16(rng, (rows, cols))
@@ -379,6 +381,10 @@ MULTI_CASES = [
     ([(64, 2, 64), (80, 2, 128)], 1024, 1),                       # group sizes differ: per layer
     ([(40, 2, 64)] * 8, 512, 3),                                  # the most layers
     ([(24, 2, 64), (40, 2, 64)], 20480, 1),                       # K > 16384: per layer
+    ([(24, 2, 64), (40, 2, 64)], 20480, 4),                       # K > 16384, batch: fused
+    ([(512, 2, 128), (1000, 2, 128)], 4096, 2),                   # batch 2: per layer (VALU kernel)
+    ([(64, 2, 128), (9000, 2, 128)], 4096, 2),                    # one layer too tall for it: per layer
+    ([(24, 2, 64), (40, 2, 64)], 40960, 4),                       # K > 32768: per layer
     ([(4100, 2, 64), (4200, 2, 64)], 1024, 6),                    # two tiles per wave, ragged
     ([(4100, 1, 128), (4200, 1, 128)], 2048, 9),                  # the same for 1:4
 ]
@@ -471,8 +477,9 @@ def test_row_ptr_is_honoured(n_keep, batch, rows, cols):
     (64, 5120, 4, 256), (33, 13824, 16, 256), (16, 1024, 5, 128),
     # two-tile blocks fewer than the compute units at batch <= 8: 8-unit chunks
     (6000, 2048, 6, 128), (5000, 3072, 3, 64),
-    # K > 16384: the workspace path splits K across blocks
-    (96, 20480, 5, 64), (300, 24576, 16, 128), (40, 32768, 9, 256)])
+    # K > 16384: four chunks per wave at batch <= 8; the workspace path splits
+    # K across blocks at batch > 8 on few rows and for any batch beyond 32768
+    (96, 20480, 5, 64), (300, 24576, 16, 128), (40, 32768, 9, 256), (64, 40960, 4, 128)])
 def test_batch_paths_with_and_without_workspace(rows, cols, batch, g):
     """i4s_run (no workspace) and i4s_run_ws (K split across blocks where the
     layer's plan uses it) both meet the tolerance for every group size; the
