@@ -1146,12 +1146,13 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep) {
   static const int forced_cpw = [] {
     const char *e = getenv("I4S_ROWS_CPW");
     const int v = e ? atoi(e) : 0;
-    return (v == 1 || v == 2) ? v : 0;
+    return (v == 1 || v == 2 || v == 4) ? v : 0;
   }();
-  if (forced_cpw == 2) r.u = 16;  // the 8-unit form has one chunk per wave
+  if (forced_cpw >= 2) r.u = 16;  // the 8-unit form has one chunk per wave
   const int maxw = r.u == 8 ? RowsGeom<8>::kMaxWaves : RowsGeom<16>::kMaxWaves;
   const int chunks = (units + r.u - 1) / r.u;
-  r.cpw = chunks > 2 * maxw ? 4 : (chunks > maxw ? 2 : (forced_cpw ? forced_cpw : 1));
+  r.cpw = chunks > 2 * maxw ? 4 : (chunks > maxw ? 2 : 1);
+  if (forced_cpw > r.cpw) r.cpw = forced_cpw;
   // dense rows are twice the bytes: two chunks of two tiles would spill; four
   // chunks per wave (K > 16384) always take one tile per wave
   if ((n_keep == 4 && r.cpw == 2) || r.cpw == 4) r.tpw = 1;
