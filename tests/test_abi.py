@@ -82,7 +82,8 @@ def test_version_and_status_strings(lib):
 
 @pytest.mark.parametrize("rows,cols,n_keep,g", [
     (512, 512, 2, 128), (4096, 4096, 2, 128), (11008, 4096, 2, 0), (4096, 11008, 2, 64),
-    (4096, 4096, 4, 64), (13824, 5120, 2, 128), (3, 192, 1, 64), (1, 64, 4, 64)])
+    (4096, 4096, 4, 64), (13824, 5120, 2, 128), (3, 192, 1, 64), (1, 64, 4, 64),
+    (65535, 32768, 4, 128), (131071, 32768, 2, 128)])   # nnz just below 2**31
 def test_pack_sizes_match_closed_form(lib, rows, cols, n_keep, g):
     sz = B.i4s_sizes()
     assert B.i4s_pack_sizes(rows, cols, n_keep, g, sz) == B.I4S_OK
@@ -94,7 +95,8 @@ def test_pack_sizes_match_closed_form(lib, rows, cols, n_keep, g):
 
 @pytest.mark.parametrize("rows,cols,n_keep,g", [
     (0, 512, 2, 128), (4, 96, 2, 64), (4, 512, 3, 128), (4, 512, 2, 32), (4, 192, 2, 128),
-    (4, 320, 2, 0), (4, 576, 2, 256), (1 << 20, 1 << 12, 4, 64), (-1, 64, 2, 64)])
+    (4, 320, 2, 0), (4, 576, 2, 256), (1 << 20, 1 << 12, 4, 64), (-1, 64, 2, 64),
+    (65536, 32768, 4, 128), (131072, 32768, 2, 128)])   # nnz = 2**31
 def test_pack_sizes_rejects(lib, rows, cols, n_keep, g):
     sz = B.i4s_sizes()
     assert B.i4s_pack_sizes(rows, cols, n_keep, g, sz) == B.I4S_ERR_INVALID_ARGUMENT

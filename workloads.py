@@ -13,6 +13,10 @@ Recipe (one numpy ``default_rng(seed)`` stream per matrix):
   rounded once to fp16 (round-to-nearest-even).
 * x: drawn from the same stream after W, ``standard_normal((B, K))`` rounded to
   fp16.  W is therefore identical for every batch size B of a given seed.
+* The largest layer of the tests (``make_weight_on_device``) is drawn on the
+  GPU by torch's seeded generator: float32 ``0.02 * randn`` rounded once to
+  fp16.  The rows the test checks are copied back from that tensor, so the
+  oracle and the library see the same weights.
 * Importance inputs (``make_importance_inputs``, a stream of their own):
   column norms ``16 * exp(0.5 * standard_normal(K))`` in float32, with 1 % of
   the columns (at least one) set to 0 (dead channels) and 1 % (at least one)
@@ -68,6 +72,23 @@ def make_weight(rows: int, cols: int, seed: int, outliers: bool = False,
         idx = rng.choice(rows * cols, n, replace=False)
         w.reshape(-1)[idx] *= 8.0
     return w.astype(np.float16)
+
+
+def make_weight_on_device(rows: int, cols: int, seed: int, device):
+    """fp16 weight [rows][cols], N(0, 0.02^2), drawn on ``device`` by torch's
+    seeded generator for that device (float32 normals, times 0.02, rounded
+    once to fp16): a layer of several GB without a host copy.  Only the test
+    of the largest layer uses it; the rows it checks are read back from the
+    returned tensor."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    w = torch.empty((rows, cols), dtype=torch.float16, device=device)
+    step = max(1, (1 << 26) // cols)  # 256 MiB of float32 at a time
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        w[r0:r1] = (0.02 * torch.randn((r1 - r0, cols), generator=g, device=device, dtype=torch.float32)).half()
+    return w
 
 
 def make_x(rng: np.random.Generator, batch: int, cols: int) -> np.ndarray:
