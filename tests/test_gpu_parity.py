@@ -314,43 +314,51 @@ def test_gemv_shapes_and_all_batches(rows, cols, n_keep, g):
         assert (y_gpu[:, rows // 2] == 0).all()
 
 
-def test_largest_layer_sampled_rows():
-    """The largest layer the format allows: dense INT4, 65535 x 32768, G = 128,
-    so nnz = 2**31 - 32768 and row_ptr's last entry sits just below 2**31.
-    Packed and multiplied on the GPU in full.  At a fixed G every row packs on
-    its own, so sampled rows (first and last, both sides of tile and block
-    edges, random ones) are checked bit for bit against the oracle's pack of
-    those rows alone, and their outputs against the oracle's GEMV of those
-    rows, at batch 1 and 16 (the last tile of 16 rows is one row short)."""
+@pytest.mark.parametrize("R,K,n_keep", [(65535, 32768, 4), (131071, 32768, 2), (65535, 65536, 2)])
+def test_largest_layer_sampled_rows(R, K, n_keep):
+    """The largest layers the format allows, G = 128: dense INT4 with 65535
+    rows of 32768 and 2:4 with 131071 rows of 32768 or 65535 rows of 65536,
+    so nnz = R * K * N / 4 sits just below 2**31 (as does row_ptr's last
+    entry).  Packed and multiplied on the GPU in full, with and without a
+    workspace (K = 65536 splits K across blocks with one).  At a fixed G every
+    row packs on its own, so sampled rows (first and last, both sides of tile
+    and block edges, random ones) are checked bit for bit against the
+    oracle's pack of those rows alone, and their outputs against the oracle's
+    GEMV of those rows, at batch 1, 4 and 16 (the last tile of 16 rows is one
+    row short)."""
     import int4_sparse_gemv_amd as I
-    R, K, G = 65535, 32768, 128
-    say(f"case largest layer {R}x{K} dense G={G}")
+    G = 128
+    nnz_row = K * n_keep // 4
+    say(f"case largest layer {R}x{K} n={n_keep} G={G}")
     w = WL.make_weight_on_device(R, K, 11, "cuda")
-    p = I.pack(w, 4, G)
+    p = I.pack(w, n_keep, G)
     torch.cuda.synchronize()
-    assert p.nnz == R * K < 2 ** 31
+    assert p.nnz == R * nnz_row < 2 ** 31
     rng = np.random.default_rng(12)
-    sel = np.unique(np.concatenate([[0, 1, 15, 16, 255, 256, 8191, 8192, 32767, 32768, 65519, 65520, 65534],
+    sel = np.unique(np.concatenate([[0, 1, 15, 16, 255, 256, 8191, 8192, 32767, 32768, R - 16, R - 15, R - 1],
                                     rng.integers(0, R, 8)]))
     sel_t = torch.from_numpy(sel).cuda()
     w_sel = w[sel_t].cpu().numpy()
     del w
     torch.cuda.empty_cache()
     say("  packed; oracle on the sampled rows")
-    ref = O.pack(w_sel, 4, G)
+    ref = O.pack(w_sel, n_keep, G)
     rp = p.row_ptr.cpu().numpy().astype(np.int64)
-    np.testing.assert_array_equal(rp, np.arange(R + 1, dtype=np.int64) * K)
-    vals = p.vals.view(R, K // 2)[sel_t].cpu().numpy()
-    scales = p.scales.view(R, K // G)[sel_t].cpu().numpy().view(np.uint16)
-    np.testing.assert_array_equal(vals, np.asarray(ref["vals"]).reshape(len(sel), K // 2))
-    np.testing.assert_array_equal(scales, np.asarray(ref["scales"]).reshape(len(sel), K // G))
+    np.testing.assert_array_equal(rp, np.arange(R + 1, dtype=np.int64) * nnz_row)
+    got = {"vals": p.vals.view(R, nnz_row // 2)[sel_t].cpu().numpy(),
+           "scales": p.scales.view(R, K // G)[sel_t].cpu().numpy().view(np.uint16)}
+    if n_keep < 4:
+        got["codes"] = p.codes.view(R, nnz_row // 8)[sel_t].cpu().numpy().view(np.uint16)
+    for k, a in got.items():
+        np.testing.assert_array_equal(a, np.asarray(ref[k]).reshape(len(sel), -1), err_msg=k)
     w_hat = O.reconstruct(ref)
     x16 = WL.make_x(np.random.default_rng(13), 16, K)
-    for b in (1, 16):
+    for b in (1, 4, 16):
         say(f"  gemv batch={b}")
-        y = gpu_run(p, x16[:b])
         y_ref, a_ref = O.gemv(w_hat, x16[:b])
-        assert_gemv_close(y[:, sel], y_ref, a_ref, f"largest layer b{b}")
+        for ws in ((True, False) if b > 1 else (True,)):
+            y = gpu_run(p, x16[:b], use_workspace=ws)
+            assert_gemv_close(y[:, sel], y_ref, a_ref, f"largest layer b{b} ws={ws}")
 
 
 def test_gemv_zero_x_and_unit_vectors():
