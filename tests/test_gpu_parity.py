@@ -314,12 +314,13 @@ def test_gemv_shapes_and_all_batches(rows, cols, n_keep, g):
         assert (y_gpu[:, rows // 2] == 0).all()
 
 
-@pytest.mark.parametrize("R,K,n_keep", [(65535, 32768, 4), (131071, 32768, 2), (65535, 65536, 2)])
+@pytest.mark.parametrize("R,K,n_keep", [(65535, 32768, 4), (131071, 32768, 2), (65535, 65536, 2),
+                                         (32767, 65536, 4), (65535, 65536, 1)])
 def test_largest_layer_sampled_rows(R, K, n_keep):
     """The largest layers the format allows, G = 128: dense INT4 with 65535
-    rows of 32768 and 2:4 with 131071 rows of 32768 or 65535 rows of 65536,
-    so nnz = R * K * N / 4 sits just below 2**31 (as does row_ptr's last
-    entry).  Packed and multiplied on the GPU in full, with and without a
+    rows of 32768 or 32767 of 65536, 2:4 with 131071 rows of 32768 or 65535
+    of 65536, so nnz = R * K * N / 4 sits just below 2**31 (as does row_ptr's
+    last entry); and 1:4 with 65535 rows of 65536 (2**30 - 16384).  Packed and multiplied on the GPU in full, with and without a
     workspace (K = 65536 splits K across blocks with one).  At a fixed G every
     row packs on its own, so sampled rows (first and last, both sides of tile
     and block edges, random ones) are checked bit for bit against the
@@ -335,8 +336,11 @@ def test_largest_layer_sampled_rows(R, K, n_keep):
     torch.cuda.synchronize()
     assert p.nnz == R * nnz_row < 2 ** 31
     rng = np.random.default_rng(12)
-    sel = np.unique(np.concatenate([[0, 1, 15, 16, 255, 256, 8191, 8192, 32767, 32768, R - 16, R - 15, R - 1],
+    half = R // 2
+    sel = np.unique(np.concatenate([[0, 1, 15, 16, 255, 256, 8191, 8192, half - 1, half, R - 16, R - 15, R - 1],
                                     rng.integers(0, R, 8)]))
+    # every sampled row exists: the gathers below have no bounds check
+    assert sel.min() >= 0 and sel.max() < R
     sel_t = torch.from_numpy(sel).cuda()
     w_sel = w[sel_t].cpu().numpy()
     del w
