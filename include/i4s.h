@@ -130,8 +130,10 @@ i4s_status i4s_pack_sizes(int32_t rows, int32_t cols, int32_t n_keep,
  *   report     : optional host struct receiving the chosen G and the SSEs.
  * Enqueues its kernels on `stream` and synchronises that stream once to read
  * back the non-finite flag and, when adaptive, the SSE totals.
+ * The output buffers, the workspace (its first i4s_pack_sizes().workspace
+ * bytes) and w_fp16 must not overlap one another.
  * Errors: I4S_ERR_INVALID_ARGUMENT (checks as in i4s_pack_sizes, null or
- * misaligned pointers), I4S_ERR_WORKSPACE_TOO_SMALL,
+ * misaligned pointers, overlapping buffers), I4S_ERR_WORKSPACE_TOO_SMALL,
  * I4S_ERR_NONFINITE_WEIGHT (the output buffers are then unspecified),
  * I4S_ERR_UNSUPPORTED (device is not gfx950), I4S_ERR_DEVICE. */
 i4s_status i4s_pack(const uint16_t *w_fp16, int32_t rows, int32_t cols,
@@ -153,7 +155,8 @@ i4s_status i4s_pack(const uint16_t *w_fp16, int32_t rows, int32_t cols,
  * Both NULL gives exactly i4s_pack's magnitude mask, and so do norms that are
  * all 1 without gradients.  Only the mask depends on them: the kept weights
  * are quantized and encoded as in i4s_pack.  A score beyond fp32's range is
- * +inf and ties other +inf scores.  Both inputs are only read.
+ * +inf and ties other +inf scores.  Both inputs are only read, and neither
+ * may overlap an output buffer or the workspace.
  * Errors: as i4s_pack, plus I4S_ERR_INVALID_ARGUMENT for a misaligned
  * col_norm or grad_fp16, a negative or non-finite norm or a non-finite
  * gradient (detected on the device; a non-finite weight is reported first). */

@@ -137,6 +137,31 @@ i4s_status i4s_pack_ex(const uint16_t *w_fp16, int32_t rows, int32_t cols, int32
   if (workspace_bytes < sz.workspace)
     return fail(I4S_ERR_WORKSPACE_TOO_SMALL, "workspace has %llu bytes, %llu needed",
                 (unsigned long long)workspace_bytes, (unsigned long long)sz.workspace);
+  {
+    // the four outputs and the workspace are written while W and the
+    // importance inputs are read: no two of them may share a byte
+    const uint64_t wb = 2ull * rows * (uint64_t)cols;
+    struct Span {
+      const void *p;
+      uint64_t n;
+      const char *name;
+    } span[] = {
+        {inout->row_ptr, sz.row_ptr, "row_ptr"}, {inout->vals, sz.vals, "vals"},
+        {n_keep < 4 ? inout->codes : nullptr, sz.codes, "codes"}, {inout->scales, sz.scales, "scales"},
+        {workspace, sz.workspace, "workspace"},
+    };
+    const Span in[] = {{w_fp16, wb, "w_fp16"}, {col_norm, 4ull * cols, "col_norm"}, {grad_fp16, wb, "grad_fp16"}};
+    const int nspan = (int)(sizeof(span) / sizeof(span[0]));
+    for (int i = 0; i < nspan; ++i) {
+      if (!span[i].p) continue;
+      for (int j = i + 1; j < nspan; ++j)
+        if (span[j].p && overlap(span[i].p, span[i].n, span[j].p, span[j].n))
+          return fail(I4S_ERR_INVALID_ARGUMENT, "%s and %s overlap", span[i].name, span[j].name);
+      for (const Span &r : in)
+        if (r.p && overlap(span[i].p, span[i].n, r.p, r.n))
+          return fail(I4S_ERR_INVALID_ARGUMENT, "%s overlaps %s", span[i].name, r.name);
+    }
+  }
   st = check_device();
   if (st != I4S_OK) return st;
 

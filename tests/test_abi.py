@@ -183,6 +183,30 @@ def test_pack_validation_fails_before_any_device_call(lib):
     assert B.i4s_pack_ex(w, 64, 250, 2, 0, n, g, ws, sz.workspace, d, rep, None) == B.I4S_ERR_INVALID_ARGUMENT
 
 
+@pytest.mark.parametrize("case", ["ws_on_w", "vals_on_w", "codes_on_scales", "row_ptr_on_ws", "scales_on_grad",
+                                  "vals_on_norm"])
+def test_pack_rejects_overlapping_buffers(lib, case):
+    sz = B.i4s_sizes()
+    assert B.i4s_pack_sizes(64, 256, 2, 0, sz) == B.I4S_OK
+    d = _desc()
+    w, ws, n, g = 1 << 30, 1 << 31, 1 << 32, 1 << 33
+    if case == "ws_on_w":
+        ws = w + 2 * 64 * 256 - 16
+    elif case == "vals_on_w":
+        d.vals = w + 1024
+    elif case == "codes_on_scales":
+        d.codes = d.scales + sz.scales - 16
+    elif case == "row_ptr_on_ws":
+        d.row_ptr = ws + sz.workspace - 16
+    elif case == "scales_on_grad":
+        d.scales = g + 4096
+    else:
+        d.vals = n
+    st = B.i4s_pack_ex(w, 64, 256, 2, 0, n, g, ws, sz.workspace, d, None, None)
+    assert st == B.I4S_ERR_INVALID_ARGUMENT
+    assert "overlap" in B.i4s_last_error()
+
+
 def test_binding_without_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError):
         B._lib_saved = B._lib
