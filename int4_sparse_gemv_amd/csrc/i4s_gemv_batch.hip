@@ -702,8 +702,8 @@ constexpr int kRUnits = 16;                  // units per chunk (the wide form)
 constexpr int kRMaxWaves = 8;                // waves per block (the wide form)
 
 // Geometry of a chunk of U units (16 or 8) in a wave's LDS area for one
-// tile: vals [16 rows][U + 1] (the extra column spreads the banks and takes
-// the vals of units past a row's end), codes [16 rows][U + 1], scales
+// tile: vals [16 rows][U + 1] (the extra column spreads the banks), codes
+// [16 rows][U + 1], scales
 // [U units][16 rows].  One load instruction covers 64 / U rows of U units
 // (4 rows x 256 bytes or 8 rows x 128 bytes of vals).
 // A dense unit-row: 64 nibbles, 32 bytes.
@@ -865,39 +865,24 @@ __device__ __forceinline__ void rows_body(
     for (int c = 0; c < CPW; ++c) {
       // chunk c of every tile to the wave's LDS areas, in the load layout.
       // A unit past the row's end (only a row's last chunk can hold one; its
-      // lane read the last unit again) must add nothing: every lane first
-      // writes vals whose nibbles are all 8, i.e. q = 0, and a lane past the
-      // end then sends its loaded vals to the row's padding column (never
-      // read) instead of its own slot.  Its codes and scale stay those of the
-      // last unit (a valid index pattern and a finite scale), and its unit
-      // never shares a quantization group with a real one (K % G == 0).  Only
-      // addresses depend on the lane, so the loads are used on every path and
-      // stay where they were issued; and there is no branch (even a
+      // lane read the last unit again) must add nothing: its scale is staged
+      // as +0, and since its unit never shares a quantization group with a
+      // real one (K % G == 0), the group's partial tile (finite: real
+      // nibbles and activations of the last unit) is multiplied by zero.
+      // Only a value depends on the lane, so the loads are used on every
+      // path and stay where they were issued; and there is no branch (even a
       // wave-uniform one here split the body and made the compiler spill).
-      const int vcol = (wave * CPW + c) * U + lu < units ? lu : ST - 1;
+      const bool unit_ok = (wave * CPW + c) * U + lu < units;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         vals_t *lv = lv_of(t);
         codes_t *lc = lc_of(t);
         uint16_t *lsc = lsc_of(t);
-        {
-          vals_t zv;
-          if constexpr (NK == 4) {
-            zv.lo = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-            zv.hi = zv.lo;
-          } else if constexpr (NK == 2) {
-            zv = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-          } else {
-            zv = u32x2_t{0x88888888u, 0x88888888u};
-          }
-#pragma unroll
-          for (int k = 0; k < NL; ++k) lv[(RL * k + lr) * ST + lu] = zv;
-        }
 #pragma unroll
         for (int k = 0; k < NL; ++k) {
-          lv[(RL * k + lr) * ST + vcol] = wv[t][k];
+          lv[(RL * k + lr) * ST + lu] = wv[t][k];
           if constexpr (NK != 4) lc[(RL * k + lr) * ST + lu] = wc[t][k];
-          lsc[lu * 16 + RL * k + lr] = wsc[t][k];
+          lsc[lu * 16 + RL * k + lr] = unit_ok ? wsc[t][k] : (uint16_t)0;
         }
       }
       if (c + 1 < CPW) {
