@@ -154,6 +154,13 @@ def _workspace(device, stream_handle: int, nbytes: int):
     return t
 
 
+def _check_out(out, batch: int, rows: int, device) -> None:
+    torch = _torch()
+    if (out.dtype != torch.float16 or tuple(out.shape) != (batch, rows) or out.device != device
+            or not out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous float16 [{batch}][{rows}] tensor on {device}")
+
+
 def run(p: PackedWeight, x, out=None, descriptor: Optional[B.i4s_packed] = None, workspace=None,
         use_workspace: bool = True):
     """y = W_hat x for x of shape [batch][cols] (or [cols]) fp16 on the GPU.
@@ -169,10 +176,14 @@ def run(p: PackedWeight, x, out=None, descriptor: Optional[B.i4s_packed] = None,
         x = x.unsqueeze(0)
     if x.dtype != torch.float16 or x.dim() != 2 or x.shape[1] != p.cols or not x.is_cuda:
         raise ValueError("x must be float16 [batch][cols] on the GPU")
+    if p.vals.device != x.device:
+        raise ValueError(f"x is on {x.device}, the packed layer on {p.vals.device}")
     x = x.contiguous()
     batch = x.shape[0]
     if out is None:
         out = torch.empty(batch, p.rows, dtype=torch.float16, device=x.device)
+    else:
+        _check_out(out, batch, p.rows, x.device)
     d = descriptor if descriptor is not None else p.descriptor()
     stream = _stream_handle(x.device)
     nbytes = 0
@@ -182,8 +193,10 @@ def run(p: PackedWeight, x, out=None, descriptor: Optional[B.i4s_packed] = None,
         nbytes = n.value
     if nbytes:
         ws = workspace if workspace is not None else _workspace(x.device, stream, nbytes)
-        B.check(B.i4s_run_ws(d, x.data_ptr(), batch, out.data_ptr(), ws.data_ptr(), ws.numel(), stream),
-                "i4s_run_ws")
+        if ws.device != x.device or not ws.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on x's device")
+        B.check(B.i4s_run_ws(d, x.data_ptr(), batch, out.data_ptr(), ws.data_ptr(),
+                             ws.numel() * ws.element_size(), stream), "i4s_run_ws")
     else:
         B.check(B.i4s_run(d, x.data_ptr(), batch, out.data_ptr(), stream), "i4s_run")
     return out[0] if squeeze else out
@@ -202,10 +215,18 @@ def run_multi(layers, x, outs=None):
         x = x.unsqueeze(0)
     if x.dtype != torch.float16 or x.dim() != 2 or not x.is_cuda:
         raise ValueError("x must be float16 [batch][cols] on the GPU")
+    for p in layers:
+        if p.vals.device != x.device:
+            raise ValueError(f"x is on {x.device}, a packed layer on {p.vals.device}")
     x = x.contiguous()
     batch = x.shape[0]
     if outs is None:
         outs = [torch.empty(batch, p.rows, dtype=torch.float16, device=x.device) for p in layers]
+    else:
+        if len(outs) != len(layers):
+            raise ValueError(f"{len(outs)} outputs for {len(layers)} layers")
+        for o, p in zip(outs, layers):
+            _check_out(o, batch, p.rows, x.device)
     descs = [p.descriptor() for p in layers]
     B.check(B.i4s_run_multi(descs, x.data_ptr(), batch, [o.data_ptr() for o in outs], _stream_handle(x.device)),
             "i4s_run_multi")

@@ -466,6 +466,31 @@ def test_run_multi_equals_single_calls(layers, cols, batch):
         assert_gemv_close(got.astype(np.float64), y_ref, a_ref, f"multi layer {m}")
 
 
+def test_binding_rejects_bad_outputs_before_any_launch():
+    """The Python layer refuses outputs of the wrong shape, dtype or layout
+    (the C ABI cannot see a tensor's size) and a workspace on no device."""
+    import int4_sparse_gemv_amd as I
+    rng = np.random.default_rng(5)
+    p = gpu_pack(rand16(rng, (40, 256)), 2, 64)
+    x = torch.from_numpy(rng.standard_normal((3, 256)).astype(np.float16)).cuda()
+    bad = [torch.empty(3, 39, dtype=torch.float16, device="cuda"),
+           torch.empty(3, 40, dtype=torch.float32, device="cuda"),
+           torch.empty(40, 3, dtype=torch.float16, device="cuda").t(),
+           torch.empty(2, 40, dtype=torch.float16, device="cuda")]
+    for o in bad:
+        with pytest.raises(ValueError):
+            I.run(p, x, out=o)
+        with pytest.raises(ValueError):
+            I.run_multi([p, p], x, outs=[o, torch.empty(3, 40, dtype=torch.float16, device="cuda")])
+    with pytest.raises(ValueError):
+        I.run_multi([p, p], x, outs=[torch.empty(3, 40, dtype=torch.float16, device="cuda")])
+    with pytest.raises(ValueError):
+        I.run(p, x.cpu())
+    good = torch.empty(3, 40, dtype=torch.float16, device="cuda")
+    I.run(p, x, out=good)
+    torch.cuda.synchronize()
+
+
 def test_run_on_side_stream():
     import int4_sparse_gemv_amd as I
     rng = np.random.default_rng(79)
