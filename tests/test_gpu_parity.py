@@ -386,6 +386,33 @@ def test_gemv_zero_x_and_unit_vectors():
             np.testing.assert_array_equal(y[b], w_hat[:, j].astype(np.float16).astype(np.float64))
 
 
+@pytest.mark.parametrize("rows,cols,n_keep", [(300, 4096, 2), (300, 4096, 1), (300, 4096, 4), (70, 20480, 2),
+                                          (40, 40960, 2), (40, 40960, 4)])
+def test_all_pruned_rows_give_exact_zero(rows, cols, n_keep):
+    """A row that is zero (every group all-pruned: scale +0, q = 0) gives
+    y = 0 exactly, and so does a zero quantization group inside a row, on
+    every kernel: batch 1 (both forms), batch 2, the matrix-core batch forms,
+    the K-split and the VALU batch kernel."""
+    rng = np.random.default_rng(rows + cols + n_keep)
+    w = rand16(rng, (rows, cols))
+    zero_rows = [0, 1, 17, rows // 2, rows - 1]
+    w[zero_rows] = 0
+    w[5, 128:384] = 0  # whole groups of row 5 (every G divides 128 and 256)
+    say(f"case all-pruned rows {rows}x{cols} n={n_keep}")
+    p = gpu_pack(w, n_keep, 128)
+    ref = O.pack(w, n_keep, 128)
+    assert_pack_equal(p, ref, "all-pruned rows")
+    w_hat = O.reconstruct(ref)
+    assert (w_hat[zero_rows] == 0).all()
+    x16 = rng.standard_normal((16, cols)).astype(np.float16)
+    for batch in (1, 2, 3, 8, 16):
+        y_ref, a_ref = O.gemv(w_hat, x16[:batch])
+        for ws in ((True, False) if batch > 1 else (True,)):
+            y = gpu_run(p, x16[:batch], use_workspace=ws)
+            assert (y[:, zero_rows] == 0).all(), f"b{batch} ws={ws}: nonzero output for an all-pruned row"
+            assert_gemv_close(y, y_ref, a_ref, f"all-pruned rows b{batch} ws={ws}")
+
+
 @pytest.mark.parametrize("n_keep", [1, 2, 4])
 def test_batch_rows_match_single_calls(n_keep):
     """Row b of a batch call matches the batch-1 call on x_b (within the
