@@ -1037,7 +1037,7 @@ __device__ __forceinline__ void rows_body(
 }
 
 template <int NK, int CPW, int SG, int TPW, int U>
-__global__ __launch_bounds__(64 * RowsGeom<U>::kMaxWaves) void gemv_smfmac_rows_kernel(
+__global__ __launch_bounds__(64 * (TPW == 4 ? 12 : RowsGeom<U>::kMaxWaves)) void gemv_smfmac_rows_kernel(
     int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
@@ -1050,7 +1050,7 @@ __global__ __launch_bounds__(64 * RowsGeom<U>::kMaxWaves) void gemv_smfmac_rows_
 // finds its layer from the cumulative block counts and runs the single-layer
 // body on it.
 template <int NK, int CPW, int SG, int TPW, int U>
-__global__ __launch_bounds__(64 * RowsGeom<U>::kMaxWaves) void gemv_smfmac_rows_multi_kernel(
+__global__ __launch_bounds__(64 * (TPW == 4 ? 12 : RowsGeom<U>::kMaxWaves)) void gemv_smfmac_rows_multi_kernel(
     int units, const uint16_t *__restrict__ x, int batch, MultiDesc d) {
   extern __shared__ __align__(16) uint8_t lds[];  // [waves][TPW][RowsGeom<U>::kTileLds]
   int m = 0;
@@ -1111,11 +1111,12 @@ struct RowsShape {
 // 8.  Measured: 5120x5120 at batch 4 / 8 / 16: 7.45 / 7.76 / 8.90 us with 16,
 // 6.63 / 7.32 / 9.01 with 8; 13824x5120 (432 blocks): 10.8 / 11.5 / 14.4 with
 // 16, 11.6 / 12.9 / 16.5 with 8.  I4S_ROWS_UNITS=8 or 16 forces it (tuning).
-RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep) {
+// want_u (8 or 16) fixes the chunk width; 0 chooses it.
+RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want_u = 0) {
   static const int forced_tpw = [] {
     const char *e = getenv("I4S_ROWS_TPW");
     const int v = e ? atoi(e) : 0;
-    return (v == 1 || v == 2) ? v : 0;
+    return (v == 1 || v == 2 || v == 4) ? v : 0;
   }();
   static const int forced_u = [] {
     const char *e = getenv("I4S_ROWS_UNITS");
@@ -1123,8 +1124,19 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep) {
     return (v == 8 || v == 16) ? v : 0;
   }();
   RowsShape r;
-  r.tpw = forced_tpw ? forced_tpw : (total_tiles >= 300 ? 2 : 1);
-  r.u = forced_u ? forced_u : ((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) ? 8 : 16);
+  // Four tiles per wave (8-unit chunks, one per wave) for batches above 8
+  // on tall layers: each B fragment then feeds four tiles, halving the
+  // activation reads through L2 against two tiles.  Cold, us at b16:
+  // 13824x5120 15.4 -> 13.2, 11008x4096 12.0 -> 10.9; at b8 and below, and
+  // with fewer than ~160 four-tile blocks, two tiles per wave are as fast or
+  // faster (5120x5120 at b16: 9.1 against 12.0).  The block's LDS (waves x
+  // 4 x 3.7 KB) caps K at 5632.
+  const int tile8 = n_keep == 1 ? RowsGeom<8, 1>::kTileLds : RowsGeom<8>::kTileLds;
+  const bool four = n_keep != 4 && batch > 8 && total_tiles >= 640 && want_u != 16 &&
+                    (size_t)((units + 7) / 8) * 4 * tile8 <= 160 * 1024;
+  r.tpw = forced_tpw ? forced_tpw : (four ? 4 : (total_tiles >= 300 ? 2 : 1));
+  r.u = forced_u ? forced_u : (((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) || r.tpw == 4) ? 8 : 16);
+  if (want_u) r.u = want_u;
   // 8-unit chunks only with one chunk per wave (K <= 8192): two chunks per
   // wave of the 16-wave form would not fit its 128 registers
   if ((units + 7) / 8 > RowsGeom<8>::kMaxWaves) r.u = 16;
@@ -1141,9 +1153,12 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep) {
   // dense rows are twice the bytes: two chunks of two tiles would spill; four
   // chunks per wave (K > 16384) always take one tile per wave
   if ((n_keep == 4 && r.cpw == 2) || r.cpw == 4) r.tpw = 1;
+  // four tiles per wave: the 8-unit one-chunk form of 2:4 and 1:4 only (LDS)
+  if (r.tpw == 4 && (r.u != 8 || r.cpw != 1 || n_keep == 4)) r.tpw = 2;
   r.waves = (chunks + r.cpw - 1) / r.cpw;
   const int tile_lds = n_keep == 4 ? (r.u == 8 ? RowsGeom<8, 4>::kTileLds : RowsGeom<16, 4>::kTileLds)
                                     : (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);
+  if (r.tpw == 4 && (size_t)r.waves * 4 * tile_lds > 160 * 1024) r.tpw = 2;  // LDS per workgroup
   r.lds = (size_t)r.waves * r.tpw * tile_lds;
   return r;
 }
@@ -1204,10 +1219,13 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
       if (r.cpw == 4) I4S_ROWS_SG(FN, 4, 1, 16, __VA_ARGS__);                           \
       if (r.cpw == 1 && r.tpw == 1) I4S_ROWS_SG(FN, 1, 1, 16, __VA_ARGS__);             \
       if (r.cpw == 1) I4S_ROWS_SG(FN, 1, 2, 16, __VA_ARGS__);                           \
-      if (r.tpw == 1) I4S_ROWS_SG(FN, 2, 1, 16, __VA_ARGS__);                           \
-      I4S_ROWS_SG(FN, 2, 2, 16, __VA_ARGS__);                                           \
+      if (r.tpw == 1 || NK == 4) I4S_ROWS_SG(FN, 2, 1, 16, __VA_ARGS__);  /* dense: 1 */ \
+      if constexpr (NK != 4) I4S_ROWS_SG(FN, 2, 2, 16, __VA_ARGS__);                    \
     }                                                                                    \
     if (r.tpw == 1) I4S_ROWS_SG(FN, 1, 1, 8, __VA_ARGS__);                              \
+    if constexpr (NK != 4) {                                                             \
+      if (r.tpw == 4) I4S_ROWS_SG(FN, 1, 4, 8, __VA_ARGS__);                            \
+    }                                                                                    \
     I4S_ROWS_SG(FN, 1, 2, 8, __VA_ARGS__);                                              \
   } while (0)
 
@@ -1223,9 +1241,16 @@ template <int NK>
 hipError_t launch_rows_multi(const i4s_packed *w, int32_t n, const uint16_t *x, int32_t batch,
                              uint16_t *const *y, hipStream_t stream) {
   const int units = w[0].cols / kSegCols;
+  // The chunk width decides how a row's sum is split across waves, and so
+  // its rounding: fuse only layers whose single calls take the same width,
+  // and keep it (the tile count per wave does not change any result bit).
+  const int u0 = rows_shape(units, (w[0].rows + 15) / 16, batch, NK).u;
   int total_tiles = 0;
-  for (int m = 0; m < n; ++m) total_tiles += (w[m].rows + 15) / 16;
-  const RowsShape r = rows_shape(units, total_tiles, batch, NK);
+  for (int m = 0; m < n; ++m) {
+    if (rows_shape(units, (w[m].rows + 15) / 16, batch, NK).u != u0) return hipErrorNotSupported;
+    total_tiles += (w[m].rows + 15) / 16;
+  }
+  const RowsShape r = rows_shape(units, total_tiles, batch, NK, u0);
   const int sg_shift = w[0].group_size == 64 ? 0 : (w[0].group_size == 128 ? 1 : 2);
   MultiDesc d = {};
   d.n = n;
@@ -1401,9 +1426,10 @@ hipError_t launch_gemv_multi(const i4s_packed *w, int32_t n, const uint16_t *x, 
       const hipError_t e = launch_gemv_b1_multi(w, n, x, y, stream);
       if (e != hipErrorNotSupported) return e;
     } else if (!valu_b2 && smfmac_enabled() && rows_kernel_enabled() && rows_kernel_fits(w[0])) {
-      if (w[0].n_keep == 2) return launch_rows_multi<2>(w, n, x, batch, y, stream);
-      if (w[0].n_keep == 1) return launch_rows_multi<1>(w, n, x, batch, y, stream);
-      return launch_rows_multi<4>(w, n, x, batch, y, stream);
+      const hipError_t e = w[0].n_keep == 2   ? launch_rows_multi<2>(w, n, x, batch, y, stream)
+                           : w[0].n_keep == 1 ? launch_rows_multi<1>(w, n, x, batch, y, stream)
+                                              : launch_rows_multi<4>(w, n, x, batch, y, stream);
+      if (e != hipErrorNotSupported) return e;
     }
   }
   for (int m = 0; m < n; ++m) {

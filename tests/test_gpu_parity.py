@@ -296,7 +296,9 @@ def test_config_pack_and_gemv(name, m):
     # dense on the matrix cores: two tiles per wave (>= 300 tiles), and two chunks per wave
     (4900, 2048, 4, 64), (40, 13824, 4, 128),
     # K > 16384 on the matrix cores: four chunks per wave
-    (24, 20480, 4, 128), (17, 32768, 4, 64), (33, 32768, 1, 256)])
+    (24, 20480, 4, 128), (17, 32768, 4, 64), (33, 32768, 1, 256),
+    # four tiles per wave at batch > 8 (>= 640 tiles, K <= 5632), ragged
+    (10241, 5632, 2, 256), (10241, 2048, 1, 64)])
 def test_gemv_shapes_and_all_batches(rows, cols, n_keep, g):
     rng = np.random.default_rng(rows + cols)
     w = rand16(rng, (rows, cols))
@@ -465,6 +467,10 @@ MULTI_CASES = [
     ([(24, 2, 64), (40, 2, 64)], 40960, 4),                       # K > 32768: per layer
     ([(4100, 2, 64), (4200, 2, 64)], 1024, 6),                    # two tiles per wave, ragged
     ([(4100, 1, 128), (4200, 1, 128)], 2048, 9),                  # the same for 1:4
+    ([(2400, 2, 128), (2400, 2, 128)], 2048, 4),                  # fused at the single calls' chunk width
+    ([(10241, 2, 128), (10241, 2, 128)], 2048, 16),               # four tiles per wave, fused
+    ([(10241, 1, 64), (10241, 1, 64)], 2048, 12),                 # the same for 1:4
+    ([(10241, 2, 128), (600, 2, 128)], 2048, 16),                 # chunk widths differ: per layer
 ]
 
 
