@@ -173,7 +173,14 @@ i4s_status i4s_pack_ex(const uint16_t *w_fp16, int32_t rows, int32_t cols,
  * SparseGemv kernel over the 2-bit CSR format).
  *   w      : host descriptor filled by i4s_pack (or an equivalent layout);
  *            group_size must be 64, 128 or 256; vals 16-byte, codes 8-byte,
- *            row_ptr 4-byte and scales 2-byte aligned.  row_ptr is read.
+ *            row_ptr 4-byte and scales 2-byte aligned.  row_ptr is read:
+ *            row i's elements start at row_ptr[i], which must lie in
+ *            [0, nnz - nnz_row] and be a multiple of 16 * n_keep (one
+ *            64-column unit); i4s_pack writes i * nnz_row.  An entry off
+ *            that grid is moved onto it (clamped to the range, rounded down
+ *            to a unit) before any weight is read at it, so such a
+ *            descriptor gives unspecified outputs but no read outside the
+ *            buffers.
  *   x_fp16 : [batch][cols] fp16 bits, contiguous, 16-byte aligned.
  *   batch  : 1 .. I4S_MAX_BATCH.
  *   y_fp16 : [batch][rows] fp16 bits, contiguous, 2-byte aligned; fully

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
       if (moved) {
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-          rstart[r] = (uint32_t)rp[r];
+          rstart[r] = safe_row_start<NK>(rp[r], (uint32_t)(rows - 1) * nnz_row);
           if (has)
             load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
                           srow[r] + ((uint32_t)u >> sg_shift));
@@ -360,7 +360,8 @@ __device__ __forceinline__ void b1_direct_body(
       for (int k = 0; k < UPL; ++k) {
         const int u = min(lane + 64 * k, units - 1);
         UnitRegs<NK> t;
-        load_unit<NK>(t, vals, codes, scales, (uint32_t)rp[r] + (uint32_t)u * 16 * NK,
+        load_unit<NK>(t, vals, codes, scales,
+                      safe_row_start<NK>(rp[r], (uint32_t)(rows - 1) * nnz_row) + (uint32_t)u * 16 * NK,
                       srow[r] + ((uint32_t)u >> sg_shift));
         if (lane + 64 * k < units) {
           uint32_t xr[32];
@@ -464,26 +465,15 @@ hipError_t launch_b1_multi_t(const i4s_packed *w, int32_t n, const uint16_t *x, 
   }
 }
 
-// I4S_B1_KERNEL=stream forces the pipelined batch-1 kernel (tuning); read once.
-bool b1_direct_enabled() {
-  static const bool v = [] {
-    const char *e = getenv("I4S_B1_KERNEL");
-    return !(e && e[0] == 's');
-  }();
-  return v;
-}
-
 template <int NK, int RPW>
 hipError_t launch_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
   const int units = w.cols / kSegCols;
-  if (b1_direct_enabled()) {
-    switch ((units + 63) / 64) {
-      case 1: return launch_b1_direct<NK, RPW, 1>(w, x, y, stream);
-      case 2: return launch_b1_direct<NK, RPW, 2>(w, x, y, stream);
-      case 3: return launch_b1_direct<NK, RPW, 3>(w, x, y, stream);
-      case 4: return launch_b1_direct<NK, RPW, 4>(w, x, y, stream);
-      default: break;  // longer rows: the pipelined kernel
-    }
+  switch ((units + 63) / 64) {
+    case 1: return launch_b1_direct<NK, RPW, 1>(w, x, y, stream);
+    case 2: return launch_b1_direct<NK, RPW, 2>(w, x, y, stream);
+    case 3: return launch_b1_direct<NK, RPW, 3>(w, x, y, stream);
+    case 4: return launch_b1_direct<NK, RPW, 4>(w, x, y, stream);
+    default: break;  // longer rows: the pipelined kernel
   }
   int kc = kLdsBudget / (kStrideB1 * 2);
   if (kc > units) kc = units;
@@ -497,54 +487,31 @@ hipError_t launch_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStr
 
 // Rows per wave of the batch-1 kernel.  One row per wave keeps 2+ blocks on
 // every CU up to ~8k rows; taller matrices take two rows per wave so each
-// block's staged activations feed more rows.  I4S_B1_RPW (1, 2 or 4)
-// overrides the choice for tuning; it is read once.
-int b1_rows_per_wave(int rows) {
-  static const int forced = [] {
-    const char *e = getenv("I4S_B1_RPW");
-    const int r = e ? atoi(e) : 0;
-    return (r == 1 || r == 2 || r == 4) ? r : 0;
-  }();
-  if (forced) return forced;
-  return rows > 8192 ? 2 : 1;
-}
+// block's staged activations feed more rows.
+int b1_rows_per_wave(int rows) { return rows > 8192 ? 2 : 1; }
 
 }  // namespace
 
 hipError_t launch_gemv_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  const int rpw = b1_rows_per_wave(w.rows);
-  if (w.n_keep == 1) {
-    switch (rpw) {
-      case 2: return launch_b1<1, 2>(w, x, y, stream);
-      case 4: return launch_b1<1, 4>(w, x, y, stream);
-      default: return launch_b1<1, 1>(w, x, y, stream);
-    }
-  }
-  if (w.n_keep == 2) {
-    switch (rpw) {
-      case 2: return launch_b1<2, 2>(w, x, y, stream);
-      case 4: return launch_b1<2, 4>(w, x, y, stream);
-      default: return launch_b1<2, 1>(w, x, y, stream);
-    }
-  }
-  switch (rpw) {
-    case 2: return launch_b1<4, 2>(w, x, y, stream);
-    case 4: return launch_b1<4, 4>(w, x, y, stream);
-    default: return launch_b1<4, 1>(w, x, y, stream);
+  const bool two = b1_rows_per_wave(w.rows) == 2;
+  switch (w.n_keep) {
+    case 1: return two ? launch_b1<1, 2>(w, x, y, stream) : launch_b1<1, 1>(w, x, y, stream);
+    case 2: return two ? launch_b1<2, 2>(w, x, y, stream) : launch_b1<2, 1>(w, x, y, stream);
+    default: return two ? launch_b1<4, 2>(w, x, y, stream) : launch_b1<4, 1>(w, x, y, stream);
   }
 }
 
 hipError_t launch_gemv_b1_multi(const i4s_packed *w, int32_t n, const uint16_t *x, uint16_t *const *y,
                                 hipStream_t stream) {
   const int units = w[0].cols / kSegCols;
-  if (!b1_direct_enabled() || units > 256) return hipErrorNotSupported;
+  if (units > 256) return hipErrorNotSupported;
   int max_rows = 0;
   for (int m = 0; m < n; ++m) {
     if (w[m].n_keep != w[0].n_keep || w[m].cols != w[0].cols) return hipErrorNotSupported;
     max_rows = max_rows > w[m].rows ? max_rows : w[m].rows;
   }
   // rows per wave as for the tallest layer alone
-  const int rpw = b1_rows_per_wave(max_rows) >= 2 ? 2 : 1;
+  const int rpw = b1_rows_per_wave(max_rows);
   switch (w[0].n_keep) {
     case 1: return rpw == 2 ? launch_b1_multi_t<1, 2>(w, n, x, y, stream) : launch_b1_multi_t<1, 1>(w, n, x, y, stream);
     case 2: return rpw == 2 ? launch_b1_multi_t<2, 2>(w, n, x, y, stream) : launch_b1_multi_t<2, 1>(w, n, x, y, stream);

@@ -180,10 +180,11 @@ __global__ __launch_bounds__(512) void gemv_bv_direct_kernel(
 #pragma unroll
     for (int v = 0; v < BV; ++v) acc[v] = 0.0f;
     UnitRegs<NK> w2[UPL];
+    const uint32_t rs = safe_row_start<NK>(rp, (uint32_t)(rows - 1) * nnz_row);
 #pragma unroll
     for (int k = 0; k < UPL; ++k) {
       const int u = min(lane + 64 * k, units - 1);
-      load_unit<NK>(w2[k], vals, codes, scales, (uint32_t)rp + (uint32_t)u * 16 * NK, srow + ((uint32_t)u >> sg_shift));
+      load_unit<NK>(w2[k], vals, codes, scales, rs + (uint32_t)u * 16 * NK, srow + ((uint32_t)u >> sg_shift));
     }
     pass(w2);
   }
@@ -218,14 +219,6 @@ hipError_t launch_bv_u(const i4s_packed &w, const uint16_t *x, int32_t batch, ui
   }
 }
 
-// I4S_BV=0 turns the batch-2 VALU kernel off (tuning); read once.
-bool bv_enabled() {
-  static const bool v = [] {
-    const char *e = getenv("I4S_BV");
-    return !(e && e[0] == '0');
-  }();
-  return v;
-}
 }  // namespace
 
 // Measured on MI355X (cold, µs per call, this kernel against the matrix-core
@@ -235,7 +228,7 @@ bool bv_enabled() {
 // 4 the matrix cores win everywhere (5120x5120 b4: 10.2 against 6.7).  So:
 // batch 2, at most 8192 rows, K <= 8192.
 bool gemv_bv_applies(const i4s_packed &w, int32_t batch) {
-  return bv_enabled() && batch == 2 && w.rows <= 8192 && w.cols / kSegCols <= 128;
+  return batch == 2 && w.rows <= 8192 && w.cols / kSegCols <= 128;
 }
 
 hipError_t launch_gemv_bv(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y, hipStream_t stream) {

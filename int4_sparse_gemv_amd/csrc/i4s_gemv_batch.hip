@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       if (moved) {
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-          rstart[r] = (uint32_t)rp[r];
+          rstart[r] = safe_row_start<NK>(rp[r], (uint32_t)(rows - 1) * nnz_row);
           if (has)
             load_unit<NK>(cur[r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
                           srow[r] + ((uint32_t)u >> sg_shift));
@@ -258,7 +258,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 // which lies in one quantization group: the group scale multiplies the fp32
 // tile after the group's last unit (exact, as in the other kernels).  Scales
 // move from the loading lanes to the accumulator lanes through a small
-// wave-private LDS slot.
+// wave-private LDS slot, with a wave-scope synchronisation on each side of
+// the exchange (lanes read what other lanes of the wave wrote, and the slot
+// is rewritten for the next block).  SG = G / 64 is a template parameter:
+// blocks of 4 units start on multiples of 4, so where a group ends inside a
+// block is known at compile time, and the block's scales are read before
+// its matrix steps.
 //
 // A block is one 16-row tile and 8 waves; wave w takes blocks of 4 units
 // w, w+8, ... (a K split inside the block) and reads its B fragments straight
@@ -320,8 +325,9 @@ struct MBlock {
 };
 
 
+template <int SG>
 __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
-    int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
+    int rows, int cols, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
     uint16_t *__restrict__ y) {
@@ -334,9 +340,8 @@ __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
   const int units = cols / kSegCols;
   const int nblk = (units + 3) / 4;
   const uint32_t nnz_row = (uint32_t)cols / 2;
-  const int sg = group_size / kSegCols;
-  const int sg_shift = sg == 1 ? 0 : (sg == 2 ? 1 : 2);
-  const uint32_t ngroups = (uint32_t)(cols / group_size);
+  constexpr int sg_shift = SG == 1 ? 0 : (SG == 2 ? 1 : 2);
+  const uint32_t ngroups = (uint32_t)units >> sg_shift;
 
   // this lane's weight row (clamped: rows past the end re-read the last row)
   const int arow = min(row0 + li, rows - 1);
@@ -370,12 +375,18 @@ __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
     uint32_t W0 = m.v[0], W1 = m.v[1], W2 = m.v[2], W3 = m.v[3], P, Q;
     transpose4(W0, W1, W2, W3);
     transpose_codes(m.c[0], m.c[1], P, Q);
+    wave_lds_sync();  // every lane has read the previous block's scales
     scs[wave][lq][li] = (uint16_t)m.s;  // scale of (row li, unit 4b+lq)
+    wave_lds_sync();  // ... and the other lanes' writes are visible
+    // the scales of the block's groups: rows 4lq..4lq+3 of each group's last unit
+    uint2 sv[4 / SG];
+#pragma unroll
+    for (int g = 0; g < 4 / SG; ++g) sv[g] = *reinterpret_cast<const uint2 *>(&scs[wave][SG * g + SG - 1][4 * lq]);
     f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int u = 4 * b + s;
-      if (u >= units) break;
+      if (u >= units) break;  // units is a multiple of SG: the last unit ends a group
       const u8_t xv = {m.x[2 * s].x, m.x[2 * s].y, m.x[2 * s].z, m.x[2 * s].w,
                        m.x[2 * s + 1].x, m.x[2 * s + 1].y, m.x[2 * s + 1].z, m.x[2 * s + 1].w};
       const h16_t bx = __builtin_bit_cast(h16_t, xv);
@@ -383,12 +394,12 @@ __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
       if (s == 1) cg = smfmac_step<1>(W1, bx, cg, P, Q);
       if (s == 2) cg = smfmac_step<2>(W2, bx, cg, P, Q);
       if (s == 3) cg = smfmac_step<3>(W3, bx, cg, P, Q);
-      if (((u + 1) & (sg - 1)) == 0) {  // the group ends with this unit
-        const uint2 sv = *reinterpret_cast<const uint2 *>(&scs[wave][s][4 * lq]);
-        acc[0] = fmaf(fp16_bits_to_float(sv.x & 0xFFFFu), cg[0], acc[0]);
-        acc[1] = fmaf(fp16_bits_to_float(sv.x >> 16), cg[1], acc[1]);
-        acc[2] = fmaf(fp16_bits_to_float(sv.y & 0xFFFFu), cg[2], acc[2]);
-        acc[3] = fmaf(fp16_bits_to_float(sv.y >> 16), cg[3], acc[3]);
+      if ((s + 1) % SG == 0) {  // the group ends with this unit (4b is a multiple of SG)
+        const uint2 g2 = sv[s / SG];
+        acc[0] = fmaf(fp16_bits_to_float(g2.x & 0xFFFFu), cg[0], acc[0]);
+        acc[1] = fmaf(fp16_bits_to_float(g2.x >> 16), cg[1], acc[1]);
+        acc[2] = fmaf(fp16_bits_to_float(g2.y & 0xFFFFu), cg[2], acc[2]);
+        acc[3] = fmaf(fp16_bits_to_float(g2.y >> 16), cg[3], acc[3]);
         cg = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
@@ -400,7 +411,7 @@ __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
     load(ma, b);
     const int32_t rp = row_ptr[arow];
     if ((uint32_t)rp != rstart) {  // a row stored elsewhere: re-fetch from row_ptr's offset
-      rstart = (uint32_t)rp;
+      rstart = safe_row_start<2>(rp, (uint32_t)(rows - 1) * nnz_row);
       load(ma, b);
     }
   }
@@ -489,7 +500,6 @@ __global__ __launch_bounds__(64 * kSWaves) void gemv_smfmac_split_kernel(
   const int xst = ups * kSegCols + 8;  // halfs per vector in LDS (16-byte pad)
   const uint32_t nnz_row = (uint32_t)units * 32;
   const uint32_t ngroups = (uint32_t)units >> sg_shift;
-  const int sgm = (1 << sg_shift) - 1;  // a group ends with unit u when ((u + 1) & sgm) == 0
 
   // 1. the activation slice: vector 2r + (tid / 256), piece tid % 256 (16 B)
   const int vpb = (u1 - u0) * (kSegCols / 8);  // pieces per vector, <= 256
@@ -561,17 +571,28 @@ __global__ __launch_bounds__(64 * kSWaves) void gemv_smfmac_split_kernel(
   f4_t acc[kSTiles];
 #pragma unroll
   for (int t = 0; t < kSTiles; ++t) acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // Each unit's product tile is scaled on its own (a unit lies in one
+  // quantization group): no group test between the matrix steps, so G does
+  // not enter the kernel's control flow.  The scales pass from the loading
+  // lanes to the accumulator lanes through the wave's LDS slot, with a
+  // wave-scope synchronisation on each side of the exchange.
   auto process = [&](const WBlock (&m)[kSTiles], int b) {
     uint32_t W[kSTiles][4], P[kSTiles], Q[kSTiles];
-    f4_t cg[kSTiles];
 #pragma unroll
     for (int t = 0; t < kSTiles; ++t) {
       W[t][0] = m[t].v[0]; W[t][1] = m[t].v[1]; W[t][2] = m[t].v[2]; W[t][3] = m[t].v[3];
       transpose4(W[t][0], W[t][1], W[t][2], W[t][3]);
       transpose_codes(m[t].c[0], m[t].c[1], P[t], Q[t]);
-      scs[wave][t][lq][li] = (uint16_t)m[t].s;
-      cg[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    wave_lds_sync();  // every lane has read the previous block's scales
+#pragma unroll
+    for (int t = 0; t < kSTiles; ++t) scs[wave][t][lq][li] = (uint16_t)m[t].s;
+    wave_lds_sync();  // ... and the other lanes' writes are visible
+    uint2 sv[kSTiles][4];  // rows 4lq..4lq+3 of units 4b..4b+3
+#pragma unroll
+    for (int t = 0; t < kSTiles; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sv[t][s] = *reinterpret_cast<const uint2 *>(&scs[wave][t][s][4 * lq]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int u = 4 * b + s;
@@ -582,21 +603,17 @@ __global__ __launch_bounds__(64 * kSWaves) void gemv_smfmac_split_kernel(
       const h16_t bx = __builtin_bit_cast(h16_t, xv);
 #pragma unroll
       for (int t = 0; t < kSTiles; ++t) {
-        if (s == 0) cg[t] = smfmac_step<0>(W[t][0], bx, cg[t], P[t], Q[t]);
-        if (s == 1) cg[t] = smfmac_step<1>(W[t][1], bx, cg[t], P[t], Q[t]);
-        if (s == 2) cg[t] = smfmac_step<2>(W[t][2], bx, cg[t], P[t], Q[t]);
-        if (s == 3) cg[t] = smfmac_step<3>(W[t][3], bx, cg[t], P[t], Q[t]);
-      }
-      if (((s + 1) & sgm) == 0) {  // the group ends with this unit (slices start on 4-unit bounds)
-#pragma unroll
-        for (int t = 0; t < kSTiles; ++t) {
-          const uint2 sv = *reinterpret_cast<const uint2 *>(&scs[wave][t][s][4 * lq]);
-          acc[t][0] = fmaf(fp16_bits_to_float(sv.x & 0xFFFFu), cg[t][0], acc[t][0]);
-          acc[t][1] = fmaf(fp16_bits_to_float(sv.x >> 16), cg[t][1], acc[t][1]);
-          acc[t][2] = fmaf(fp16_bits_to_float(sv.y & 0xFFFFu), cg[t][2], acc[t][2]);
-          acc[t][3] = fmaf(fp16_bits_to_float(sv.y >> 16), cg[t][3], acc[t][3]);
-          cg[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
+        const f4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+        f4_t cg;
+        if (s == 0) cg = smfmac_step<0>(W[t][0], bx, z, P[t], Q[t]);
+        if (s == 1) cg = smfmac_step<1>(W[t][1], bx, z, P[t], Q[t]);
+        if (s == 2) cg = smfmac_step<2>(W[t][2], bx, z, P[t], Q[t]);
+        if (s == 3) cg = smfmac_step<3>(W[t][3], bx, z, P[t], Q[t]);
+        const uint2 g2 = sv[t][s];
+        acc[t][0] = fmaf(fp16_bits_to_float(g2.x & 0xFFFFu), cg[0], acc[t][0]);
+        acc[t][1] = fmaf(fp16_bits_to_float(g2.x >> 16), cg[1], acc[t][1]);
+        acc[t][2] = fmaf(fp16_bits_to_float(g2.y & 0xFFFFu), cg[2], acc[t][2]);
+        acc[t][3] = fmaf(fp16_bits_to_float(g2.y >> 16), cg[3], acc[t][3]);
       }
     }
   };
@@ -617,7 +634,7 @@ __global__ __launch_bounds__(64 * kSWaves) void gemv_smfmac_split_kernel(
   if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
     for (int t = 0; t < kSTiles; ++t) {
-      rstart[t] = (uint32_t)rp[t];
+      rstart[t] = safe_row_start<2>(rp[t], (uint32_t)(rows - 1) * nnz_row);
       acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
 #pragma unroll
@@ -873,6 +890,14 @@ __device__ __forceinline__ void rows_body(
       // path and stay where they were issued; and there is no branch (even a
       // wave-uniform one here split the body and made the compiler spill).
       const bool unit_ok = (wave * CPW + c) * U + lu < units;
+      // The area is the wave's own, written in the load layout and read back
+      // by other lanes of the wave in the matrix layout: a wave-scope
+      // synchronisation before the writes of every chunk after the first
+      // (the previous chunk's reads are done) and after the writes (they are
+      // visible).  The first chunk's area has not been read yet, and a
+      // synchronisation there would also keep the compiler from issuing the
+      // last weight and activation loads between the first LDS writes.
+      if (c > 0) wave_lds_sync();
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         vals_t *lv = lv_of(t);
@@ -885,6 +910,7 @@ __device__ __forceinline__ void rows_body(
           lsc[lu * 16 + RL * k + lr] = unit_ok ? wsc[t][k] : (uint16_t)0;
         }
       }
+      wave_lds_sync();
       if (c + 1 < CPW) {
         __builtin_amdgcn_sched_barrier(0);
         load_chunk(c + 1);
@@ -990,7 +1016,7 @@ __device__ __forceinline__ void rows_body(
     for (int t = 0; t < TPW; ++t) {
       for (int r = 0; r < 4; ++r) {
         const int row = min(row0 + 16 * t + 4 * lq + r, rows - 1);
-        const uint32_t rs = (uint32_t)row_ptr[row];
+        const uint32_t rs = safe_row_start<NK>(row_ptr[row], (uint32_t)(rows - 1) * nnz_row);
         float sum = 0.0f;
         for (int c = 0; c < CPW; ++c) {
           for (int uu = 0; uu < U; ++uu) {
@@ -1015,8 +1041,9 @@ __device__ __forceinline__ void rows_body(
     }
   }
 
-  // sum the waves' partial tiles (each wave writes into its own area, which
-  // it no longer reads) and store y
+  // sum the waves' partial tiles (each wave writes into its own area, once
+  // all its lanes are done reading it) and store y
+  wave_lds_sync();
   f4_t *red = reinterpret_cast<f4_t *>(wl);
 #pragma unroll
   for (int t = 0; t < TPW; ++t) red[64 * t + lane] = acc[t];
@@ -1036,8 +1063,18 @@ __device__ __forceinline__ void rows_body(
   }
 }
 
+// Waves per SIMD the compiler must leave room for: the one-chunk two-tile
+// 2:4 form runs two 8-wave blocks per CU only at <= 128 VGPRs (4 waves per
+// SIMD); at 129 or more the blocks of a layer run one after the other.
+template <int NK, int CPW, int TPW, int U>
+constexpr int rows_min_waves() {
+  return (NK == 2 && CPW == 1 && TPW == 2 && U == 16) ? 4 : 1;
+}
+
 template <int NK, int CPW, int SG, int TPW, int U>
-__global__ __launch_bounds__(64 * (TPW == 4 ? 12 : RowsGeom<U>::kMaxWaves)) void gemv_smfmac_rows_kernel(
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 64 * (TPW == 4 ? 12 : RowsGeom<U>::kMaxWaves)),
+                          amdgpu_waves_per_eu(rows_min_waves<NK, CPW, TPW, U>())))
+void gemv_smfmac_rows_kernel(
     int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
@@ -1050,7 +1087,9 @@ __global__ __launch_bounds__(64 * (TPW == 4 ? 12 : RowsGeom<U>::kMaxWaves)) void
 // finds its layer from the cumulative block counts and runs the single-layer
 // body on it.
 template <int NK, int CPW, int SG, int TPW, int U>
-__global__ __launch_bounds__(64 * (TPW == 4 ? 12 : RowsGeom<U>::kMaxWaves)) void gemv_smfmac_rows_multi_kernel(
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 64 * (TPW == 4 ? 12 : RowsGeom<U>::kMaxWaves)),
+                          amdgpu_waves_per_eu(rows_min_waves<NK, CPW, TPW, U>())))
+void gemv_smfmac_rows_multi_kernel(
     int units, const uint16_t *__restrict__ x, int batch, MultiDesc d) {
   extern __shared__ __align__(16) uint8_t lds[];  // [waves][TPW][RowsGeom<U>::kTileLds]
   int m = 0;
@@ -1078,15 +1117,6 @@ hipError_t launch_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint1
   return hipGetLastError();
 }
 
-// I4S_ROWS_KERNEL=0 keeps the older tile kernel (tuning and cross-checks)
-bool rows_kernel_enabled() {
-  static const bool v = [] {
-    const char *e = getenv("I4S_ROWS_KERNEL");
-    return !(e && e[0] == '0');
-  }();
-  return v;
-}
-
 // The rows kernel covers up to 8 waves of 1, 2 or 4 chunks: K <= 32768.
 bool rows_kernel_fits(const i4s_packed &w) {
   const int chunks = (w.cols / kSegCols + kRUnits - 1) / kRUnits;
@@ -1098,8 +1128,7 @@ bool rows_kernel_fits(const i4s_packed &w) {
 // one tile per wave keeps twice the blocks for layers with few rows.
 // Measured on MI355X: two tiles win from 320 tiles up (5120 rows: 7.7 / 8.0 /
 // 8.8 us against 7.8 / 9.0 / 12.3 at batch 4 / 8 / 16), one tile wins at 256
-// (4096 rows, 1:4: 5.2 / 5.5 / 6.7 against 6.9 / 7.1 / 7.9).  I4S_ROWS_TPW=1
-// or 2 forces the choice (tuning); read once.
+// (4096 rows, 1:4: 5.2 / 5.5 / 6.7 against 6.9 / 7.1 / 7.9).
 struct RowsShape {
   int u, cpw, waves, tpw;
   size_t lds;
@@ -1110,19 +1139,9 @@ struct RowsShape {
 // two-tile blocks are fewer than the compute units and the batch is at most
 // 8.  Measured: 5120x5120 at batch 4 / 8 / 16: 7.45 / 7.76 / 8.90 us with 16,
 // 6.63 / 7.32 / 9.01 with 8; 13824x5120 (432 blocks): 10.8 / 11.5 / 14.4 with
-// 16, 11.6 / 12.9 / 16.5 with 8.  I4S_ROWS_UNITS=8 or 16 forces it (tuning).
+// 16, 11.6 / 12.9 / 16.5 with 8.
 // want_u (8 or 16) fixes the chunk width; 0 chooses it.
 RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want_u = 0) {
-  static const int forced_tpw = [] {
-    const char *e = getenv("I4S_ROWS_TPW");
-    const int v = e ? atoi(e) : 0;
-    return (v == 1 || v == 2 || v == 4) ? v : 0;
-  }();
-  static const int forced_u = [] {
-    const char *e = getenv("I4S_ROWS_UNITS");
-    const int v = e ? atoi(e) : 0;
-    return (v == 8 || v == 16) ? v : 0;
-  }();
   RowsShape r;
   // Four tiles per wave (8-unit chunks, one per wave) for batches above 8
   // on tall layers: each B fragment then feeds four tiles, halving the
@@ -1134,22 +1153,15 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
   const int tile8 = n_keep == 1 ? RowsGeom<8, 1>::kTileLds : RowsGeom<8>::kTileLds;
   const bool four = n_keep != 4 && batch > 8 && total_tiles >= 640 && want_u != 16 &&
                     (size_t)((units + 7) / 8) * 4 * tile8 <= 160 * 1024;
-  r.tpw = forced_tpw ? forced_tpw : (four ? 4 : (total_tiles >= 300 ? 2 : 1));
-  r.u = forced_u ? forced_u : (((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) || r.tpw == 4) ? 8 : 16);
+  r.tpw = four ? 4 : (total_tiles >= 300 ? 2 : 1);
+  r.u = ((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) || r.tpw == 4) ? 8 : 16;
   if (want_u) r.u = want_u;
   // 8-unit chunks only with one chunk per wave (K <= 8192): two chunks per
   // wave of the 16-wave form would not fit its 128 registers
   if ((units + 7) / 8 > RowsGeom<8>::kMaxWaves) r.u = 16;
-  static const int forced_cpw = [] {
-    const char *e = getenv("I4S_ROWS_CPW");
-    const int v = e ? atoi(e) : 0;
-    return (v == 1 || v == 2 || v == 4) ? v : 0;
-  }();
-  if (forced_cpw >= 2) r.u = 16;  // the 8-unit form has one chunk per wave
   const int maxw = r.u == 8 ? RowsGeom<8>::kMaxWaves : RowsGeom<16>::kMaxWaves;
   const int chunks = (units + r.u - 1) / r.u;
   r.cpw = chunks > 2 * maxw ? 4 : (chunks > maxw ? 2 : 1);
-  if (forced_cpw > r.cpw) r.cpw = forced_cpw;
   // dense rows are twice the bytes: two chunks of two tiles would spill; four
   // chunks per wave (K > 16384) always take one tile per wave
   if ((n_keep == 4 && r.cpw == 2) || r.cpw == 4) r.tpw = 1;
@@ -1273,10 +1285,17 @@ hipError_t launch_rows_multi(const i4s_packed *w, int32_t n, const uint16_t *x, 
 
 hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                          hipStream_t stream) {
-  if (rows_kernel_enabled() && rows_kernel_fits(w)) return launch_rows<2>(w, x, batch, y, stream);
+  if (rows_kernel_fits(w)) return launch_rows<2>(w, x, batch, y, stream);
   const dim3 grid((unsigned)((w.rows + 15) / 16)), block(64 * kMWaves);
-  hipLaunchKernelGGL(gemv_smfmac_kernel, grid, block, 0, stream, w.rows, w.cols, w.group_size, w.row_ptr,
-                     w.vals, w.codes, w.scales, x, batch, y);
+  if (w.group_size == 64)
+    hipLaunchKernelGGL(gemv_smfmac_kernel<1>, grid, block, 0, stream, w.rows, w.cols, w.row_ptr, w.vals,
+                       w.codes, w.scales, x, batch, y);
+  else if (w.group_size == 128)
+    hipLaunchKernelGGL(gemv_smfmac_kernel<2>, grid, block, 0, stream, w.rows, w.cols, w.row_ptr, w.vals,
+                       w.codes, w.scales, x, batch, y);
+  else
+    hipLaunchKernelGGL(gemv_smfmac_kernel<4>, grid, block, 0, stream, w.rows, w.cols, w.row_ptr, w.vals,
+                       w.codes, w.scales, x, batch, y);
   return hipGetLastError();
 }
 
@@ -1321,16 +1340,6 @@ hipError_t launch_smfmac_split(const i4s_packed &w, const uint16_t *x, int32_t b
   }
 }
 
-// I4S_BATCH_PATH=valu forces the VALU batch kernel for 2:4 and 1:4 (tuning
-// and cross-checks); read once.
-bool smfmac_enabled() {
-  static const bool v = [] {
-    const char *e = getenv("I4S_BATCH_PATH");
-    return !(e && e[0] == 'v');
-  }();
-  return v;
-}
-
 template <int NK>
 hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                      hipStream_t stream) {
@@ -1338,10 +1347,10 @@ hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint
     const hipError_t e = launch_gemv_bv(w, x, batch, y, stream);
     if (e != hipErrorNotSupported) return e;
   }
-  if (NK == 2 && batch >= 2 && smfmac_enabled()) {
+  if (NK == 2 && batch >= 2) {
     return launch_smfmac(w, x, batch, y, stream);
   }
-  if ((NK == 1 || NK == 4) && batch >= 2 && smfmac_enabled() && rows_kernel_enabled() && rows_kernel_fits(w)) {
+  if ((NK == 1 || NK == 4) && batch >= 2 && rows_kernel_fits(w)) {
     return launch_rows<NK>(w, x, batch, y, stream);
   }
   if (batch <= 1) {
@@ -1380,16 +1389,9 @@ SplitPlan split_plan(const i4s_packed &w, int32_t batch) {
   // with four chunks per wave (K > 16384), hot, us at b4 / b8 / b16:
   // 4096x28672 rows 17.4 / 20.8 / 29.9 against split 23.3 / 23.1 / 24.7,
   // 8192x20480 rows 25.5 / 30.6 / 43.3 against split 47.3 / 47.5 / 46.6.
-  // The rows kernel needs no workspace and no second launch.  I4S_SPLIT=0 /
-  // 1 forces the split off or on (tuning and cross-checks).
-  static const int split_env = [] {
-    const char *e = getenv("I4S_SPLIT");
-    return e ? (e[0] == '0' ? 0 : 1) : -1;
-  }();
-  const bool wanted =
-      split_env >= 0 ? split_env == 1
-                     : (units > 4 * kRMaxWaves * kRUnits ||
-                        (units > 2 * kRMaxWaves * kRUnits && batch > 8 && w.rows <= 4096));
+  // The rows kernel needs no workspace and no second launch.
+  const bool wanted = units > 4 * kRMaxWaves * kRUnits ||
+                      (units > 2 * kRMaxWaves * kRUnits && batch > 8 && w.rows <= 4096);
   if (!wanted) return SplitPlan{};
   if (pl.ksplit > 1) pl.partial_bytes = (size_t)pl.ksplit * pl.row_groups * kSWaves * kSTiles * 64 * sizeof(f4_t);
   pl.workspace_bytes = pl.partial_bytes;
@@ -1398,7 +1400,7 @@ SplitPlan split_plan(const i4s_packed &w, int32_t batch) {
 
 hipError_t launch_gemv_ws(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                           const SplitPlan &pl, void *workspace, hipStream_t stream) {
-  if (pl.ksplit >= 1 && smfmac_enabled()) return launch_smfmac_split(w, x, batch, y, pl, workspace, stream);
+  if (pl.ksplit >= 1) return launch_smfmac_split(w, x, batch, y, pl, workspace, stream);
   return launch_gemv(w, x, batch, y, stream);
 }
 
@@ -1425,7 +1427,7 @@ hipError_t launch_gemv_multi(const i4s_packed *w, int32_t n, const uint16_t *x, 
     if (batch == 1) {
       const hipError_t e = launch_gemv_b1_multi(w, n, x, y, stream);
       if (e != hipErrorNotSupported) return e;
-    } else if (!valu_b2 && smfmac_enabled() && rows_kernel_enabled() && rows_kernel_fits(w[0])) {
+    } else if (!valu_b2 && rows_kernel_fits(w[0])) {
       const hipError_t e = w[0].n_keep == 2   ? launch_rows_multi<2>(w, n, x, batch, y, stream)
                            : w[0].n_keep == 1 ? launch_rows_multi<1>(w, n, x, batch, y, stream)
                                               : launch_rows_multi<4>(w, n, x, batch, y, stream);

@@ -17,8 +17,6 @@
 // four lane reads (no LDS traffic).
 #pragma once
 
-#include <stdlib.h>
-
 #include "i4s_internal.h"
 
 namespace i4s {
@@ -188,6 +186,34 @@ __device__ inline void init_tables(uint32_t *lut) {
   } else if constexpr (NK == 1) {
     if (threadIdx.x < 16) init_single_table(lut);
   }
+}
+
+// A row start read from row_ptr, made safe to use as an offset: clamped to
+// [0, last_start] (last_start = (rows - 1) * nnz_row, the start of the last
+// row) and aligned down to a whole 64-column unit (16 * NK elements).  A
+// descriptor that meets the documented precondition passes unchanged; one
+// that does not reads inside the buffers (and gives unspecified values)
+// instead of reading out of bounds.  Used only on the rare path of a row
+// stored away from the format's offset.
+template <int NK>
+__device__ inline uint32_t safe_row_start(int32_t rp, uint32_t last_start) {
+  const uint32_t v = rp < 0 ? 0u : (uint32_t)rp;
+  return (v < last_start ? v : last_start) & ~(16u * NK - 1u);
+}
+
+// Orders the LDS accesses of one wave around an exchange between its own
+// lanes (a lane writes, other lanes of the same wave read, or the area is
+// rewritten after such reads): everything a lane wrote before it is seen by
+// every lane of the wave after it, and no LDS access of the wave moves
+// across it.  Wavefront-scope fences restricted to LDS around a wave
+// barrier.  A wave's LDS operations complete in program order, so on this
+// ISA it emits no instruction; what it adds is that the compiler may no
+// longer move the accesses of different lanes past one another, which the
+// language otherwise allows for accesses that race between lanes.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
 // Block barrier that orders LDS only: the fences are restricted to the local
