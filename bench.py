@@ -7,17 +7,26 @@ offline work); its time is reported separately as ``pack_ms``.
 
 Cold (the headline): the packed layer is copied P = ceil(1 GiB / packed
 bytes) times (byte-identical device copies, > 4x the 256 MB last-level
-cache) and the steps visit the copies round-robin, so every call streams its
-weights from HBM.  Hot (reported, labelled cache-resident): one copy.  The K
-timed steps are captured once into a HIP graph and replayed, so host launch
-overhead does not pace the GPU; the graph holds exactly K launches.  The
-timed replay is bracketed by torch.cuda.synchronize() and by HIP events on
-the stream the kernels run on.
+cache) and the steps visit the copies round-robin; before every timed trial
+an untimed 512 MiB read evicts the caches, so no copy is still cached when a
+trial starts, whatever the step count.  Hot (reported, labelled
+cache-resident): one copy, no eviction.
+
+Timing: the K timed steps are captured once into a HIP graph.  A trial
+enqueues, on one stream, (the eviction read), a bounded delay kernel, event
+e0, one replay of the graph, event e1.  The delay keeps the GPU busy while the
+host submits the graph, so e0..e1 spans exactly the K calls running back to
+back and not the host's launch of the graph.  Per call = (e1 - e0) / K; the
+median over trials is reported, and ``value``, ``ms_per_step``,
+``pct_of_peak`` and ``roofline`` all come from that one figure.  Wall time
+around each trial (torch.cuda.synchronize() on both sides) is reported as
+well.
 
 Prints ONE JSON line for the 4096x4096 2:4 G128 batch-1 layer.  ``value`` is
 packed bytes per call / seconds per call (GB/s, decimal) in cold mode.
 ``--suite FILE`` additionally measures every workload (all matrices and
-batch sizes, and the 224-call 7B stack in layer order) and writes a table.
+batch sizes, each batch-1 layer next to a read-only launch of its own bytes,
+the 224-call 7B stacks per layer and per pass) and writes a table.
 """
 
 from __future__ import annotations
@@ -36,9 +45,16 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD specification
 METRIC = "µs/call and effective HBM GB/s (% of peak) of packed INT4 SparseGEMV, 4096×4096 b=1"
-# the batch-1 kernel's sources: a traffic profile is used only while they are unchanged
-B1_SRCS = [os.path.join(ROOT, "int4_sparse_gemv_amd", "csrc", f) for f in ("i4s_gemv_b1.hip", "i4s_gemv_common.h")]
+CSRC = os.path.join(ROOT, "int4_sparse_gemv_amd", "csrc")
+# the batch-1 kernel's sources: a profile is used only while they are unchanged
+B1_SRCS = [os.path.join(CSRC, f) for f in ("i4s_gemv_b1.hip", "i4s_gemv_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_c2_4096.json")
+KTIME_FILE = os.path.join(ROOT, "profiles", "kernel_time_gemv_c2_4096.json")
+FLUSH_BYTES = 512 << 20  # > 2x the last-level cache
+# read-only launch shapes tried for the floor: (16-byte loads per lane,
+# threads per block, blocks; 0 = one block per slab of the data)
+FLOOR_SHAPES = [(v, t, 0) for t in (256, 512, 1024) for v in (1, 2, 4, 8)] + \
+               [(4, 512, 256), (4, 512, 512), (2, 1024, 256), (8, 256, 1024), (2, 512, 1024)]
 
 
 def parse():
@@ -54,9 +70,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (PMC traffic calibration)")
-    ap.add_argument("--eager", action="store_true", help="time plain stream launches instead of a graph")
     ap.add_argument("--suite", default=None, help="also measure every workload and write a table here")
-    ap.add_argument("--no-stack", action="store_true", help="with --suite: skip the 224-matrix 7B stack")
+    ap.add_argument("--no-stack", action="store_true", help="with --suite: skip the 224-matrix 7B stacks")
     ap.add_argument("--only", default=None, help="with --suite: comma-separated workloads to measure")
     ap.add_argument("--suite-steps", type=int, default=1000, help="with --suite: timed calls per layer and trial")
     ap.add_argument("--no-floors", action="store_true",
@@ -72,6 +87,10 @@ def sha_of(paths):
     return h.hexdigest()[:16]
 
 
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
 class Runner:
     """Packs layers and times graph-captured sequences of i4s_run calls."""
 
@@ -79,12 +98,28 @@ class Runner:
         import torch
         import int4_sparse_gemv_amd as I
         from int4_sparse_gemv_amd import _binding as B
+        from int4_sparse_gemv_amd import build as BLD
         self.torch, self.I, self.B, self.args = torch, I, B, args
         self.lib = B.load()
         self.dev = torch.device("cuda:0")
         torch.cuda.set_device(self.dev)
         self.stream = torch.cuda.current_stream(self.dev)
         self.keep = []
+        f = ctypes.CDLL(BLD.FLOOR_LIB)
+        f.i4sf_stream_read.restype = ctypes.c_int
+        f.i4sf_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        f.i4sf_stream_read_shape.restype = ctypes.c_int
+        f.i4sf_stream_read_shape.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        f.i4sf_chase.restype = ctypes.c_int
+        f.i4sf_chase.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+        f.i4sf_delay.restype = ctypes.c_int
+        f.i4sf_delay.argtypes = [ctypes.c_uint32, ctypes.c_void_p]
+        self.floor = f
+        self.sink = torch.zeros(16, dtype=torch.int32, device=self.dev)
+        self.flush_buf = torch.full((FLUSH_BYTES,), 0x5A, dtype=torch.uint8, device=self.dev)
 
     def to_dev(self, a16):
         import numpy as np
@@ -121,60 +156,70 @@ class Runner:
         self.keep.append(ws)
         return [(d, xp, b, yp, ws.data_ptr() if n else None, ws.numel()) for d, xp, b, yp, n in out]
 
-    def timed(self, seq, steps, warmup, trials):
-        """Median (wall ms per step, event ms per step) over trials; seq is visited round-robin.
+    def evict(self):
+        """One untimed read of FLUSH_BYTES: afterwards no earlier data is cached."""
+        st = self.floor.i4sf_stream_read(self.flush_buf.data_ptr(), FLUSH_BYTES, 0, self.sink.data_ptr(),
+                                         self.stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"i4sf_stream_read returned {st}")
 
-        An item of seq is an i4s_run_ws argument tuple or a callable taking
-        the stream handle and returning a status."""
-        import numpy as np
+    def capture(self, seq, n):
+        """A HIP graph of n calls visiting seq round-robin.  An item of seq is
+        an i4s_run_ws argument tuple or a callable taking the stream handle
+        and returning a status."""
         torch, run_ws = self.torch, self.lib.i4s_run_ws
-
-        def run(item, sh):
-            return item(sh) if callable(item) else run_ws(*item, sh)
-        walls, evs = [], []
-        if self.args.eager:
-            sh = self.stream.cuda_stream
-            for i in range(warmup):
-                assert run(seq[i % len(seq)], sh) == 0
-            for _ in range(trials):
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                t = time.perf_counter()
-                e0.record(self.stream)
-                for i in range(steps):
-                    run(seq[i % len(seq)], sh)
-                e1.record(self.stream)
-                torch.cuda.synchronize()
-                walls.append((time.perf_counter() - t) * 1e3 / steps)
-                evs.append(e0.elapsed_time(e1) / steps)
-            return float(np.median(walls)), float(np.median(evs))
         cap = torch.cuda.Stream(self.dev)
-        graphs = []
-        for n in (warmup, steps):
-            g = torch.cuda.CUDAGraph()
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g, stream=cap):
-                for i in range(n):
-                    st = run(seq[i % len(seq)], cap.cuda_stream)
-                    if st != 0:
-                        raise self.B.I4SError(st, "i4s_run")
-            graphs.append(g)
-        g_warm, g = graphs
-        for _ in range(trials):
-            g_warm.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t = time.perf_counter()
-            e0.record(self.stream)
-            g.replay()
-            e1.record(self.stream)
-            torch.cuda.synchronize()
-            walls.append((time.perf_counter() - t) * 1e3 / steps)
-            evs.append(e0.elapsed_time(e1) / steps)
-        del graphs, g, g_warm
-        return float(np.median(walls)), float(np.median(evs))
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(n):
+                item = seq[i % len(seq)]
+                st = item(cap.cuda_stream) if callable(item) else run_ws(*item, cap.cuda_stream)
+                if st != 0:
+                    raise self.B.I4SError(st, "i4s_run")
+        return g
 
-    def launch_floor_us(self, steps=2000):
+    def replay_timed(self, g, steps, evict):
+        """One trial: (eviction), delay, e0, replay, e1.  Returns (device ms
+        per step, wall ms per step, whether the host finished submitting the
+        graph before the delay ended)."""
+        torch = self.torch
+        delay_us = min(100000, 1000 + 5 * steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if evict:
+            self.evict()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t1 = time.perf_counter()
+        st = self.floor.i4sf_delay(delay_us, self.stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"i4sf_delay returned {st}")
+        e0.record(self.stream)
+        g.replay()
+        e1.record(self.stream)
+        submit_us = (time.perf_counter() - t1) * 1e6
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        return e0.elapsed_time(e1) / steps, wall / steps, submit_us < 0.8 * delay_us
+
+    def timed(self, seq, steps, warmup, trials, evict):
+        """Median over trials of the device time per call (ms) of `steps`
+        calls visiting seq round-robin, plus the per-trial figures."""
+        import numpy as np
+        g_warm = self.capture(seq, max(1, warmup))
+        g = self.capture(seq, steps)
+        g_warm.replay()
+        evs, walls, oks = [], [], []
+        for _ in range(trials):
+            ev, wall, ok = self.replay_timed(g, steps, evict)
+            evs.append(ev)
+            walls.append(wall)
+            oks.append(ok)
+        del g, g_warm
+        return {"ms": float(np.median(evs)), "wall_ms": float(np.median(walls)), "trials_ms": evs,
+                "queued": all(oks)}
+
+    def launch_floor_us(self, steps=2000, trials=3):
         """Per-launch time of a one-element fill kernel replayed the same way (the dispatch floor)."""
         import numpy as np
         torch = self.torch
@@ -185,67 +230,36 @@ class Runner:
         with torch.cuda.graph(g, stream=cap):
             for _ in range(steps):
                 t.fill_(1.0)
-        res = []
-        for _ in range(3):
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(self.stream)
-            g.replay()
-            e1.record(self.stream)
-            torch.cuda.synchronize()
-            res.append(e0.elapsed_time(e1) * 1e3 / steps)
+        g.replay()
+        res = [self.replay_timed(g, steps, False)[0] * 1e3 for _ in range(trials)]
         return float(np.median(res))
 
-    def floors(self, nbytes, steps=2000, trials=3):
-        """What one launch can reach at this size on this part, timed like the GEMV.
-
-        stream_read_*: a kernel that only reads nbytes once (libi4s_floor.so,
-        one 16-byte load per lane), cold over >= 1.5 GB of copies and hot;
-        load_latency_ns: one lane chasing 4000 dependent loads through a random
-        cycle spread over 2 GiB (one entry per KiB)."""
-        import numpy as np
-        from int4_sparse_gemv_amd import build as BLD
+    def read_floor(self, nbytes, shapes, steps=2000, trials=3):
+        """Cold and hot per-launch time (us) of read-only launches of nbytes
+        for each shape (vpl, threads, blocks), timed like the GEMV."""
         torch = self.torch
-        lib = ctypes.CDLL(BLD.FLOOR_LIB)
-        lib.i4sf_stream_read.restype = ctypes.c_int
-        lib.i4sf_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p,
-                                         ctypes.c_void_p]
-        lib.i4sf_chase.restype = ctypes.c_int
-        lib.i4sf_chase.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p,
-                                   ctypes.c_void_p]
         nb = nbytes // 16 * 16
-        sink = torch.zeros(16, dtype=torch.int32, device=self.dev)
-        copies = max(4, math.ceil(1.5 * (1 << 30) / nb))
+        copies = max(4, math.ceil((1 << 30) / nb))
         bufs = [torch.full((nb,), 0x5A, dtype=torch.uint8, device=self.dev) for _ in range(copies)]
-
-        def timed_reads(nbuf, nt):
-            cap = torch.cuda.Stream(self.dev)
-            g = torch.cuda.CUDAGraph()
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g, stream=cap):
-                for i in range(steps):
-                    st = lib.i4sf_stream_read(bufs[i % nbuf].data_ptr(), nb, nt, sink.data_ptr(), cap.cuda_stream)
-                    if st != 0:
-                        raise RuntimeError(f"i4sf_stream_read returned {st}")
-            res = []
-            for _ in range(trials):
-                g.replay()
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(self.stream)
-                g.replay()
-                e1.record(self.stream)
-                torch.cuda.synchronize()
-                res.append(e0.elapsed_time(e1) * 1e3 / steps)
-            del g
-            return float(np.median(res))
-
-        out = {"bytes": nb, "copies": copies,
-               "stream_read_cold_us": {"nontemporal": timed_reads(copies, 1), "plain": timed_reads(copies, 0)},
-               "stream_read_hot_us": timed_reads(1, 0)}
+        out = []
+        for vpl, threads, blocks in shapes:
+            def item(i):
+                buf = bufs[i % copies]
+                return lambda sh, buf=buf: self.floor.i4sf_stream_read_shape(
+                    buf.data_ptr(), nb, vpl, threads, blocks, self.sink.data_ptr(), sh)
+            cold = self.timed([item(i) for i in range(copies)], steps, 20, trials, True)
+            hot = self.timed([item(0)], steps, 20, trials, False)
+            out.append({"vpl": vpl, "threads": threads, "blocks": blocks,
+                        "cold_us": round(cold["ms"] * 1e3, 4), "hot_us": round(hot["ms"] * 1e3, 4)})
         del bufs
-        # pointer chase: a single random cycle through M entries 1 KiB apart
+        torch.cuda.empty_cache()
+        return out
+
+    def latency_ns(self, trials=3):
+        """One lane chasing 4000 dependent loads through a random cycle spread
+        over 2 GiB (one entry per KiB)."""
+        import numpy as np
+        torch = self.torch
         M, spacing, hops = 1 << 21, 256, 4000
         gen = torch.Generator(device=self.dev)
         gen.manual_seed(0)
@@ -258,7 +272,7 @@ class Runner:
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(self.stream)
-            st = lib.i4sf_chase(nxt.data_ptr(), nxt.numel(), hops, outv.data_ptr(), self.stream.cuda_stream)
+            st = self.floor.i4sf_chase(nxt.data_ptr(), nxt.numel(), hops, outv.data_ptr(), self.stream.cuda_stream)
             e1.record(self.stream)
             torch.cuda.synchronize()
             if st != 0:
@@ -268,10 +282,9 @@ class Runner:
         expect = int(order[(k0 + hops) % M]) * spacing
         if int(outv.item()) != expect:
             raise RuntimeError(f"pointer chase ended at {int(outv.item())}, expected {expect}")
-        out["load_latency_ns"] = float(np.median(lat))
         del nxt, order
         torch.cuda.empty_cache()
-        return out
+        return float(np.median(lat))
 
     def measure_layer(self, m, batch, steps, warmup, trials):
         """Cold and hot timing of one matrix at one batch size."""
@@ -285,27 +298,25 @@ class Runner:
         n_cold = max(1, math.ceil((1 << 30) / nbytes))
         cps = [p] + [self.clone(p) for _ in range(n_cold - 1)]
         seq = self.calls([(c, x, y, batch) for c in cps])
-        cold_wall, cold_ev = self.timed(seq, steps, warmup, trials)
-        hot_wall, hot_ev = self.timed(seq[:1], steps, warmup, trials)
+        cold = self.timed(seq, steps, warmup, trials, True)
+        hot = self.timed(seq[:1], steps, warmup, trials, False)
         del cps, seq
         self.keep.clear()
         torch.cuda.empty_cache()
         flops = 2 * (p.nnz) * batch
+        cold_us, hot_us = cold["ms"] * 1e3, hot["ms"] * 1e3
         return {"matrix": m.name, "rows": m.rows, "cols": m.cols, "n_keep": m.n_keep, "group_size": p.group_size,
                 "batch": batch, "packed_bytes": nbytes, "copies": n_cold, "pack_ms": round(pack_ms, 3),
-                "cold_wall_ms": cold_wall, "cold_us": cold_ev * 1e3, "hot_us": hot_ev * 1e3,
-                "cold_gbs": nbytes / (cold_ev * 1e-3) / 1e9, "hot_gbs": nbytes / (hot_ev * 1e-3) / 1e9,
-                "cold_tflops": flops / (cold_ev * 1e-3) / 1e12}
+                "cold_us": cold_us, "hot_us": hot_us, "cold_wall_us": cold["wall_ms"] * 1e3,
+                "cold_trials_us": [round(t * 1e3, 4) for t in cold["trials_ms"]], "queued": cold["queued"],
+                "cold_gbs": nbytes / (cold_us * 1e-6) / 1e9, "hot_gbs": nbytes / (hot_us * 1e-6) / 1e9,
+                "cold_tflops": flops / (cold_us * 1e-6) / 1e12}
 
-    def measure_stack(self, trials, name="c4_stack7b", fused=False):
-        """The 224 projections of a 32-layer 7B stack in layer order: one call
-        each, or (fused) q/k/v and gate/up as one i4s_run_multi call each, so
-        4 calls per layer.  Fused projections read the same x, as in a model."""
+    def stack_items(self, name):
         import workloads as WL
         torch = self.torch
-        mats = WL.WORKLOADS[name].matrices
         items, total, groups = [], 0, {}
-        for m in mats:
+        for m in WL.WORKLOADS[name].matrices:
             w16, x16 = WL.make_weight_and_x(m, 1)
             p, _ = self.pack(w16, m)
             x = self.to_dev(x16)
@@ -313,30 +324,79 @@ class Runner:
             items.append((p, x, y, 1))
             total += p.packed_nbytes()
             groups[p.group_size] = groups.get(p.group_size, 0) + 1
-        if fused:
-            seq = []
-            for layer in range(len(items) // 7):
-                li = items[7 * layer: 7 * layer + 7]  # q, k, v, o, gate, up, down
-                for grp in (li[0:3], li[3:4], li[4:6], li[6:7]):
-                    if len(grp) == 1:
-                        seq.extend(self.calls(grp))
-                        continue
-                    descs = [p.descriptor() for p, _, _, _ in grp]
-                    arr = (self.B.i4s_packed * len(grp))(*descs)
-                    ys = (ctypes.c_void_p * len(grp))(*[y.data_ptr() for _, _, y, _ in grp])
-                    self.keep.extend([descs, arr, ys])
-                    xp = grp[0][1].data_ptr()  # the group shares its first projection's x
-                    seq.append(lambda sh, arr=arr, n=len(grp), xp=xp, ys=ys:
-                               self.lib.i4s_run_multi(arr, n, xp, 1, ys, sh))
+        return items, total, groups
+
+    def layer_calls(self, items, layer, fused):
+        """The calls of one layer: 7 single calls, or (fused) q/k/v and
+        gate/up as one i4s_run_multi call each (4 calls).  Fused projections
+        read the same x, as in a model."""
+        li = items[7 * layer: 7 * layer + 7]  # q, k, v, o, gate, up, down
+        if not fused:
+            return self.calls(li)
+        seq = []
+        for grp in (li[0:3], li[3:4], li[4:6], li[6:7]):
+            if len(grp) == 1:
+                seq.extend(self.calls(grp))
+                continue
+            descs = [p.descriptor() for p, _, _, _ in grp]
+            arr = (self.B.i4s_packed * len(grp))(*descs)
+            ys = (ctypes.c_void_p * len(grp))(*[y.data_ptr() for _, _, y, _ in grp])
+            self.keep.extend([descs, arr, ys])
+            xp = grp[0][1].data_ptr()  # the group shares its first projection's x
+            seq.append(lambda sh, arr=arr, n=len(grp), xp=xp, ys=ys:
+                       self.lib.i4s_run_multi(arr, n, xp, 1, ys, sh))
+        return seq
+
+    def measure_stack(self, trials, name="c4_stack7b", fused=False, items=None):
+        """The 224 projections of a 32-layer 7B stack in layer order (2.7 GB
+        per pass, so every call streams from HBM).  Per pass: one captured
+        graph of the whole pass, timed like the GEMV.  Per layer: in one
+        eager pass queued behind a delay kernel, an event after each layer's
+        calls; a layer's time is the span between its two events."""
+        import numpy as np
+        torch = self.torch
+        own = items is None
+        if own:
+            items, total, groups = self.stack_items(name)
         else:
-            seq = self.calls(items)
-        wall, ev = self.timed(seq, len(seq), len(seq), trials)
-        res = {"calls": len(seq), "fused": fused, "packed_bytes": total, "us_per_pass": ev * len(seq) * 1e3,
-               "us_per_layer": ev * len(seq) * 1e3 / 32, "gbs": total / (ev * len(seq) * 1e-3) / 1e9,
-               "group_sizes": groups}
-        del items, seq
+            items, total, groups = items
+        layers = len(items) // 7
+        per_layer = [self.layer_calls(items, l, fused) for l in range(layers)]
+        seq = [c for calls in per_layer for c in calls]
+        r = self.timed(seq, len(seq), len(seq), trials, False)
+        pass_us = r["ms"] * len(seq) * 1e3
+        # per layer, eager, one pass per trial
+        run_ws = self.lib.i4s_run_ws
+        sh = self.stream.cuda_stream
+        spans = []
+        for _ in range(trials):
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(layers + 1)]
+            st = self.floor.i4sf_delay(50000, sh)
+            if st != 0:
+                raise RuntimeError(f"i4sf_delay returned {st}")
+            ev[0].record(self.stream)
+            for l, calls in enumerate(per_layer):
+                for item in calls:
+                    s = item(sh) if callable(item) else run_ws(*item, sh)
+                    if s != 0:
+                        raise self.B.I4SError(s, "i4s_run")
+                ev[l + 1].record(self.stream)
+            torch.cuda.synchronize()
+            spans.append([ev[l].elapsed_time(ev[l + 1]) * 1e3 for l in range(layers)])
+        layer_us = [float(v) for v in np.median(np.array(spans), axis=0)]
+        layer_bytes = [sum(p.packed_nbytes() for p, _, _, _ in items[7 * l: 7 * l + 7]) for l in range(layers)]
+        res = {"calls": len(seq), "fused": fused, "packed_bytes": total, "us_per_pass": pass_us,
+               "us_per_layer": pass_us / layers, "gbs": total / (pass_us * 1e-6) / 1e9,
+               "group_sizes": groups,
+               "layers": [{"layer": l, "us": round(layer_us[l], 3), "bytes": layer_bytes[l],
+                           "gbs": round(layer_bytes[l] / (layer_us[l] * 1e-6) / 1e9, 1)} for l in range(layers)],
+               "eager_pass_us": round(sum(layer_us), 2)}
+        del seq, per_layer
         self.keep.clear()
-        torch.cuda.empty_cache()
+        if own:
+            del items
+            torch.cuda.empty_cache()
         return res
 
 
@@ -354,6 +414,7 @@ def main():
     batch = args.batch or wl.batches[0]
 
     head = R.measure_layer(m, batch, args.steps, args.warmup, args.trials)
+    say(f"headline: {head['cold_us']:.4f} us/call cold, {head['hot_us']:.4f} hot, queued {head['queued']}")
     floor_us = R.launch_floor_us()
 
     if args.calib_copy:
@@ -366,24 +427,34 @@ def main():
         del a, b
 
     nbytes = head["packed_bytes"]
-    achieved = nbytes / (head["cold_us"] * 1e-6) / 1e9
+    us = head["cold_us"]
+    achieved = nbytes / (us * 1e-6) / 1e9
+    src_sha = sha_of(B1_SRCS)
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if (tr.get("kernel_source_sha") == sha_of(B1_SRCS) and tr.get("workload") == args.workload
+        if (tr.get("kernel_source_sha") == src_sha and tr.get("workload") == args.workload
                 and tr.get("batch") == batch):
             traffic = tr.get("hbm_bytes_per_launch")
+    kernel_only = None
+    if os.path.exists(KTIME_FILE):
+        with open(KTIME_FILE) as f:
+            kt = json.load(f)
+        if (kt.get("kernel_source_sha") == src_sha and kt.get("workload") == args.workload
+                and kt.get("batch") == batch):
+            kernel_only = {k: kt[k] for k in ("kernel", "avg_us", "calls", "profile", "kernel_source_sha")
+                           if k in kt}
     kname = kernel_label(m, batch)
 
     result = {
         "metric": METRIC,
-        "value": round(nbytes / (head["cold_wall_ms"] * 1e-3) / 1e9, 2),
+        "value": round(achieved, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(head["cold_wall_ms"], 6),
+        "ms_per_step": round(us * 1e-3, 7),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -394,11 +465,14 @@ def main():
                         f"{'dense' if m.n_keep == 4 else str(m.n_keep) + ':4'} INT4 G{head['group_size']}, "
                         f"batch {batch}, fp16 activations, fp32 accumulation",
             "rows": m.rows, "cols": m.cols, "n_keep": m.n_keep, "group_size": head["group_size"], "batch": batch,
-            "mode": "cold", "copies": head["copies"], "timing": "eager" if args.eager else "hip_graph",
+            "mode": "cold", "copies": head["copies"], "timing": "hip_graph, queued behind a delay kernel",
             "packed_bytes": nbytes, "x_bytes": 2 * batch * m.cols, "y_bytes": 2 * batch * m.rows,
         },
-        "us_per_call": round(head["cold_us"], 4),
+        "us_per_call": round(us, 4),
         "pct_of_peak": round(100 * achieved / PEAK_HBM_GBS, 2),
+        "trials_us": head["cold_trials_us"],
+        "queued": head["queued"],
+        "wall_us_per_call": round(head["cold_wall_us"], 4),
         "hot": {"us_per_call": round(head["hot_us"], 4), "gbs": round(head["hot_gbs"], 2),
                 "note": "one copy, cache-resident (L2/MALL), not an HBM figure"},
         "launch_floor_us": round(floor_us, 4),
@@ -406,21 +480,28 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": kname,
                      "algorithmic_bytes_per_launch": nbytes},
+        "kernel_only": kernel_only,
     }
 
     if not args.no_floors:
-        fl = R.floors(nbytes)
-        best = min(fl["stream_read_cold_us"].values())
-        fl["read_only_ceiling_gbs"] = round(nbytes / (best * 1e-6) / 1e9, 2)
-        fl["gemv_frac_of_read_only_ceiling"] = round(achieved / fl["read_only_ceiling_gbs"], 4)
-        fl["empty_launch_us"] = round(floor_us, 4)
-        for k in ("stream_read_hot_us", "load_latency_ns"):
-            fl[k] = round(fl[k], 4)
-        fl["stream_read_cold_us"] = {k: round(v, 4) for k, v in fl["stream_read_cold_us"].items()}
-        result["floors"] = fl
+        shapes = R.read_floor(nbytes, FLOOR_SHAPES)
+        best = min(shapes, key=lambda s: s["cold_us"])
+        plain = R.read_floor(nbytes, [(1, 256, 0)], trials=3)[0]
+        result["floors"] = {
+            "bytes": nbytes // 16 * 16,
+            "read_only_shapes": shapes,
+            "best_shape": {k: best[k] for k in ("vpl", "threads", "blocks")},
+            "read_only_cold_us": best["cold_us"],
+            "read_only_hot_us": best["hot_us"],
+            "one_load_per_lane_cold_us": plain["cold_us"],
+            "read_only_ceiling_gbs": round(nbytes / (best["cold_us"] * 1e-6) / 1e9, 2),
+            "gemv_frac_of_read_only_ceiling": round(best["cold_us"] / us, 4),
+            "empty_launch_us": round(floor_us, 4),
+            "load_latency_ns": round(R.latency_ns(), 2),
+        }
 
     if args.suite:
-        rows = run_suite(R, args)
+        rows = run_suite(R, args, result.get("floors", {}).get("best_shape"))
         with open(args.suite, "w") as f:
             json.dump({"headline": result, "suite": rows}, f, indent=1)
 
@@ -449,13 +530,16 @@ def kernel_label(m, batch):
     return f"gemv_kernel<{m.n_keep},BT>=" + str(batch)
 
 
-def run_suite(R, args):
+def run_suite(R, args, floor_shape):
     import workloads as WL
     out = []
     names = ("c1_512", "c2_4096", "c3_mlp7b", "c5_verify13b", "c4_stack7b", "x1_4096_1to4", "x2_mix_stack7b")
     stacks = ("c4_stack7b", "x2_mix_stack7b")
     if args.only:
         names = tuple(n for n in names if n in args.only.split(","))
+    shapes = [(1, 256, 0), (2, 512, 0), (4, 512, 0)]
+    if floor_shape and tuple(floor_shape.values()) not in shapes:
+        shapes.append((floor_shape["vpl"], floor_shape["threads"], floor_shape["blocks"]))
     for name in names:
         wl = WL.WORKLOADS[name]
         mats = wl.matrices
@@ -463,51 +547,72 @@ def run_suite(R, args):
             # one outer and one inner layer individually; the whole stack below
             mats = [m for m in mats if m.name.startswith(("L0.", "L4."))]
         for m in mats:
+            floor = None
             for b in wl.batches:
                 r = R.measure_layer(m, b, args.suite_steps, max(1, args.suite_steps // 10), 3)
                 r["workload"] = name
-                print(f"suite {name}/{m.name} b{b}: cold {r['cold_us']:.2f} us ({r['cold_gbs']:.0f} GB/s), "
-                      f"hot {r['hot_us']:.2f} us", file=sys.stderr, flush=True)
+                if floor is None:
+                    fl = R.read_floor(r["packed_bytes"], shapes, steps=args.suite_steps)
+                    floor = min(fl, key=lambda s: s["cold_us"])
+                r["read_only_cold_us"] = floor["cold_us"]
+                r["read_only_shape"] = [floor["vpl"], floor["threads"], floor["blocks"]]
+                r["frac_of_read_only"] = round(floor["cold_us"] / r["cold_us"], 4)
+                say(f"suite {name}/{m.name} b{b}: cold {r['cold_us']:.2f} us ({r['cold_gbs']:.0f} GB/s), "
+                    f"hot {r['hot_us']:.2f} us, read-only {floor['cold_us']:.2f} us")
                 out.append(r)
     for name in stacks:
         if args.no_stack or name not in names:
             continue
+        items = R.stack_items(name)
         for fused in (False, True):
-            s = R.measure_stack(3, name, fused)
+            s = R.measure_stack(3, name, fused, items=items)
             s["workload"] = name + ("/all-fused" if fused else "/all")
-            print(f"suite {s['workload']}: {s['us_per_pass']:.1f} us per {s['calls']}-call pass "
-                  f"({s['gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+            say(f"suite {s['workload']}: {s['us_per_pass']:.1f} us per {s['calls']}-call pass "
+                f"({s['gbs']:.0f} GB/s); eager per-layer sum {s['eager_pass_us']:.1f} us")
             out.append(s)
+        del items
+        R.torch.cuda.empty_cache()
     return out
 
 
 def cpu_baseline(args, m, batch, w16, x16, packed_bytes):
-    """The oracle as it stands, on this host's cores, on a bounded sample."""
+    """The oracle as it stands, on this host's cores, on a bounded sample:
+    its pack of the layer once, its reconstruction once, then 3 warm-up and
+    at least 10 timed GEMV calls (until cpu_seconds have passed); the median
+    call is reported."""
+    import numpy as np
     import oracle as O
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if info:
+            threads = max(d.get("num_threads", 1) for d in info)
+            blas = ", ".join(f"{d.get('internal_api')} {d.get('version')}" for d in info)
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        pass
+    t = time.perf_counter()
     ref = O.pack(w16, m.n_keep, m.group_size)
+    pack_s = time.perf_counter() - t
     t = time.perf_counter()
     w_hat = O.reconstruct(ref)
     recon_s = time.perf_counter() - t
-    O.gemv(w_hat, x16)
-    n = 0
-    t = time.perf_counter()
-    while True:
+    for _ in range(3):
         O.gemv(w_hat, x16)
-        n += 1
-        el = time.perf_counter() - t
-        if el >= args.cpu_seconds and n >= 3:
-            break
-    us = el / n * 1e6
+    reps = []
+    t_all = time.perf_counter()
+    while len(reps) < 10 or time.perf_counter() - t_all < args.cpu_seconds:
+        t = time.perf_counter()
+        O.gemv(w_hat, x16)
+        reps.append(time.perf_counter() - t)
+    us = float(np.median(reps)) * 1e6
     return {"value": round(packed_bytes / (us * 1e-6) / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "us_per_call": round(us, 1),
-            "sample": f"{n} oracle GEMV calls (float64 W_hat @ x over the reconstructed {m.rows}x{m.cols} "
-                      f"layer, plus the |W_hat|@|x| tolerance sums) in {el:.1f} s; reconstruction "
-                      f"{recon_s:.2f} s once, not per call"}
+            "kind": "oracle", "us_per_call": round(us, 1), "blas": blas,
+            "oracle_pack_s": round(pack_s, 3), "reconstruct_s": round(recon_s, 3),
+            "sample": f"median of {len(reps)} oracle GEMV calls after 3 warm-ups (float64 W_hat @ x over the "
+                      f"reconstructed {m.rows}x{m.cols} layer, plus the |W_hat|@|x| tolerance sums), "
+                      f"{sum(reps):.1f} s in all; the oracle's pack ({pack_s:.2f} s) and reconstruction "
+                      f"({recon_s:.2f} s) once, not per call"}
 
 
 if __name__ == "__main__":

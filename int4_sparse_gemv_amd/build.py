@@ -14,6 +14,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -57,12 +58,19 @@ def _run(cmd):
     return out
 
 
+def _compile(cc, src, tmp):
+    obj = os.path.join(tmp, src + ".o")
+    cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    return obj, _run(cmd)
+
+
 def _link(cc, sources, lib, tmp, verbose):
+    # one hipcc process per source, in parallel (the batch kernels dominate)
+    jobs = max(1, min(len(sources), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        done = list(ex.map(lambda src: _compile(cc, src, tmp), sources))
     objs = []
-    for src in sources:
-        obj = os.path.join(tmp, src + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
-        out = _run(cmd)
+    for obj, out in done:
         if verbose and out.strip():
             print(out)
         objs.append(obj)
