@@ -44,7 +44,8 @@
  *
  * CONVENTIONS.  Every pointer to tensor data is a DEVICE pointer unless
  * marked "host".  The caller owns all memory: the library never allocates or
- * frees device memory.  `stream` is a hipStream_t passed as void* (NULL is
+ * frees device memory (i4s_run_noalloc uses a fixed array in the library's
+ * code object instead of a caller workspace).  `stream` is a hipStream_t passed as void* (NULL is
  * the null stream).  All argument checks run before anything is enqueued; a
  * failed check returns I4S_ERR_INVALID_ARGUMENT (or another status) and
  * leaves every buffer untouched.  Errors raised by the HIP runtime come back
@@ -65,6 +66,7 @@ extern "C" {
 #define I4S_FORMAT_VERSION 1
 #define I4S_MAX_BATCH 16
 #define I4S_MAX_MULTI 8
+#define I4S_NOALLOC_SCRATCH_BYTES (32u << 20) /* static scratch of i4s_run_noalloc, per GPU */
 
 typedef enum i4s_status {
   I4S_OK = 0,
@@ -249,6 +251,23 @@ i4s_status i4s_run_multi(const i4s_packed *w /* host, n entries */, int32_t n,
                          const uint16_t *x_fp16, int32_t batch,
                          uint16_t *const *y_fp16 /* host, n device pointers */,
                          void *stream);
+
+/* i4s_run_ws for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * workspace is a static array inside the library, I4S_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from the first call on that GPU until the process ends.
+ * Same arguments, kernels and results (bit for bit) as i4s_run_ws with a
+ * caller workspace; calls no allocating routine.
+ * Every call on a GPU shares that GPU's array and leaves its contents
+ * behind (nothing in it needs clearing: the partial sums are written before
+ * they are read in the same call), so calls that may overlap on one GPU --
+ * on different streams, or from several threads without ordering -- race
+ * and must not be made.
+ * Errors: as i4s_run, plus I4S_ERR_WORKSPACE_TOO_SMALL when
+ * i4s_run_workspace_size() exceeds I4S_NOALLOC_SCRATCH_BYTES (checked before
+ * anything is enqueued; such a layer needs i4s_run_ws). */
+i4s_status i4s_run_noalloc(const i4s_packed *w /* host */, const uint16_t *x_fp16,
+                           int32_t batch, uint16_t *y_fp16, void *stream);
 
 /* Static text for a status code (never NULL). */
 const char *i4s_status_string(i4s_status s);

@@ -22,6 +22,7 @@ I4S_ERR_WORKSPACE_TOO_SMALL = 4
 I4S_ERR_DEVICE = 5
 I4S_MAX_BATCH = 16
 I4S_MAX_MULTI = 8
+I4S_NOALLOC_SCRATCH_BYTES = 32 << 20
 I4S_FORMAT_VERSION = 1
 
 
@@ -78,6 +79,8 @@ SIGNATURES = {
                                               ctypes.POINTER(ctypes.c_uint64)]),
     "i4s_run_ws": (ctypes.c_int, [ctypes.POINTER(i4s_packed), ctypes.c_void_p, ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
+    "i4s_run_noalloc": (ctypes.c_int, [ctypes.POINTER(i4s_packed), ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p]),
     "i4s_run_multi": (ctypes.c_int, [ctypes.POINTER(i4s_packed), ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
     "i4s_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -147,6 +150,10 @@ def i4s_run_workspace_size(packed, batch, out):
 
 def i4s_run_ws(packed, x_ptr, batch, y_ptr, ws_ptr, ws_bytes, stream):
     return load().i4s_run_ws(ctypes.byref(packed), x_ptr, batch, y_ptr, ws_ptr, ws_bytes, stream)
+
+
+def i4s_run_noalloc(packed, x_ptr, batch, y_ptr, stream):
+    return load().i4s_run_noalloc(ctypes.byref(packed), x_ptr, batch, y_ptr, stream)
 
 
 def i4s_run_multi(packed_list, x_ptr, batch, y_ptrs, stream):

@@ -299,6 +299,29 @@ i4s_status i4s_run_ws(const i4s_packed *w, const uint16_t *x_fp16, int32_t batch
   return I4S_OK;
 }
 
+i4s_status i4s_run_noalloc(const i4s_packed *w, const uint16_t *x_fp16, int32_t batch, uint16_t *y_fp16,
+                           void *stream) {
+  i4s_status st = validate_run(w, x_fp16, batch, y_fp16);
+  if (st != I4S_OK) return st;
+  const i4s::SplitPlan plan = i4s::split_plan(*w, batch);
+  if (plan.workspace_bytes > I4S_NOALLOC_SCRATCH_BYTES)
+    return fail(I4S_ERR_WORKSPACE_TOO_SMALL,
+                "this layer and batch need %llu bytes of workspace, more than the %llu of the static scratch; "
+                "use i4s_run_ws",
+                (unsigned long long)plan.workspace_bytes, (unsigned long long)I4S_NOALLOC_SCRATCH_BYTES);
+  st = check_device();
+  if (st != I4S_OK) return st;
+  void *ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    const hipError_t e = i4s::noalloc_scratch(&ws);
+    if (e != hipSuccess) return device_error(e, "static scratch address");
+  }
+  const hipError_t e = i4s::launch_gemv_ws(*w, x_fp16, batch, y_fp16, plan, ws,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "gemv launch");
+  return I4S_OK;
+}
+
 i4s_status i4s_run_multi(const i4s_packed *w, int32_t n, const uint16_t *x_fp16, int32_t batch,
                          uint16_t *const *y_fp16, void *stream) {
   if (!w || !y_fp16) return fail(I4S_ERR_INVALID_ARGUMENT, "w or y_fp16 is NULL");

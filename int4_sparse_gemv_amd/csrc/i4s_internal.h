@@ -98,4 +98,8 @@ hipError_t launch_gemv_ws(const i4s_packed &w, const uint16_t *x, int32_t batch,
                           uint16_t *y, const SplitPlan &plan, void *workspace,
                           hipStream_t stream);
 
+// Device address of the current device's static scratch array
+// (I4S_NOALLOC_SCRATCH_BYTES, i4s_noalloc.hip), looked up once per device.
+hipError_t noalloc_scratch(void **ptr);
+
 }  // namespace i4s

@@ -34,7 +34,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["i4s_pack_sizes", "i4s_pack", "i4s_pack_ex", "i4s_run", "i4s_run_workspace_size", "i4s_run_ws",
-         "i4s_run_multi",
+         "i4s_run_multi", "i4s_run_noalloc",
          "i4s_status_string", "i4s_last_error", "i4s_version", "i4s_format_version"])
 
 
