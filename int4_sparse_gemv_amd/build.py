@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libi4s.so")
 FLOOR_LIB = os.path.join(PKG, "libi4s_floor.so")
 
-SOURCES = ("i4s_api.cpp", "i4s_pack.hip", "i4s_gemv_b1.hip", "i4s_gemv_b2.hip", "i4s_gemv_batch.hip",
+SOURCES = ("i4s_api.cpp", "i4s_plan.cpp", "i4s_pack.hip", "i4s_gemv_b1.hip", "i4s_gemv_b2.hip", "i4s_gemv_batch.hip",
            "i4s_noalloc.hip")
 
 HIPCC_FLAGS = [

@@ -89,6 +89,16 @@ hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch,
 // only after being written in the same call).  ksplit == 0 means "no split
 // kernel" (batch 1, not 2:4, or switched off) and a workspace of 0 bytes;
 // ksplit == 1 runs the split kernel without partials (0 bytes).
+// Shapes shared by the batch kernels (i4s_gemv_batch.hip) and the host-side
+// plan of a call (i4s_plan.cpp).
+constexpr int kSWaves = 8;                       // K-split kernel: waves per block
+constexpr int kSTiles = 2;                       // K-split kernel: 16-row tiles per wave
+constexpr int kSRows = 16 * kSTiles * kSWaves;   // K-split kernel: 256 rows per block
+constexpr int kSMaxBlocks = 8;                   // K-split kernel: blocks of 4 units per slice
+constexpr int kSPartialTileBytes = 64 * 16;      // one fp32 16x16 partial tile (64 lanes x 4 floats)
+constexpr int kRUnits = 16;                      // rows kernel: units per chunk (the wide form)
+constexpr int kRMaxWaves = 8;                    // rows kernel: waves per block (the wide form)
+
 struct SplitPlan {
   int row_groups = 0, ksplit = 0, ups = 0;
   size_t partial_bytes = 0, workspace_bytes = 0;
