@@ -12,15 +12,17 @@ an untimed 512 MiB read evicts the caches, so no copy is still cached when a
 trial starts, whatever the step count.  Hot (reported, labelled
 cache-resident): one copy, no eviction.
 
-Timing: the K timed steps are captured once into a HIP graph.  A trial
-enqueues, on one stream, (the eviction read), a bounded delay kernel, event
-e0, one replay of the graph, event e1.  The delay keeps the GPU busy while the
-host submits the graph, so e0..e1 spans exactly the K calls running back to
-back and not the host's launch of the graph.  Per call = (e1 - e0) / K; the
+Timing: a trial enqueues, on one stream, (the eviction read), a bounded
+delay kernel, event e0, exactly K calls, event e1.  The delay keeps the GPU
+busy while the host enqueues the calls, so e0..e1 spans the K calls running
+back to back, not the host's launch rate (``queued`` says whether the host
+finished enqueueing before the delay ended).  Per call = (e1 - e0) / K; the
 median over trials is reported, and ``value``, ``ms_per_step``,
 ``pct_of_peak`` and ``roofline`` all come from that one figure.  Wall time
 around each trial (torch.cuda.synchronize() on both sides) is reported as
-well.
+well.  (Replaying a captured HIP graph instead adds about 10 us per replay
+on this system, 0.5 us per call at K = 20; the events bracketing eager
+launches add about 3 us per trial.)
 
 Prints ONE JSON line for the 4096x4096 2:4 G128 batch-1 layer.  ``value`` is
 packed bytes per call / seconds per call (GB/s, decimal) in cold mode.
@@ -76,6 +78,15 @@ def parse():
     ap.add_argument("--suite-steps", type=int, default=1000, help="with --suite: timed calls per layer and trial")
     ap.add_argument("--no-floors", action="store_true",
                     help="skip the read-only and latency floor measurements")
+    ap.add_argument("--lib", default=None,
+                    help="time this build of libi4s (e.g. one made with build --define ... --out PATH)")
+    ap.add_argument("--batch-paths", action="store_true",
+                    help="instead of the headline: 2:4 layers at batch 2, 3, 4 and 8, one JSON line")
+    ap.add_argument("--stack", default=None,
+                    help="instead of the headline: one 7B stack (c4_stack7b or x2_mix_stack7b), per pass and per layer")
+    ap.add_argument("--summarize-rocprof", nargs=2, metavar=("DIR", "OUT"), default=None,
+                    help="summarize rocprofv3 CSV output under DIR into the text file OUT (no GPU needed)")
+    ap.add_argument("--min-calls", type=int, default=20, help="with --summarize-rocprof")
     return ap.parse_args()
 
 
@@ -92,7 +103,7 @@ def say(msg):
 
 
 class Runner:
-    """Packs layers and times graph-captured sequences of i4s_run calls."""
+    """Packs layers and times queued sequences of i4s_run calls."""
 
     def __init__(self, args):
         import torch
@@ -100,7 +111,8 @@ class Runner:
         from int4_sparse_gemv_amd import _binding as B
         from int4_sparse_gemv_amd import build as BLD
         self.torch, self.I, self.B, self.args = torch, I, B, args
-        self.lib = B.load()
+        # (the HIP runtime torch brings is loaded first, then the library)
+        self.lib = B.load(os.path.abspath(args.lib)) if getattr(args, "lib", None) else B.load()
         self.dev = torch.device("cuda:0")
         torch.cuda.set_device(self.dev)
         self.stream = torch.cuda.current_stream(self.dev)
@@ -163,39 +175,34 @@ class Runner:
         if st != 0:
             raise RuntimeError(f"i4sf_stream_read returned {st}")
 
-    def capture(self, seq, n):
-        """A HIP graph of n calls visiting seq round-robin.  An item of seq is
-        an i4s_run_ws argument tuple or a callable taking the stream handle
-        and returning a status."""
-        torch, run_ws = self.torch, self.lib.i4s_run_ws
-        cap = torch.cuda.Stream(self.dev)
-        g = torch.cuda.CUDAGraph()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=cap):
-            for i in range(n):
-                item = seq[i % len(seq)]
-                st = item(cap.cuda_stream) if callable(item) else run_ws(*item, cap.cuda_stream)
-                if st != 0:
-                    raise self.B.I4SError(st, "i4s_run")
-        return g
+    def launch(self, item, sh):
+        """Enqueue one call: an i4s_run_ws argument tuple, or a callable
+        taking the stream handle and returning a status."""
+        st = item(sh) if callable(item) else self.lib.i4s_run_ws(*item, sh)
+        if st != 0:
+            raise self.B.I4SError(st, "i4s_run")
 
-    def replay_timed(self, g, steps, evict):
-        """One trial: (eviction), delay, e0, replay, e1.  Returns (device ms
-        per step, wall ms per step, whether the host finished submitting the
-        graph before the delay ended)."""
+    def run_timed(self, seq, steps, evict):
+        """One trial: (eviction), delay, e0, `steps` calls visiting seq
+        round-robin, e1 -- all enqueued on the one stream before the delay
+        ends.  Returns (device ms per step, wall ms per step, whether the host
+        had enqueued everything before the delay ended)."""
         torch = self.torch
-        delay_us = min(100000, 1000 + 5 * steps)
+        sh = self.stream.cuda_stream
+        delay_us = min(100000, 2000 + 20 * steps)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         if evict:
             self.evict()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t1 = time.perf_counter()
-        st = self.floor.i4sf_delay(delay_us, self.stream.cuda_stream)
+        st = self.floor.i4sf_delay(delay_us, sh)
         if st != 0:
             raise RuntimeError(f"i4sf_delay returned {st}")
         e0.record(self.stream)
-        g.replay()
+        n = len(seq)
+        for i in range(steps):
+            self.launch(seq[i % n], sh)
         e1.record(self.stream)
         submit_us = (time.perf_counter() - t1) * 1e6
         torch.cuda.synchronize()
@@ -204,35 +211,30 @@ class Runner:
 
     def timed(self, seq, steps, warmup, trials, evict):
         """Median over trials of the device time per call (ms) of `steps`
-        calls visiting seq round-robin, plus the per-trial figures."""
+        calls visiting seq round-robin, after `warmup` untimed calls, plus the
+        per-trial figures."""
         import numpy as np
-        g_warm = self.capture(seq, max(1, warmup))
-        g = self.capture(seq, steps)
-        g_warm.replay()
+        sh = self.stream.cuda_stream
+        for i in range(warmup):
+            self.launch(seq[i % len(seq)], sh)
         evs, walls, oks = [], [], []
         for _ in range(trials):
-            ev, wall, ok = self.replay_timed(g, steps, evict)
+            ev, wall, ok = self.run_timed(seq, steps, evict)
             evs.append(ev)
             walls.append(wall)
             oks.append(ok)
-        del g, g_warm
         return {"ms": float(np.median(evs)), "wall_ms": float(np.median(walls)), "trials_ms": evs,
                 "queued": all(oks)}
 
     def launch_floor_us(self, steps=2000, trials=3):
-        """Per-launch time of a one-element fill kernel replayed the same way (the dispatch floor)."""
-        import numpy as np
+        """Per-launch time of a one-element fill kernel timed the same way (the dispatch floor)."""
         torch = self.torch
         t = torch.zeros(1, device=self.dev)
-        cap = torch.cuda.Stream(self.dev)
-        g = torch.cuda.CUDAGraph()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=cap):
-            for _ in range(steps):
-                t.fill_(1.0)
-        g.replay()
-        res = [self.replay_timed(g, steps, False)[0] * 1e3 for _ in range(trials)]
-        return float(np.median(res))
+
+        def fill(sh):
+            t.fill_(1.0)
+            return 0
+        return self.timed([fill], steps, 20, trials, False)["ms"] * 1e3
 
     def read_floor(self, nbytes, shapes, steps=2000, trials=3):
         """Cold and hot per-launch time (us) of read-only launches of nbytes
@@ -349,10 +351,10 @@ class Runner:
 
     def measure_stack(self, trials, name="c4_stack7b", fused=False, items=None):
         """The 224 projections of a 32-layer 7B stack in layer order (2.7 GB
-        per pass, so every call streams from HBM).  Per pass: one captured
-        graph of the whole pass, timed like the GEMV.  Per layer: in one
-        eager pass queued behind a delay kernel, an event after each layer's
-        calls; a layer's time is the span between its two events."""
+        per pass, so every call streams from HBM).  Per pass: the calls of a
+        whole pass, timed like the GEMV.  Per layer: in one pass queued behind
+        a delay kernel, an event after each layer's calls; a layer's time is
+        the span between its two events (the events themselves add a little)."""
         import numpy as np
         torch = self.torch
         own = items is None
@@ -365,8 +367,7 @@ class Runner:
         seq = [c for calls in per_layer for c in calls]
         r = self.timed(seq, len(seq), len(seq), trials, False)
         pass_us = r["ms"] * len(seq) * 1e3
-        # per layer, eager, one pass per trial
-        run_ws = self.lib.i4s_run_ws
+        # per layer: one pass per trial, an event after each layer
         sh = self.stream.cuda_stream
         spans = []
         for _ in range(trials):
@@ -378,9 +379,7 @@ class Runner:
             ev[0].record(self.stream)
             for l, calls in enumerate(per_layer):
                 for item in calls:
-                    s = item(sh) if callable(item) else run_ws(*item, sh)
-                    if s != 0:
-                        raise self.B.I4SError(s, "i4s_run")
+                    self.launch(item, sh)
                 ev[l + 1].record(self.stream)
             torch.cuda.synchronize()
             spans.append([ev[l].elapsed_time(ev[l + 1]) * 1e3 for l in range(layers)])
@@ -391,7 +390,7 @@ class Runner:
                "group_sizes": groups,
                "layers": [{"layer": l, "us": round(layer_us[l], 3), "bytes": layer_bytes[l],
                            "gbs": round(layer_bytes[l] / (layer_us[l] * 1e-6) / 1e9, 1)} for l in range(layers)],
-               "eager_pass_us": round(sum(layer_us), 2)}
+               "per_layer_sum_us": round(sum(layer_us), 2)}
         del seq, per_layer
         self.keep.clear()
         if own:
@@ -400,15 +399,101 @@ class Runner:
         return res
 
 
+BATCH_PATH_LAYERS = (("c2_4096", "w"), ("c5_verify13b", "attn"), ("c5_verify13b", "up"))
+
+
+def batch_paths(R, args):
+    """Cold and hot us/call of 2:4 layers at batch 2, 3, 4 and 8 through the
+    loaded build of the library, with the kernel each call ran."""
+    import workloads as WL
+    rows = []
+    for wl, name in BATCH_PATH_LAYERS:
+        m = next(mm for mm in WL.WORKLOADS[wl].matrices if mm.name == name)
+        for b in (2, 3, 4, 8):
+            r = R.measure_layer(m, b, args.steps, args.warmup, args.trials)
+            say(f"{wl}/{name} {m.rows}x{m.cols} b{b}: cold {r['cold_us']:.3f} us, hot {r['hot_us']:.3f} us")
+            rows.append({"layer": f"{m.rows}x{m.cols}", "batch": b, "cold_us": round(r["cold_us"], 4),
+                         "hot_us": round(r["hot_us"], 4)})
+    return {"lib": args.lib or "default", "steps": args.steps, "trials": args.trials, "rows": rows}
+
+
+def summarize_rocprof(d, out, min_calls):
+    """rocprofv3 CSV output (kernel traces, counter collections) -> a short text file.
+
+    Kernel trace: runs of >= min_calls consecutive dispatches of one kernel
+    and grid (median, mean and minimum duration), then per kernel over the
+    whole run.  Counters: the mean per dispatch of every counter, per kernel
+    and grid."""
+    import csv
+    import glob
+    import statistics as st
+    from collections import defaultdict
+    lines = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*_kernel_trace.csv"), recursive=True)):
+        rows = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"]))
+        runs, cur, key = [], [], None
+        for r in rows:
+            k = (r["Kernel_Name"], r["Grid_Size_X"], r["Grid_Size_Y"], r["Workgroup_Size_X"])
+            if k != key and cur:
+                runs.append((key, cur))
+                cur = []
+            key = k
+            cur.append(r)
+        if cur:
+            runs.append((key, cur))
+        lines.append(f"# kernel trace {os.path.basename(f)}: runs of >= {min_calls} consecutive dispatches "
+                     f"of one kernel and grid")
+        lines.append("# n | median us | mean us | min us | grid x,y | block | kernel")
+        for (name, gx, gy, wg), run in runs:
+            if len(run) < min_calls:
+                continue
+            du = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in run]
+            lines.append(f"{len(run)} | {st.median(du):.3f} | {st.mean(du):.3f} | {min(du):.3f} | {gx},{gy} | {wg} | "
+                         f"{name[:160]}")
+        agg = defaultdict(list)
+        for r in rows:
+            agg[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines.append("# per kernel over the whole run: calls | mean us | median us | kernel")
+        for name, du in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"{len(du)} | {st.mean(du):.3f} | {st.median(du):.3f} | {name[:160]}")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*_counter_collection.csv"), recursive=True)):
+        vals = defaultdict(lambda: defaultdict(list))
+        disp = defaultdict(set)
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"], r.get("Grid_Size", r.get("Grid_Size_X", "")))
+            vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            disp[key].add(r["Dispatch_Id"])
+        lines.append(f"# counters {os.path.basename(f)}: mean per dispatch, kernels with >= {min_calls} dispatches")
+        for key, cv in sorted(vals.items(), key=lambda kv: kv[0][0]):
+            if len(disp[key]) < min_calls:
+                continue
+            cs = ", ".join(f"{c}={st.mean(v):.6g}" for c, v in sorted(cv.items()))
+            lines.append(f"{len(disp[key])} dispatches | grid {key[1]} | {key[0][:160]} | {cs}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_rocprof:
+        summarize_rocprof(*args.summarize_rocprof, args.min_calls)
+        return
     import workloads as WL
 
     R = Runner(args)
+    if args.batch_paths:
+        print(json.dumps(batch_paths(R, args)), flush=True)
+        return
+    if args.stack:
+        items = R.stack_items(args.stack)
+        out = {"workload": args.stack, "passes": [R.measure_stack(args.trials, args.stack, f, items=items)
+                                                  for f in (False, True)]}
+        print(json.dumps(out), flush=True)
+        return
     wl = WL.WORKLOADS[args.workload]
     m = wl.matrices[0] if args.matrix is None else next(mm for mm in wl.matrices if mm.name == args.matrix)
     batch = args.batch or wl.batches[0]
@@ -465,7 +550,7 @@ def main():
                         f"{'dense' if m.n_keep == 4 else str(m.n_keep) + ':4'} INT4 G{head['group_size']}, "
                         f"batch {batch}, fp16 activations, fp32 accumulation",
             "rows": m.rows, "cols": m.cols, "n_keep": m.n_keep, "group_size": head["group_size"], "batch": batch,
-            "mode": "cold", "copies": head["copies"], "timing": "hip_graph, queued behind a delay kernel",
+            "mode": "cold", "copies": head["copies"], "timing": "stream launches queued behind a delay kernel",
             "packed_bytes": nbytes, "x_bytes": 2 * batch * m.cols, "y_bytes": 2 * batch * m.rows,
         },
         "us_per_call": round(us, 4),
@@ -568,7 +653,7 @@ def run_suite(R, args, floor_shape):
             s = R.measure_stack(3, name, fused, items=items)
             s["workload"] = name + ("/all-fused" if fused else "/all")
             say(f"suite {s['workload']}: {s['us_per_pass']:.1f} us per {s['calls']}-call pass "
-                f"({s['gbs']:.0f} GB/s); eager per-layer sum {s['eager_pass_us']:.1f} us")
+                f"({s['gbs']:.0f} GB/s); per-layer sum {s['per_layer_sum_us']:.1f} us")
             out.append(s)
         del items
         R.torch.cuda.empty_cache()

@@ -5,6 +5,11 @@ library's HIP and C++ sources under ``csrc/`` into
 ``int4_sparse_gemv_amd/libi4s.so``, and the benchmark's floor kernels
 (``csrc/i4s_floor.hip``) into ``libi4s_floor.so``.  It always recompiles.
 hipcc cross-compiles for gfx950 without a GPU present.
+
+``--define NAME=VALUE`` (repeatable) overrides one of the kernel-choice
+thresholds of ``csrc/i4s_internal.h`` and ``--out PATH`` writes that build of
+the library elsewhere (for measuring the alternatives with ``bench.py
+--lib PATH``); the default library is only ever built with the defaults.
 """
 
 from __future__ import annotations
@@ -59,17 +64,18 @@ def _run(cmd):
     return out
 
 
-def _compile(cc, src, tmp):
+def _compile(cc, src, tmp, defines=()):
     obj = os.path.join(tmp, src + ".o")
-    cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [cc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE, "-I", CSRC, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     return obj, _run(cmd)
 
 
-def _link(cc, sources, lib, tmp, verbose):
+def _link(cc, sources, lib, tmp, verbose, defines=()):
     # one hipcc process per source, in parallel (the batch kernels dominate)
     jobs = max(1, min(len(sources), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(jobs) as ex:
-        done = list(ex.map(lambda src: _compile(cc, src, tmp), sources))
+        done = list(ex.map(lambda src: _compile(cc, src, tmp, defines), sources))
     objs = []
     for obj, out in done:
         if verbose and out.strip():
@@ -80,14 +86,35 @@ def _link(cc, sources, lib, tmp, verbose):
     os.replace(tmp_lib, lib)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libi4s.so and libi4s_floor.so; returns the path of libi4s.so."""
+THRESHOLDS = ("I4S_BATCH2_VALU_MAX_ROWS", "I4S_BATCH2_VALU_MAX_K", "I4S_MATRIX_CORE_MIN_BATCH")
+
+
+def build(verbose: bool = False, defines=(), out: str = None) -> str:
+    """Compile libi4s.so and libi4s_floor.so; returns the path of libi4s.so.
+
+    With ``defines`` (NAME=VALUE strings, NAME one of THRESHOLDS) and ``out``,
+    build only the library, with those thresholds, at ``out``."""
+    for d in defines:
+        if d.split("=", 1)[0] not in THRESHOLDS or "=" not in d:
+            raise ValueError(f"--define takes NAME=VALUE with NAME in {THRESHOLDS}, got {d!r}")
+    if defines and not out:
+        raise ValueError("a build with --define needs --out (the default library keeps the defaults)")
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="i4s_build_") as tmp:
+        if out:
+            os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+            _link(cc, SOURCES, os.path.abspath(out), tmp, verbose, tuple(defines))
+            return os.path.abspath(out)
         _link(cc, SOURCES, LIB, tmp, verbose)
         _link(cc, ("i4s_floor.hip",), FLOOR_LIB, tmp, verbose)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("--define", action="append", default=[])
+    ap.add_argument("--out", default=None)
+    a = ap.parse_args()
+    print(build(verbose=a.v, defines=a.define, out=a.out))

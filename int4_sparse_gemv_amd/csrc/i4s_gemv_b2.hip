@@ -228,7 +228,7 @@ hipError_t launch_bv_u(const i4s_packed &w, const uint16_t *x, int32_t batch, ui
 // 4 the matrix cores win everywhere (5120x5120 b4: 10.2 against 6.7).  So:
 // batch 2, at most 8192 rows, K <= 8192.
 bool gemv_bv_applies(const i4s_packed &w, int32_t batch) {
-  return batch == 2 && w.rows <= 8192 && w.cols / kSegCols <= 128;
+  return batch == 2 && w.rows <= I4S_BATCH2_VALU_MAX_ROWS && w.cols <= I4S_BATCH2_VALU_MAX_K;
 }
 
 hipError_t launch_gemv_bv(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y, hipStream_t stream) {

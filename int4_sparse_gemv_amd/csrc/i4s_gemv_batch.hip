@@ -1341,10 +1341,10 @@ hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint
     const hipError_t e = launch_gemv_bv(w, x, batch, y, stream);
     if (e != hipErrorNotSupported) return e;
   }
-  if (NK == 2 && batch >= 2) {
+  if (NK == 2 && batch >= I4S_MATRIX_CORE_MIN_BATCH) {
     return launch_smfmac(w, x, batch, y, stream);
   }
-  if ((NK == 1 || NK == 4) && batch >= 2 && rows_kernel_fits(w)) {
+  if ((NK == 1 || NK == 4) && batch >= I4S_MATRIX_CORE_MIN_BATCH && rows_kernel_fits(w)) {
     return launch_rows<NK>(w, x, batch, y, stream);
   }
   if (batch <= 1) {
@@ -1387,7 +1387,7 @@ hipError_t launch_gemv_multi(const i4s_packed *w, int32_t n, const uint16_t *x, 
     if (batch == 1) {
       const hipError_t e = launch_gemv_b1_multi(w, n, x, y, stream);
       if (e != hipErrorNotSupported) return e;
-    } else if (!valu_b2 && rows_kernel_fits(w[0])) {
+    } else if (!valu_b2 && batch >= I4S_MATRIX_CORE_MIN_BATCH && rows_kernel_fits(w[0])) {
       const hipError_t e = w[0].n_keep == 2   ? launch_rows_multi<2>(w, n, x, batch, y, stream)
                            : w[0].n_keep == 1 ? launch_rows_multi<1>(w, n, x, batch, y, stream)
                                               : launch_rows_multi<4>(w, n, x, batch, y, stream);

@@ -89,6 +89,24 @@ hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch,
 // only after being written in the same call).  ksplit == 0 means "no split
 // kernel" (batch 1, not 2:4, or switched off) and a workspace of 0 bytes;
 // ksplit == 1 runs the split kernel without partials (0 bytes).
+// Kernel-choice thresholds.  Fixed when the library is built (nothing read
+// at run time changes which kernel runs); a build may override them with -D
+// to measure the alternatives (python -m int4_sparse_gemv_amd.build --define).
+//   I4S_BATCH2_VALU_MAX_ROWS / _MAX_K: batch 2 runs on the two-vector VALU
+//     kernel for layers of at most this many rows and columns (0 rows: never);
+//   I4S_MATRIX_CORE_MIN_BATCH: from this batch up, layers run on the matrix
+//     cores (the VALU batch kernel below it, and for shapes the matrix-core
+//     kernels do not cover).
+#ifndef I4S_BATCH2_VALU_MAX_ROWS
+#define I4S_BATCH2_VALU_MAX_ROWS 8192
+#endif
+#ifndef I4S_BATCH2_VALU_MAX_K
+#define I4S_BATCH2_VALU_MAX_K 8192
+#endif
+#ifndef I4S_MATRIX_CORE_MIN_BATCH
+#define I4S_MATRIX_CORE_MIN_BATCH 2
+#endif
+
 // Shapes shared by the batch kernels (i4s_gemv_batch.hip) and the host-side
 // plan of a call (i4s_plan.cpp).
 constexpr int kSWaves = 8;                       // K-split kernel: waves per block
