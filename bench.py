@@ -605,7 +605,7 @@ def kernel_label(m, batch):
         if units <= 256:
             return f"gemv_b1_direct_kernel<{m.n_keep},{rpw},{(units + 63) // 64},8>"
         return f"gemv_b1_kernel<{m.n_keep},{rpw},8>"
-    if batch == 2 and m.rows <= 8192 and units <= 128:
+    if batch == 2 and m.rows <= 8192 and units <= 64:
         return f"gemv_bv_direct_kernel<{m.n_keep},2,{(units + 63) // 64}>"
     long_split = units > 256 and batch > 8 and m.rows <= 4096
     if units <= 512 and not (m.n_keep == 2 and long_split):

@@ -240,7 +240,7 @@ i4s_status i4s_run_ws(const i4s_packed *w /* host */, const uint16_t *x_fp16,
  *            not overlap one another, x, or any layer's packed buffers.
  * Results are bit-identical to n i4s_run calls.  One launch when the layers
  * share n_keep and group_size and either batch is 1 and cols <= 16384, or
- * batch >= 2 and cols <= 32768 (except batch 2 with cols <= 8192 and a layer
+ * batch >= 2 and cols <= 32768 (except batch 2 with cols <= 4096 and a layer
  * of at most 8192 rows, which single calls run on another kernel, and layers
  * whose single calls split the row into chunks of different widths);
  * otherwise one launch per layer, in order, on `stream`.  Asynchronous; allocates nothing.

@@ -12,7 +12,7 @@
 // once -- dequantized fp16 pairs and, for 2:4 and 1:4, the v_perm_b32
 // selectors -- and then multiplied with each vector in turn, so the second
 // vector costs one selection and one v_dot2 per group.  Used for batch 2 on
-// layers of at most 8192 rows and K <= 8192; taller layers and larger
+// layers of at most 8192 rows and K <= 4096; taller or wider layers and larger
 // batches go to the sparse matrix cores.
 
 #include "i4s_gemv_common.h"
@@ -221,12 +221,13 @@ hipError_t launch_bv_u(const i4s_packed &w, const uint16_t *x, int32_t batch, ui
 
 }  // namespace
 
-// Measured on MI355X (cold, µs per call, this kernel against the matrix-core
-// kernel at batch 2): 4096x4096 1:4 3.51 / 4.43, 4096x4096 2:4 3.92 / 4.25,
-// 5120x5120 2:4 6.33 / 6.51, but 13824x5120 2:4 12.4 / 10.5 (every block
-// stages both vectors, and tall layers have many blocks), and at batch 3 and
-// 4 the matrix cores win everywhere (5120x5120 b4: 10.2 against 6.7).  So:
-// batch 2, at most 8192 rows, K <= 8192.
+// Measured on MI355X (cold, us per call, this kernel against the matrix-core
+// kernel at batch 2): 4096x4096 2:4 4.04 / 4.45 and 1:4 3.51 / 4.43, but
+// 5120x5120 2:4 7.05 / 6.65 and 13824x5120 2:4 19.3 / 11.3 (every block
+// stages both vectors, and tall layers have many blocks); at batch 3 and 4
+// the matrix cores win everywhere (5120x5120 b4: 13.3 against 6.9).  So:
+// batch 2, at most I4S_BATCH2_VALU_MAX_ROWS rows and I4S_BATCH2_VALU_MAX_K
+// columns (8192 and 4096).
 bool gemv_bv_applies(const i4s_packed &w, int32_t batch) {
   return batch == 2 && w.rows <= I4S_BATCH2_VALU_MAX_ROWS && w.cols <= I4S_BATCH2_VALU_MAX_K;
 }

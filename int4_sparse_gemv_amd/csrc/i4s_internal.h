@@ -66,7 +66,7 @@ struct MultiDesc {
 // GEMV kernels.  launch_gemv (i4s_gemv_batch.hip) dispatches every call;
 // launch_gemv_b1 (i4s_gemv_b1.hip) runs batch 1 for n_keep 2 and 4.
 hipError_t launch_gemv_b1(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream);
-// Batch 2 on the VALU for layers of at most 8192 rows and K <= 8192 (each
+// Batch 2 on the VALU for layers of at most 8192 rows and K <= 4096 (each
 // unit decoded once, then multiplied with both vectors); returns
 // hipErrorNotSupported (launching nothing) where it does not apply.
 hipError_t launch_gemv_bv(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
@@ -101,7 +101,7 @@ hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch,
 #define I4S_BATCH2_VALU_MAX_ROWS 8192
 #endif
 #ifndef I4S_BATCH2_VALU_MAX_K
-#define I4S_BATCH2_VALU_MAX_K 8192
+#define I4S_BATCH2_VALU_MAX_K 4096
 #endif
 #ifndef I4S_MATRIX_CORE_MIN_BATCH
 #define I4S_MATRIX_CORE_MIN_BATCH 2
