@@ -196,10 +196,13 @@ i4s_status i4s_run(const i4s_packed *w /* host */, const uint16_t *x_fp16,
                    int32_t batch, uint16_t *y_fp16, void *stream);
 
 /* Bytes of device workspace i4s_run_ws needs for this layer and batch; 0
- * when the call needs none: batch 1, a pattern other than 2:4, K <= 16384,
- * K <= 32768 unless the batch exceeds 8 on at most 4096 rows (the one-launch
- * batch kernel covers those rows whole), or a layer whose K split has a
- * single slice.  Host-only and pure.  Errors:
+ * when the call needs none.  Only the 2:4 batch GEMV splits K across blocks,
+ * and only where that is faster than the one-launch kernel over whole rows:
+ * K > 32768 (beyond the one-launch kernel) at any batch >= 2; batch 3-8 with
+ * K >= 8192 where the one-launch kernel would run fewer than 192 blocks
+ * (fewer than 3072 rows, or 4800 to 6143 rows, where it takes two 16-row
+ * tiles per block); batch 9-16 with K >= 5120 on at most 8192 rows; and not
+ * when K <= 1024 (a single slice).  Host-only and pure.  Errors:
  * I4S_ERR_INVALID_ARGUMENT (descriptor inconsistent, batch out of range,
  * bytes == NULL). */
 i4s_status i4s_run_workspace_size(const i4s_packed *w /* host */, int32_t batch,
@@ -207,8 +210,8 @@ i4s_status i4s_run_workspace_size(const i4s_packed *w /* host */, int32_t batch,
 
 /* y = W_hat x as i4s_run, using a caller workspace that lets the 2:4 batch
  * kernel split K across blocks (section 3.3 of the page: the activations of
- * a block's slice are staged on chip once for 256 rows).  Same arguments as
- * i4s_run plus:
+ * a block's 1024-column slice are staged on chip once for up to 128 rows).
+ * Same arguments as i4s_run plus:
  *   workspace       : device buffer of at least i4s_run_workspace_size()
  *                     bytes, 16-byte aligned (may be NULL when that size is
  *                     0).  Scratch for the fp32 partial sums of each slice:

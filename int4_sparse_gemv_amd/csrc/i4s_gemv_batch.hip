@@ -441,250 +441,6 @@ __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// batch kernel on the sparse matrix cores with a K split across blocks
-//
-// Same matrix-core step as above, but a block owns 256 rows (8 waves, each
-// two 16-row tiles) and one slice of K.  The slice of x (batch vectors x the
-// slice's columns) is staged once in LDS and shared by the 16 tiles, and
-// each B fragment a wave reads from LDS feeds the matrix steps of both of
-// its tiles.  A block writes its 16 partial fp32 tiles to the caller's
-// workspace with plain stores; a second, small kernel on the same stream sums
-// the slices in slice order (deterministic) and stores y.  The kernel
-// boundary makes the partials visible across the XCDs' L2 caches, so no
-// device-scope atomics, fences or counters are needed, and the workspace is
-// plain scratch.
-//
-// Order of issue per wave: the activation slice, the first block of weights
-// of both tiles, the LDS write of the slice (which waits for those loads
-// only), then every other weight load.  A wave with more loads outstanding
-// than its CU accepts stalls at issue, so this puts the slice in LDS before
-// the bulk of the weight stream; the barrier orders LDS only.
-
-
-// Weight registers of one block of 4 units for one lane.
-struct WBlock {
-  uint32_t v[4];
-  uint32_t c[2];
-  uint32_t s;
-};
-
-// partial tile index: slice ks, row group rg, tile t (0..15) of the group;
-// each tile is 64 lanes x 4 floats (lane j + 16q: rows 4q..4q+3, vector j)
-__device__ inline size_t split_tile(int ks, int ngrp, int rg, int t) {
-  return ((size_t)ks * ngrp + rg) * (kSWaves * kSTiles) + t;
-}
-
-// The activation slice is staged by ROUNDS loads per thread (two vectors per
-// round, 256 threads per vector, so ROUNDS = ceil(batch / 2)); NB = ups / 4
-// blocks of 4 units per tile.  Both are template parameters so that every
-// load is issued unconditionally (clamped indices) and the compiler can count
-// exactly the loads issued after the activations.
-template <int NB, int ROUNDS>
-__global__ __launch_bounds__(64 * kSWaves) void gemv_smfmac_split_kernel(
-    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
-    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
-    const uint16_t *__restrict__ scales, const uint16_t *x, int batch,
-    uint16_t *__restrict__ y, f4_t *__restrict__ partial, int ksplit, int ups) {
-  extern __shared__ __align__(16) uint16_t xs[];          // [batch][ups * 64 + 8]
-  __shared__ __align__(16) uint16_t scs[kSWaves][kSTiles][4][16];
-  const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
-  const int li = lane % 16, lq = lane / 16;
-  const int rg = blockIdx.x, ks = blockIdx.y, ngrp = gridDim.x;
-  const int cols = units * kSegCols;
-  const int u0 = ks * ups, u1 = min(units, u0 + ups);
-  const int xst = ups * kSegCols + 8;  // halfs per vector in LDS (16-byte pad)
-  const uint32_t nnz_row = (uint32_t)units * 32;
-  const uint32_t ngroups = (uint32_t)units >> sg_shift;
-
-  // 1. the activation slice: vector 2r + (tid / 256), piece tid % 256 (16 B)
-  const int vpb = (u1 - u0) * (kSegCols / 8);  // pieces per vector, <= 256
-  const int xc = threadIdx.x % 256, xh = threadIdx.x / 256;
-  const int xcc = min(xc, vpb - 1);
-  u32x4_t xg[ROUNDS];  // a native vector type: one load, no struct copy
-#pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    const int bv = min(2 * r + xh, batch - 1);
-    xg[r] = *reinterpret_cast<const u32x4_t *>(x + (int64_t)bv * cols + (int64_t)u0 * kSegCols + 8 * xcc);
-  }
-  // x is deliberately not __restrict__: its loads then stay ordered before
-  // the weight loads across the scheduling barriers below (invariant loads
-  // would float past them).
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 2. weights of the wave's two tiles (units past the slice re-read its last
-  // unit; their matrix steps are skipped)
-  int arow[kSTiles];
-  uint32_t rstart[kSTiles];
-#pragma unroll
-  for (int t = 0; t < kSTiles; ++t) {
-    arow[t] = min(rg * kSRows + (wave * kSTiles + t) * 16 + li, rows - 1);
-    rstart[t] = (uint32_t)arow[t] * nnz_row;
-  }
-  const int b0 = u0 / 4;
-  auto load = [&](WBlock &m, int t, int b, bool nt) {  // block b (units 4b..4b+3) of tile t
-    const int u = min(4 * b + lq, u1 - 1);
-    const uint32_t e0 = rstart[t] + (uint32_t)u * 32;
-    const uint32_t si = (uint32_t)arow[t] * ngroups + ((uint32_t)u >> sg_shift);
-    if (nt) {
-      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vals + (e0 >> 1)));
-      const u32x2_t c = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(codes + (e0 >> 3)));
-      m.v[0] = v.x; m.v[1] = v.y; m.v[2] = v.z; m.v[3] = v.w;
-      m.c[0] = c.x; m.c[1] = c.y;
-      m.s = __builtin_nontemporal_load(scales + si);
-    } else {
-      const uint4 v = *reinterpret_cast<const uint4 *>(vals + (e0 >> 1));
-      const uint2 c = *reinterpret_cast<const uint2 *>(codes + (e0 >> 3));
-      m.v[0] = v.x; m.v[1] = v.y; m.v[2] = v.z; m.v[3] = v.w;
-      m.c[0] = c.x; m.c[1] = c.y;
-      m.s = scales[si];
-    }
-  };
-  WBlock mw[kSTiles][NB];
-#pragma unroll
-  for (int t = 0; t < kSTiles; ++t) load(mw[t][0], t, b0, true);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 3. the slice to LDS (threads with a clamped index write the same piece
-  // to the same place again), then the rest of the weight stream
-#pragma unroll
-  for (int r = 0; r < ROUNDS; ++r)
-    *reinterpret_cast<u32x4_t *>(xs + min(2 * r + xh, batch - 1) * xst + 8 * xcc) = xg[r];
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 1; i < NB; ++i)
-#pragma unroll
-    for (int t = 0; t < kSTiles; ++t) load(mw[t][i], t, b0 + i, true);
-  int32_t rp[kSTiles];
-#pragma unroll
-  for (int t = 0; t < kSTiles; ++t) rp[t] = row_ptr[arow[t]];
-  lds_barrier();  // orders LDS only: no wave waits here for its weights
-  __builtin_amdgcn_sched_barrier(0);
-
-  // B lane (vector li, column quarter lq); lanes past `batch` read the last
-  // real vector (their output columns are never stored)
-  const uint16_t *xl = xs + min(li, batch - 1) * xst + 8 * lq;
-  f4_t acc[kSTiles];
-#pragma unroll
-  for (int t = 0; t < kSTiles; ++t) acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  // Each unit's product tile is scaled on its own (a unit lies in one
-  // quantization group): no group test between the matrix steps, so G does
-  // not enter the kernel's control flow.  The scales pass from the loading
-  // lanes to the accumulator lanes through the wave's LDS slot, with a
-  // wave-scope synchronisation on each side of the exchange.
-  auto process = [&](const WBlock (&m)[kSTiles], int b) {
-    uint32_t W[kSTiles][4], P[kSTiles], Q[kSTiles];
-#pragma unroll
-    for (int t = 0; t < kSTiles; ++t) {
-      W[t][0] = m[t].v[0]; W[t][1] = m[t].v[1]; W[t][2] = m[t].v[2]; W[t][3] = m[t].v[3];
-      transpose4(W[t][0], W[t][1], W[t][2], W[t][3]);
-      transpose_codes(m[t].c[0], m[t].c[1], P[t], Q[t]);
-    }
-    wave_lds_sync();  // every lane has read the previous block's scales
-#pragma unroll
-    for (int t = 0; t < kSTiles; ++t) scs[wave][t][lq][li] = (uint16_t)m[t].s;
-    wave_lds_sync();  // ... and the other lanes' writes are visible
-    uint2 sv[kSTiles][4];  // rows 4lq..4lq+3 of units 4b..4b+3
-#pragma unroll
-    for (int t = 0; t < kSTiles; ++t)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) sv[t][s] = *reinterpret_cast<const uint2 *>(&scs[wave][t][s][4 * lq]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int u = 4 * b + s;
-      if (u >= u1) break;
-      const uint4 xa = *reinterpret_cast<const uint4 *>(xl + (u - u0) * kSegCols);
-      const uint4 xb = *reinterpret_cast<const uint4 *>(xl + (u - u0) * kSegCols + 32);
-      const u8_t xv = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-      const h16_t bx = __builtin_bit_cast(h16_t, xv);
-#pragma unroll
-      for (int t = 0; t < kSTiles; ++t) {
-        const f4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-        f4_t cg;
-        if (s == 0) cg = smfmac_step<0>(W[t][0], bx, z, P[t], Q[t]);
-        if (s == 1) cg = smfmac_step<1>(W[t][1], bx, z, P[t], Q[t]);
-        if (s == 2) cg = smfmac_step<2>(W[t][2], bx, z, P[t], Q[t]);
-        if (s == 3) cg = smfmac_step<3>(W[t][3], bx, z, P[t], Q[t]);
-        const uint2 g2 = sv[t][s];
-        acc[t][0] = fmaf(fp16_bits_to_float(g2.x & 0xFFFFu), cg[0], acc[t][0]);
-        acc[t][1] = fmaf(fp16_bits_to_float(g2.x >> 16), cg[1], acc[t][1]);
-        acc[t][2] = fmaf(fp16_bits_to_float(g2.y & 0xFFFFu), cg[2], acc[t][2]);
-        acc[t][3] = fmaf(fp16_bits_to_float(g2.y >> 16), cg[3], acc[t][3]);
-      }
-    }
-  };
-
-  // 4. multiply as the weights arrive; the row_ptr check comes afterwards (a
-  // wave with a row stored away from the format's offset fetches its
-  // weights again and recomputes; the check is the same for the whole wave)
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    WBlock cur[kSTiles];
-#pragma unroll
-    for (int t = 0; t < kSTiles; ++t) cur[t] = mw[t][i];
-    process(cur, b0 + i);
-  }
-  bool moved = false;
-#pragma unroll
-  for (int t = 0; t < kSTiles; ++t) moved |= (uint32_t)rp[t] != rstart[t];
-  if (__builtin_amdgcn_ballot_w64(moved) != 0) {
-#pragma unroll
-    for (int t = 0; t < kSTiles; ++t) {
-      rstart[t] = safe_row_start<2>(rp[t], (uint32_t)(rows - 1) * nnz_row);
-      acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      WBlock cur[kSTiles];
-#pragma unroll
-      for (int t = 0; t < kSTiles; ++t) load(cur[t], t, b0 + i, false);
-      process(cur, b0 + i);
-    }
-  }
-
-  // 5. one slice: store y; several: the partial tiles (the columns of real
-  // vectors only)
-#pragma unroll
-  for (int t = 0; t < kSTiles; ++t) {
-    const int tile = wave * kSTiles + t;
-    if (ksplit == 1) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rg * kSRows + tile * 16 + 4 * lq + r;
-        if (li < batch && row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(acc[t][r]);
-      }
-    } else if (li < batch) {
-      partial[split_tile(ks, ngrp, rg, tile) * 64 + lane] = acc[t];
-    }
-  }
-}
-
-// Sums the ksplit partial tiles of every row in slice order and stores y.
-// One thread per (row group, tile, lane); lanes of vectors past `batch` idle.
-__global__ __launch_bounds__(256) void gemv_split_reduce_kernel(
-    int rows, int batch, int ngrp, int ksplit, const f4_t *__restrict__ partial, uint16_t *__restrict__ y) {
-  const int gid = blockIdx.x * 256 + threadIdx.x;  // < ngrp * 16 * 64 by the grid
-  const int lane = gid % 64, tile = (gid / 64) % (kSWaves * kSTiles), rg = gid / (64 * kSWaves * kSTiles);
-  const int li = lane % 16, lq = lane / 16;
-  if (li >= batch) return;
-  f4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = 0; k0 < ksplit; k0 += 8) {  // up to 8 loads in flight, summed in slice order
-    f4_t part[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      part[k] = partial[split_tile(min(k0 + k, ksplit - 1), ngrp, rg, tile) * 64 + lane];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k0 + k < ksplit) sum += part[k];
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = rg * kSRows + tile * 16 + 4 * lq + r;
-    if (row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(sum[r]);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // batch kernel on the sparse matrix cores, one 16-row tile per block over the
 // whole of K (2:4 and 1:4, 2 <= batch <= 16, K <= 16384; no workspace)
 //
@@ -1095,6 +851,301 @@ void gemv_smfmac_rows_multi_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// batch kernel on the sparse matrix cores with K split across blocks (2:4,
+// 2 <= batch <= 16; needs the caller's workspace)
+//
+// A block is kKWaves waves, one slice of K (kKUnits = 16 units, 1024
+// columns) and one group of kKWaves * TW 16-row tiles.  The slice is the fast
+// block index, so the slices of a row group are in flight together and the
+// group's rows are read as a whole.  The block stages its slice of x (the
+// batch vectors' 1024 columns, rows padded by 16 bytes so that the B reads
+// of 16 vectors fall in distinct banks) in LDS once; B fragments then come
+// from LDS, not through the vector L1, which on this part moves ~56 bytes
+// per clock per CU against several times that for LDS reads -- and a B
+// fragment is 2 KB per unit whatever the batch, 5x the weight bytes of a
+// tile's unit.  Each wave runs its TW tiles one after the other: it loads a
+// tile's weights as 4 rows x 256 bytes per instruction (the shape that
+// streams fastest), writes them to its LDS area in that layout, reads them
+// back in the matrix layout (lane (i, kq): row i, unit 4b + kq) and goes on
+// as the other SMFMAC kernels (4x4 transposes across the lane groups, one
+// matrix step per unit, group scales on the fp32 tiles).  The loads of the
+// next two tiles are in flight while a tile is multiplied.  Each tile's fp32
+// partial product goes to the workspace, and a second small kernel sums the
+// slices in slice order (deterministic) and stores y; the kernel boundary
+// makes the partials visible across the XCDs' L2 caches, so no device-scope
+// atomics, fences or counters are needed and the workspace is plain scratch.
+// With a single slice (K <= 1024) the kernel stores y itself.
+
+// partial tile index: slice ks, row group rg (of tpg tiles), tile t of the
+// group; each tile is 64 lanes x 4 floats (lane j + 16q: rows 4q..4q+3,
+// vector j)
+__device__ inline size_t slice_tile(int ks, int ngrp, int rg, int tpg, int t) {
+  return ((size_t)ks * ngrp + rg) * tpg + t;
+}
+
+// One tile's result of the slice kernel: y itself when there is a single
+// slice, else the tile's partial (the columns of real vectors only).
+__device__ inline void slice_store(const f4_t &acc, int tile, int ks, int ksplit, int rg, int ngrp, int tw,
+                                   int rows, int batch, uint16_t *__restrict__ y, f4_t *__restrict__ partial) {
+  const int lane = threadIdx.x % 64, li = lane % 16, lq = lane / 16;
+  if (li >= batch) return;
+  if (ksplit == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = tile * 16 + 4 * lq + r;
+      if (row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(acc[r]);
+    }
+  } else {
+    const int tpg = kKWaves * tw;
+    partial[slice_tile(ks, ngrp, rg, tpg, tile - rg * tpg) * 64 + lane] = acc;
+  }
+}
+
+// ROUNDS = loads per thread that stage the slice of x (two vectors per
+// round): 2, 4 or 8 for batch <= 4, 8, 16.  SG = G / 64.  TW = tiles per
+// wave.  All three are template parameters so that every load is issued
+// unconditionally (clamped indices) and the compiler can count exactly the
+// loads issued after each one.
+template <int SG, int TW, int ROUNDS>
+__global__ __launch_bounds__(64 * kKWaves) void gemv_smfmac_slice_kernel(
+    int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
+    const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *x, int batch,
+    uint16_t *__restrict__ y, f4_t *__restrict__ partial) {
+  typedef RowsGeom<kKUnits> Geo;  // a tile's staging area, as in the rows kernel
+  constexpr int NL = Geo::kLoads, ST = Geo::kStride;
+  static_assert(Geo::kRowsPerLoad == 4 && NL == 4, "a tile is 4 loads of 4 rows x 16 units");
+  extern __shared__ __align__(16) uint8_t lds[];  // x: [batch][kKXStride] halfs, then [waves][Geo::kTileLds]
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int li = lane % 16, lq = lane / 16;  // the matrix layout
+  const int lu = lane % 16, lr = lane / 16;  // the load layout: unit lu of row 4k + lr
+  const int ksplit = gridDim.x, ngrp = gridDim.y;
+  // The slices of a row group share the cache lines of its scales and
+  // row_ptr: all of them run on one XCD (one L2).  Blocks go to the XCDs
+  // round-robin by linear index, so linear index L takes row group
+  // 8 * (L / (8 * ksplit)) + L % 8 and slice (L / 8) % ksplit; the groups
+  // past the last multiple of 8 take the rest in the same way.  (Measured
+  // on MI355X: 1-2 us faster than slice-major order on the 13B layers.)
+  int ks, rg;
+  {
+    const int L = (int)(blockIdx.y * gridDim.x + blockIdx.x), ng8 = ngrp / 8 * 8;
+    if (L < ng8 * ksplit) {
+      rg = (L / 8) / ksplit * 8 + L % 8;
+      ks = (L / 8) % ksplit;
+    } else {
+      const int r = L - ng8 * ksplit, rem = ngrp - ng8;  // rem >= 1 here
+      rg = ng8 + r % rem;
+      ks = r / rem;
+    }
+  }
+  const int u0 = ks * kKUnits, nu = min(kKUnits, units - u0);  // live units of the slice (>= 1 by the grid)
+  const int cols = units * kSegCols;
+  const uint32_t nnz_row = (uint32_t)units * 32;
+  const uint32_t ngroups = (uint32_t)units >> sg_shift;
+  const int tile0 = (rg * kKWaves + wave) * TW;  // the wave's first tile
+  uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
+  uint8_t *wl = lds + (size_t)batch * kKXStride * 2 + wave * Geo::kTileLds;
+  u32x4_t *lv = reinterpret_cast<u32x4_t *>(wl);                                      // [16 rows][ST]
+  u32x2_t *lc = reinterpret_cast<u32x2_t *>(wl + Geo::kValsBytes);                    // [16 rows][ST]
+  uint16_t *lsc = reinterpret_cast<uint16_t *>(wl + Geo::kValsBytes + Geo::kCodesBytes);  // [16 / SG groups][16 rows]
+
+  // 1. the slice of x: vector 2r + (tid / 128), 16-byte piece tid % 128 of the
+  // live units (threads with a clamped index fetch, and later write, a piece
+  // that another thread also writes: the same bytes to the same place)
+  const int xh = threadIdx.x / 128, xp = min((int)threadIdx.x % 128, nu * 8 - 1);
+  u32x4_t xg[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int v = min(2 * r + xh, batch - 1);
+    xg[r] = *reinterpret_cast<const u32x4_t *>(x + (int64_t)v * cols + (int64_t)u0 * kSegCols + 8 * xp);
+  }
+  // x is deliberately not __restrict__: its loads then stay ordered before
+  // the weight loads across the scheduling barrier (invariant loads would
+  // float past it).
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. weights: tile j of the wave, lane (unit lu, row 4k + lr).  A unit past
+  // the slice's end re-reads its last live unit, and a group past it its
+  // last live group; their scales are staged as +0 below, and since K % G
+  // == 0 and slices start on multiples of 16 units, such units form whole
+  // quantization groups, whose partial tiles (finite) are multiplied by
+  // zero.  Scales: NS loads per tile, lane (row l % 16, group 4i + l / 16 of
+  // the slice) -- a 64-lane load costs the address unit about the same
+  // whatever its width, so the tile's 16 x 16 / SG scales take 4 / SG
+  // loads, not one per load of weights (measured: the 2-byte scale and
+  // 4-byte row_ptr loads, 8 per tile, cost 1.5 us of the 13824x5120 layer at
+  // batch 4).  Two buffers: tile j uses buffer j % 2.
+  constexpr int NG = kKUnits / SG, NS = NG / 4;  // groups per slice, scale loads per tile
+  const int ngl = nu / SG;                        // live groups (nu % SG == 0: K % G == 0)
+  u32x4_t wv[2][NL];
+  u32x2_t wc[2][NL];
+  uint16_t wsc[2][NS];
+  const int ul = u0 + min(lu, nu - 1);
+  auto load_tile = [&](int j, int b) {
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const uint32_t row = (uint32_t)min((tile0 + j) * 16 + 4 * k + lr, rows - 1);
+      const uint32_t e0 = row * nnz_row + (uint32_t)ul * 32;
+      wv[b][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vals + (e0 >> 1)));
+      wc[b][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(codes + (e0 >> 3)));
+    }
+    const uint32_t srow = (uint32_t)min((tile0 + j) * 16 + li, rows - 1);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int g = min(4 * i + lq, ngl - 1);
+      wsc[b][i] = __builtin_nontemporal_load(scales + srow * ngroups + (uint32_t)(u0 / SG + g));
+    }
+  };
+  // row_ptr of the wave's 16 * TW rows, one load: lane l takes row l % (16 * TW)
+  const int rrow = min(tile0 * 16 + lane % (16 * TW), rows - 1);
+  // 3. the slice to LDS and a block barrier (it orders LDS only) before any
+  // weight load is issued.  Loads return roughly in the order the memory
+  // system receives them: behind the layer's whole weight stream (every
+  // wave issues its tiles at once) the slice arrived microseconds late
+  // (per-wave clock stamps on a 13824x5120 layer at batch 4: median 3.4 us
+  // after the wave's start, against 1.1 us when it goes first).  And a wave
+  // that has issued its weight loads reaches a barrier late: with a layer's
+  // loads outstanding, issue stalls until the memory system drains (median
+  // 4.1 us at the barrier when it followed the weight loads).
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r)
+    *reinterpret_cast<u32x4_t *>(xs + min(2 * r + xh, batch - 1) * kKXStride + 8 * xp) = xg[r];
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(0, 0);
+  if constexpr (TW > 1) load_tile(1, 1);
+  const int32_t rp = row_ptr[rrow];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // B lane (vector li, column quarter lq); lanes past `batch` read the last
+  // real vector (their output columns are never stored)
+  const uint16_t *xl = xs + min(li, batch - 1) * kKXStride + 8 * lq;
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int b = j & 1;
+    // The staging area is the wave's own, written in the load layout and
+    // read back by other lanes of the wave in the matrix layout: a
+    // wave-scope synchronisation before the writes of every tile after the
+    // first (the previous tile's reads are done) and after the writes.
+    if (j > 0) wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      lv[(4 * k + lr) * ST + lu] = wv[b][k];
+      lc[(4 * k + lr) * ST + lu] = wc[b][k];
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) lsc[(4 * i + lq) * 16 + li] = 4 * i + lq < ngl ? wsc[b][i] : (uint16_t)0;
+    wave_lds_sync();
+    if (j + 2 < TW) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(j + 2, b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      // the matrix layout: lane (row li, chunk lq) takes unit 4bb + lq
+      const u32x4_t v = lv[li * ST + 4 * bb + lq];
+      const u32x2_t cw = lc[li * ST + 4 * bb + lq];
+      uint32_t W0 = v.x, W1 = v.y, W2 = v.z, W3 = v.w, P, Q;
+      transpose4(W0, W1, W2, W3);
+      transpose_codes(cw.x, cw.y, P, Q);
+      // the scales of the block's groups (rows 4lq..4lq+3 of each), read
+      // before the matrix steps
+      u32x2_t sv[4 / SG];
+#pragma unroll
+      for (int g = 0; g < 4 / SG; ++g)
+        sv[g] = *reinterpret_cast<const u32x2_t *>(&lsc[(4 * bb / SG + g) * 16 + 4 * lq]);
+      f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // units past the slice's end read the last live unit's columns
+        const int ub = min(4 * bb + s, nu - 1);
+        const u32x4_t xa = *reinterpret_cast<const u32x4_t *>(xl + ub * kSegCols);
+        const u32x4_t xb = *reinterpret_cast<const u32x4_t *>(xl + ub * kSegCols + 32);
+        const u8_t xv = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+        const h16_t hb = __builtin_bit_cast(h16_t, xv);
+        if (s == 0) cg = smfmac_step<0>(W0, hb, cg, P, Q);
+        if (s == 1) cg = smfmac_step<1>(W1, hb, cg, P, Q);
+        if (s == 2) cg = smfmac_step<2>(W2, hb, cg, P, Q);
+        if (s == 3) cg = smfmac_step<3>(W3, hb, cg, P, Q);
+        if ((s + 1) % SG == 0) {  // the group ends with this unit
+          const u32x2_t g2 = sv[s / SG];
+          acc[0] = fmaf(fp16_bits_to_float(g2.x & 0xFFFFu), cg[0], acc[0]);
+          acc[1] = fmaf(fp16_bits_to_float(g2.x >> 16), cg[1], acc[1]);
+          acc[2] = fmaf(fp16_bits_to_float(g2.y & 0xFFFFu), cg[2], acc[2]);
+          acc[3] = fmaf(fp16_bits_to_float(g2.y >> 16), cg[3], acc[3]);
+          cg = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+      }
+    }
+    slice_store(acc, tile0 + j, ks, ksplit, rg, ngrp, TW, rows, batch, y, partial);
+  }
+
+  // row_ptr check (wave-uniform).  A row stored away from the format's
+  // offset is rare: the wave then recomputes its tiles' share of this slice
+  // from row_ptr's offsets with a plain per-lane loop (lane (vector li,
+  // quarter lq) owns rows 4lq..4lq+3 of each tile, as in the matrix
+  // accumulator) and stores again, within the same tolerance.
+  if (__builtin_amdgcn_ballot_w64((uint32_t)rp != (uint32_t)rrow * nnz_row) != 0) {
+    const uint16_t *xv = x + (int64_t)min(li, batch - 1) * cols;
+    for (int j = 0; j < TW; ++j) {
+      f4_t acc;
+      for (int r = 0; r < 4; ++r) {
+        const int row = min((tile0 + j) * 16 + 4 * lq + r, rows - 1);
+        const uint32_t rs = safe_row_start<2>(row_ptr[row], (uint32_t)(rows - 1) * nnz_row);
+        float sum = 0.0f;
+        for (int u = u0; u < u0 + nu; ++u) {
+          float g = 0.0f;
+          for (int e = 0; e < 32; ++e) {
+            const uint32_t el = rs + (uint32_t)u * 32 + (uint32_t)e;
+            const uint32_t word = reinterpret_cast<const uint32_t *>(vals)[el >> 3];
+            const uint32_t k8 = el & 7u;
+            const uint32_t slot = (k8 & 1u) ? 4u + (k8 >> 1) : (k8 >> 1);
+            const int q = (int)((word >> (4 * slot)) & 0xFu) - 8;
+            const uint32_t code = (codes[el >> 3] >> (2 * (el & 7u))) & 3u;
+            const int col = u * kSegCols + 4 * (e / 2) + (int)code;
+            g = fmaf((float)q, fp16_bits_to_float(xv[col]), g);
+          }
+          sum = fmaf(fp16_bits_to_float(scales[(uint32_t)row * ngroups + ((uint32_t)u >> sg_shift)]), g, sum);
+        }
+        acc[r] = sum;
+      }
+      slice_store(acc, tile0 + j, ks, ksplit, rg, ngrp, TW, rows, batch, y, partial);
+    }
+  }
+}
+
+
+// Sums the ksplit partial tiles of every row in slice order and stores y.
+// One thread per (row group, tile, lane); lanes of vectors past `batch` idle.
+// tpg = tiles per row group (a multiple of 4, so the grid of 256-thread
+// blocks covers the groups exactly).
+__global__ __launch_bounds__(256) void gemv_slice_reduce_kernel(
+    int rows, int batch, int ngrp, int tpg, int ksplit, const f4_t *__restrict__ partial,
+    uint16_t *__restrict__ y) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;  // < ngrp * tpg * 64 by the grid
+  const int lane = gid % 64, tile = (gid / 64) % tpg, rg = gid / (64 * tpg);
+  const int li = lane % 16, lq = lane / 16;
+  if (li >= batch) return;
+  f4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < ksplit; k0 += 8) {  // up to 8 loads in flight, summed in slice order
+    f4_t part[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      part[k] = partial[slice_tile(min(k0 + k, ksplit - 1), ngrp, rg, tpg, tile) * 64 + lane];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k0 + k < ksplit) sum += part[k];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = (rg * tpg + tile) * 16 + 4 * lq + r;
+    if (row < rows) y[(int64_t)li * rows + row] = (uint16_t)float_to_fp16_bits(sum[r]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 
 template <int NK, int BT, int RPW>
@@ -1293,44 +1344,47 @@ hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, 
   return hipGetLastError();
 }
 
-template <int NB, int ROUNDS>
-hipError_t launch_split_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+template <int SG, int TW, int RN>
+hipError_t launch_slice_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                           const SplitPlan &pl, f4_t *partial, hipStream_t stream) {
-  const size_t lds = (size_t)batch * (pl.ups * kSegCols + 8) * 2;
-  const dim3 grid((unsigned)pl.row_groups, (unsigned)pl.ksplit), block(64 * kSWaves);
-  const int units = w.cols / kSegCols;
-  const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
-  hipLaunchKernelGGL((gemv_smfmac_split_kernel<NB, ROUNDS>), grid, block, lds, stream, w.rows, units, sg_shift,
-                     w.row_ptr, w.vals, w.codes, w.scales, x, batch, y, partial, pl.ksplit, pl.ups);
+  const size_t lds = (size_t)batch * kKXStride * 2 + kKWaves * RowsGeom<kKUnits>::kTileLds;  // <= 61,184 bytes
+  const int sg_shift = SG == 1 ? 0 : (SG == 2 ? 1 : 2);
+  hipLaunchKernelGGL((gemv_smfmac_slice_kernel<SG, TW, RN>), dim3((unsigned)pl.ksplit, (unsigned)pl.row_groups),
+                     dim3(64 * kKWaves), lds, stream, w.rows, w.cols / kSegCols, sg_shift, w.row_ptr, w.vals,
+                     w.codes, w.scales, x, batch, y, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ksplit == 1) return e;
-  const unsigned threads = (unsigned)pl.row_groups * kSWaves * kSTiles * 64;  // a multiple of 256
-  hipLaunchKernelGGL(gemv_split_reduce_kernel, dim3(threads / 256), dim3(256), 0, stream, w.rows, batch,
-                     pl.row_groups, pl.ksplit, partial, y);
+  const int tpg = kKWaves * TW;
+  const unsigned threads = (unsigned)pl.row_groups * (unsigned)tpg * 64u;  // a multiple of 256
+  hipLaunchKernelGGL(gemv_slice_reduce_kernel, dim3(threads / 256), dim3(256), 0, stream, w.rows, batch,
+                     pl.row_groups, tpg, pl.ksplit, partial, y);
   return hipGetLastError();
 }
 
-template <int NB>
-hipError_t launch_split_nb(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+template <int SG, int TW>
+hipError_t launch_slice_tw(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                            const SplitPlan &pl, f4_t *partial, hipStream_t stream) {
-  if (batch <= 2) return launch_split_t<NB, 1>(w, x, batch, y, pl, partial, stream);
-  if (batch <= 4) return launch_split_t<NB, 2>(w, x, batch, y, pl, partial, stream);
-  if (batch <= 8) return launch_split_t<NB, 4>(w, x, batch, y, pl, partial, stream);
-  return launch_split_t<NB, 8>(w, x, batch, y, pl, partial, stream);
+  if (batch <= 4) return launch_slice_t<SG, TW, 2>(w, x, batch, y, pl, partial, stream);
+  if (batch <= 8) return launch_slice_t<SG, TW, 4>(w, x, batch, y, pl, partial, stream);
+  return launch_slice_t<SG, TW, 8>(w, x, batch, y, pl, partial, stream);
 }
 
-hipError_t launch_smfmac_split(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+template <int SG>
+hipError_t launch_slice_sg(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
+                           const SplitPlan &pl, f4_t *partial, hipStream_t stream) {
+  if (pl.tw == 1) return launch_slice_tw<SG, 1>(w, x, batch, y, pl, partial, stream);
+  if (pl.tw == 2) return launch_slice_tw<SG, 2>(w, x, batch, y, pl, partial, stream);
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_smfmac_slice(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                                const SplitPlan &pl, void *workspace, hipStream_t stream) {
   f4_t *partial = static_cast<f4_t *>(workspace);
-  switch (pl.ups / 4) {
-    case 1: return launch_split_nb<1>(w, x, batch, y, pl, partial, stream);
-    case 2: return launch_split_nb<2>(w, x, batch, y, pl, partial, stream);
-    case 3: return launch_split_nb<3>(w, x, batch, y, pl, partial, stream);
-    case 4: return launch_split_nb<4>(w, x, batch, y, pl, partial, stream);
-    case 5: return launch_split_nb<5>(w, x, batch, y, pl, partial, stream);
-    case 6: return launch_split_nb<6>(w, x, batch, y, pl, partial, stream);
-    case 7: return launch_split_nb<7>(w, x, batch, y, pl, partial, stream);
-    default: return launch_split_nb<8>(w, x, batch, y, pl, partial, stream);
+  switch (w.group_size) {
+    case 64: return launch_slice_sg<1>(w, x, batch, y, pl, partial, stream);
+    case 128: return launch_slice_sg<2>(w, x, batch, y, pl, partial, stream);
+    case 256: return launch_slice_sg<4>(w, x, batch, y, pl, partial, stream);
+    default: return hipErrorNotSupported;
   }
 }
 
@@ -1360,7 +1414,7 @@ hipError_t launch_nk(const i4s_packed &w, const uint16_t *x, int32_t batch, uint
 
 hipError_t launch_gemv_ws(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                           const SplitPlan &pl, void *workspace, hipStream_t stream) {
-  if (pl.ksplit >= 1) return launch_smfmac_split(w, x, batch, y, pl, workspace, stream);
+  if (pl.ksplit >= 1) return launch_smfmac_slice(w, x, batch, y, pl, workspace, stream);
   return launch_gemv(w, x, batch, y, stream);
 }
 

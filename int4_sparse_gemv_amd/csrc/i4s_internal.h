@@ -84,11 +84,12 @@ hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch,
                        uint16_t *y, hipStream_t stream);
 
 // K split of the batch 2:4 GEMV across blocks (needs a caller workspace):
-// row_groups (of 256 rows) x ksplit blocks, ups 64-column units per slice.
-// The workspace holds the fp32 partial tiles of every slice (scratch: read
-// only after being written in the same call).  ksplit == 0 means "no split
-// kernel" (batch 1, not 2:4, or switched off) and a workspace of 0 bytes;
-// ksplit == 1 runs the split kernel without partials (0 bytes).
+// ksplit slices of kKUnits 64-column units x row_groups groups of
+// kKWaves * tw 16-row tiles.  The workspace holds the fp32 partial tiles of
+// every slice (scratch: read only after being written in the same call).
+// ksplit == 0 means "no split kernel" (batch 1, not 2:4, or a shape the rows
+// kernel runs faster) and a workspace of 0 bytes; ksplit == 1 runs the split
+// kernel without partials (0 bytes).
 // Kernel-choice thresholds.  Fixed when the library is built (nothing read
 // at run time changes which kernel runs); a build may override them with -D
 // to measure the alternatives (python -m int4_sparse_gemv_amd.build --define).
@@ -106,19 +107,21 @@ hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch,
 #ifndef I4S_MATRIX_CORE_MIN_BATCH
 #define I4S_MATRIX_CORE_MIN_BATCH 2
 #endif
+#ifndef I4S_SPLIT_TW2_MIN_BLOCKS
+#define I4S_SPLIT_TW2_MIN_BLOCKS 384
+#endif
 
 // Shapes shared by the batch kernels (i4s_gemv_batch.hip) and the host-side
 // plan of a call (i4s_plan.cpp).
-constexpr int kSWaves = 8;                       // K-split kernel: waves per block
-constexpr int kSTiles = 2;                       // K-split kernel: 16-row tiles per wave
-constexpr int kSRows = 16 * kSTiles * kSWaves;   // K-split kernel: 256 rows per block
-constexpr int kSMaxBlocks = 8;                   // K-split kernel: blocks of 4 units per slice
-constexpr int kSPartialTileBytes = 64 * 16;      // one fp32 16x16 partial tile (64 lanes x 4 floats)
+constexpr int kKWaves = 4;                       // K-split kernel: waves per block
+constexpr int kKUnits = 16;                      // K-split kernel: units per slice
+constexpr int kKXStride = kKUnits * kSegCols + 8;  // K-split kernel: halfs per staged vector
+constexpr int kKPartialTileBytes = 64 * 16;      // one fp32 16x16 partial tile (64 lanes x 4 floats)
 constexpr int kRUnits = 16;                      // rows kernel: units per chunk (the wide form)
 constexpr int kRMaxWaves = 8;                    // rows kernel: waves per block (the wide form)
 
 struct SplitPlan {
-  int row_groups = 0, ksplit = 0, ups = 0;
+  int row_groups = 0, ksplit = 0, tw = 0;
   size_t partial_bytes = 0, workspace_bytes = 0;
 };
 SplitPlan split_plan(const i4s_packed &w, int32_t batch);

@@ -6,36 +6,45 @@
 
 namespace i4s {
 
+// Which batch 2:4 calls the K-split kernel takes (two launches: the sliced
+// product, then the sum of the slices) rather than the rows kernel (one
+// launch, every block over whole rows).  Measured on MI355X, cold, us per
+// call, rows kernel against K split:
+//   the rows kernel does not fit beyond K = 32768;
+//   batch 3-8, long rows on few rows (the rows kernel then runs fewer than
+//   ~190 blocks): 5120x13824 b3 / b4 / b8 14.7 / 14.9 / 16.1 against
+//   14.4 / 14.4 / 14.4; 2048x8192 b8 8.0 / 6.9; 1024x16384 b4 10.4 / 8.1;
+//   but 4096x11008 b4 (256 blocks) 10.8 / 11.3 and 5120x5120 b4 6.9 / 7.9;
+//   batch 9-16 on at most 512 tiles of 16 rows and K >= 5120: 5120x5120
+//   9.5 / 8.3, 4096x11008 15.7 / 12.4, 4096x14336 17.3 / 13.4, 4096x28672
+//   31.5 / 22.1, 8192x8192 13.7 / 13.4; but 4096x4096 6.7 / 7.3 and the
+//   tall layers (13824x5120 13.3 / 15.5, 14336x4096 11.6 / 12.9);
+//   batch 2: the rows kernel (5120x13824 14.5 / 14.8) or the VALU kernel.
+bool split_wanted(int rows, int units, int32_t batch) {
+  const int tiles = (rows + 15) / 16;
+  if (units > 4 * kRMaxWaves * kRUnits) return true;  // K > 32768
+  if (batch >= 3 && batch <= 8) {
+    const int rows_blocks = tiles >= 300 ? (tiles + 1) / 2 : tiles;  // the rows kernel's blocks
+    return units >= 128 && rows_blocks < 192;
+  }
+  if (batch > 8) return units >= 80 && tiles <= 512;
+  return false;
+}
+
 SplitPlan split_plan(const i4s_packed &w, int32_t batch) {
   SplitPlan pl{};
   if (w.n_keep != 2 || batch < 2) return pl;  // no workspace: the other kernels need none
   const int units = w.cols / kSegCols;
-  pl.row_groups = (w.rows + kSRows - 1) / kSRows;
-  // activations of one slice must fit the LDS budget (60 KB, leaving room
-  // for the kernel's static LDS under the 64 KB per-block default)
-  int max_ups = ((60 * 1024 / 2) / batch - 8) / kSegCols / 4 * 4;
-  if (max_ups > 4 * kSMaxBlocks) max_ups = 4 * kSMaxBlocks;  // every block's weights in registers
-  if (max_ups < 4) max_ups = 4;
-  // about one block per CU: 256 / row groups slices, at least 4 units each
-  int ks = (256 + pl.row_groups - 1) / pl.row_groups;
-  if (ks > (units + 3) / 4) ks = (units + 3) / 4;
-  if (ks < 1) ks = 1;
-  int ups = ((units + ks - 1) / ks + 3) / 4 * 4;
-  if (ups > max_ups) ups = max_ups;
-  pl.ups = ups;
-  pl.ksplit = (units + ups - 1) / ups;
-  // When the split pays: where the rows kernel does not fit (K > 32768), and
-  // for K > 16384 at batch > 8 on at most 4096 rows.  Measured on MI355X: on
-  // the 13B-shaped layers the rows kernel is as fast or faster at every batch
-  // (5120x13824 at batch 16: 19.5 us both; everywhere else 5-40 % faster);
-  // with four chunks per wave (K > 16384), hot, us at b4 / b8 / b16:
-  // 4096x28672 rows 17.4 / 20.8 / 29.9 against split 23.3 / 23.1 / 24.7,
-  // 8192x20480 rows 25.5 / 30.6 / 43.3 against split 47.3 / 47.5 / 46.6.
-  // The rows kernel needs no workspace and no second launch.
-  const bool wanted = units > 4 * kRMaxWaves * kRUnits ||
-                      (units > 2 * kRMaxWaves * kRUnits && batch > 8 && w.rows <= 4096);
-  if (!wanted) return SplitPlan{};
-  if (pl.ksplit > 1) pl.partial_bytes = (size_t)pl.ksplit * pl.row_groups * kSWaves * kSTiles * kSPartialTileBytes;
+  if (!split_wanted(w.rows, units, batch)) return pl;
+  const int tiles = (w.rows + 15) / 16;
+  pl.ksplit = (units + kKUnits - 1) / kKUnits;
+  // two tiles per wave where that still leaves >= I4S_SPLIT_TW2_MIN_BLOCKS
+  // blocks, else one
+  const int groups2 = (tiles + 2 * kKWaves - 1) / (2 * kKWaves);
+  pl.tw = (int64_t)pl.ksplit * groups2 >= I4S_SPLIT_TW2_MIN_BLOCKS ? 2 : 1;
+  pl.row_groups = (tiles + kKWaves * pl.tw - 1) / (kKWaves * pl.tw);
+  if (pl.ksplit > 1)
+    pl.partial_bytes = (size_t)pl.ksplit * pl.row_groups * kKWaves * pl.tw * kKPartialTileBytes;
   pl.workspace_bytes = pl.partial_bytes;
   return pl;
 }

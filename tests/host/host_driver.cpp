@@ -281,15 +281,20 @@ void test_workspace_and_noalloc() {
   CHECK(n == 0);
   d.n_keep = 2; d.cols = 20480; d.nnz = 4096ll * 20480 / 2;
   EXPECT(I4S_OK, i4s_run_workspace_size(&d, 16, &n));
-  CHECK(n > 0);  // K > 16384 at batch > 8 on at most 4096 rows
+  CHECK(n > 0);  // batch > 8, K >= 5120 on at most 512 tiles
   EXPECT(I4S_OK, i4s_run_workspace_size(&d, 8, &n));
-  CHECK(n == 0);
+  CHECK(n == 0);  // batch <= 8 on 4096 rows: the rows kernel's 256 blocks
   d.rows = 5000; d.nnz = 5000ll * 20480 / 2;
   EXPECT(I4S_OK, i4s_run_workspace_size(&d, 16, &n));
-  CHECK(n == 0);
-  d.cols = 4096; d.nnz = 5000ll * 4096 / 2;
+  CHECK(n > 0);  // 313 tiles
+  EXPECT(I4S_OK, i4s_run_workspace_size(&d, 8, &n));
+  CHECK(n > 0);  // batch <= 8, the rows kernel's 157 blocks
+  d.rows = 9000; d.nnz = 9000ll * 20480 / 2;
   EXPECT(I4S_OK, i4s_run_workspace_size(&d, 16, &n));
-  CHECK(n == 0);
+  CHECK(n == 0);  // 563 tiles: a tall layer keeps the rows kernel
+  d.rows = 5000; d.cols = 4096; d.nnz = 5000ll * 4096 / 2;
+  EXPECT(I4S_OK, i4s_run_workspace_size(&d, 16, &n));
+  CHECK(n == 0);  // K < 5120
   EXPECT(I4S_ERR_INVALID_ARGUMENT, i4s_run_workspace_size(&d, 16, nullptr));
   EXPECT(I4S_ERR_INVALID_ARGUMENT, i4s_run_workspace_size(&d, 0, &n));
 

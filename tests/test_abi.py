@@ -217,24 +217,45 @@ def test_binding_without_library_fails_loudly(tmp_path):
             B._lib = B._lib_saved
 
 
+def _split_workspace(rows, cols):
+    """Bytes of the K split's fp32 partial tiles: slices of 16 units (1024
+    columns) x groups of 4 waves x tw 16-row tiles, 64 lanes x 16 bytes per
+    tile; tw = 2 where that still leaves >= 384 blocks."""
+    units, tiles = cols // 64, -(-rows // 16)
+    ksplit = -(-units // 16)
+    tw = 2 if ksplit * -(-tiles // 8) >= 384 else 1
+    return ksplit * -(-tiles // (4 * tw)) * 4 * tw * 64 * 16 if ksplit > 1 else 0
+
+
 def test_run_workspace_size_is_host_only_and_planned(lib):
     n = ctypes.c_uint64()
+
+    def size(rows, cols, batch, n_keep=2, g=128):
+        assert B.i4s_run_workspace_size(_desc(rows, cols, n_keep, g), batch, n) == B.I4S_OK
+        return n.value
     # batch 1 and non-2:4 patterns need no workspace
-    assert B.i4s_run_workspace_size(_desc(4096, 4096, 2, 128), 1, n) == B.I4S_OK and n.value == 0
-    assert B.i4s_run_workspace_size(_desc(4096, 4096, 4, 128), 8, n) == B.I4S_OK and n.value == 0
-    # 2:4 batch with K <= 16384: one launch over whole rows, no workspace
-    for batch in (2, 4, 8, 16):
-        assert B.i4s_run_workspace_size(_desc(13824, 5120, 2, 128), batch, n) == B.I4S_OK and n.value == 0
-        assert B.i4s_run_workspace_size(_desc(5120, 13824, 2, 128), batch, n) == B.I4S_OK and n.value == 0
-    # 16384 < K <= 32768: whole rows too, except batch > 8 on at most 4096 rows
-    assert B.i4s_run_workspace_size(_desc(5120, 20480, 2, 128), 16, n) == B.I4S_OK and n.value == 0
-    assert B.i4s_run_workspace_size(_desc(4096, 20480, 2, 128), 8, n) == B.I4S_OK and n.value == 0
-    # the others split K: fp32 partial tiles, 16 tiles x 64 lanes x 16 bytes
-    # per (256-row group, K slice)
-    assert B.i4s_run_workspace_size(_desc(4096, 20480, 2, 128), 16, n) == B.I4S_OK
-    assert n.value > 0 and n.value % (16 * 64 * 16) == 0
-    assert B.i4s_run_workspace_size(_desc(5120, 40960, 2, 128), 4, n) == B.I4S_OK
-    assert n.value > 0 and n.value % (16 * 64 * 16) == 0
+    assert size(4096, 4096, 1) == 0 and size(4096, 4096, 8, n_keep=4) == 0 and size(4096, 4096, 8, n_keep=1) == 0
+    # tall layers and short rows run the one-launch rows kernel at every batch
+    for batch in (2, 3, 4, 8, 16):
+        assert size(13824, 5120, batch) == 0 and size(14336, 4096, batch) == 0 and size(4096, 4096, batch) == 0
+    # batch 2 never splits below K = 32768
+    assert size(5120, 13824, 2) == 0 and size(1024, 16384, 2) == 0
+    # batch 3-8: long rows (K >= 8192) on layers where the rows kernel would
+    # run fewer than 192 blocks split K; 4096 rows (256 blocks) do not
+    for batch in (3, 4, 8):
+        assert size(5120, 13824, batch) == _split_workspace(5120, 13824) == 4587520
+        assert size(2048, 8192, batch) == _split_workspace(2048, 8192) > 0
+        assert size(4096, 11008, batch) == 0 and size(5120, 5120, batch) == 0
+    # batch 9-16: K >= 5120 on at most 512 tiles
+    for batch in (9, 16):
+        for rows, cols in ((5120, 5120), (4096, 11008), (8192, 8192), (4096, 28672)):
+            assert size(rows, cols, batch) == _split_workspace(rows, cols) > 0
+        assert size(8208, 8192, batch) == 0  # 513 tiles
+    # beyond K = 32768 the rows kernel does not fit: every batch >= 2 splits
+    for batch in (2, 4, 16):
+        assert size(5120, 40960, batch) == _split_workspace(5120, 40960) > 0
+    # a single slice (K <= 1024) needs no partials
+    assert size(64, 1024, 16) == 0
     assert B.i4s_run_workspace_size(_desc(), 0, n) == B.I4S_ERR_INVALID_ARGUMENT
     assert lib.i4s_run_workspace_size(ctypes.byref(_desc()), 2, None) == B.I4S_ERR_INVALID_ARGUMENT
 
