@@ -201,8 +201,9 @@ i4s_status i4s_run(const i4s_packed *w /* host */, const uint16_t *x_fp16,
  * K > 32768 (beyond the one-launch kernel) at any batch >= 2; batch 3-8 with
  * K >= 8192 where the one-launch kernel would run fewer than 192 blocks
  * (fewer than 3072 rows, or 4800 to 6143 rows, where it takes two 16-row
- * tiles per block); batch 9-16 with K >= 5120 on at most 8192 rows; and not
- * when K <= 1024 (a single slice).  Host-only and pure.  Errors:
+ * tiles per block), and at batch 8 up to 256 blocks (4096 rows); batch 9-16
+ * with K >= 5120 on at most 8192 rows; and not when K <= 1024 (a single
+ * slice).  Host-only and pure.  Errors:
  * I4S_ERR_INVALID_ARGUMENT (descriptor inconsistent, batch out of range,
  * bytes == NULL). */
 i4s_status i4s_run_workspace_size(const i4s_packed *w /* host */, int32_t batch,

@@ -44,6 +44,12 @@ HIPCC_FLAGS = [
     # the GEMV's first loads do not wait for a scalar memory round trip (the
     # code object keeps a fallback that loads them itself)
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
+    # matrix instructions read and write their accumulators in VGPRs: left to
+    # its heuristics the compiler put the K-split kernel's per-group tiles in
+    # AGPRs, and every group then cost 4 v_accvgpr_read + 4 v_accvgpr_write
+    # (8 of ~26 VALU instructions per unit); the other kernels already used
+    # VGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
 

@@ -13,8 +13,11 @@ namespace i4s {
 //   the rows kernel does not fit beyond K = 32768;
 //   batch 3-8, long rows on few rows (the rows kernel then runs fewer than
 //   ~190 blocks): 5120x13824 b3 / b4 / b8 14.7 / 14.9 / 16.1 against
-//   14.4 / 14.4 / 14.4; 2048x8192 b8 8.0 / 6.9; 1024x16384 b4 10.4 / 8.1;
-//   but 4096x11008 b4 (256 blocks) 10.8 / 11.3 and 5120x5120 b4 6.9 / 7.9;
+//   14.4 / 14.3 / 14.4; 2048x8192 b8 8.0 / 6.9; 1024x16384 b4 10.4 / 8.1;
+//   but 4096x11008 b4 (256 blocks) 10.8 / 11.3, 4096x14336 b6 11.4 / 12.2
+//   and 5120x5120 b4 6.9 / 7.9; at batch 8 also 256 blocks: 4096x11008
+//   12.2 / 10.6, 4096x14336 12.9 / 12.1, 4096x28672 22.4 / 19.1, 3072x8192
+//   8.4 / 7.9 (8192x8192 11.5 / 11.7);
 //   batch 9-16 on at most 512 tiles of 16 rows and K >= 5120: 5120x5120
 //   9.5 / 8.3, 4096x11008 15.7 / 12.4, 4096x14336 17.3 / 13.4, 4096x28672
 //   31.5 / 22.1, 8192x8192 13.7 / 13.4; but 4096x4096 6.7 / 7.3 and the
@@ -25,7 +28,7 @@ bool split_wanted(int rows, int units, int32_t batch) {
   if (units > 4 * kRMaxWaves * kRUnits) return true;  // K > 32768
   if (batch >= 3 && batch <= 8) {
     const int rows_blocks = tiles >= 300 ? (tiles + 1) / 2 : tiles;  // the rows kernel's blocks
-    return units >= 128 && rows_blocks < 192;
+    return units >= 128 && (rows_blocks < 192 || (batch == 8 && rows_blocks <= 256));
   }
   if (batch > 8) return units >= 80 && tiles <= 512;
   return false;

@@ -283,7 +283,9 @@ void test_workspace_and_noalloc() {
   EXPECT(I4S_OK, i4s_run_workspace_size(&d, 16, &n));
   CHECK(n > 0);  // batch > 8, K >= 5120 on at most 512 tiles
   EXPECT(I4S_OK, i4s_run_workspace_size(&d, 8, &n));
-  CHECK(n == 0);  // batch <= 8 on 4096 rows: the rows kernel's 256 blocks
+  CHECK(n > 0);  // batch 8 on 4096 rows: the rows kernel's 256 blocks
+  EXPECT(I4S_OK, i4s_run_workspace_size(&d, 4, &n));
+  CHECK(n == 0);  // ... but not below batch 8
   d.rows = 5000; d.nnz = 5000ll * 20480 / 2;
   EXPECT(I4S_OK, i4s_run_workspace_size(&d, 16, &n));
   CHECK(n > 0);  // 313 tiles

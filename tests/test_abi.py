@@ -241,11 +241,15 @@ def test_run_workspace_size_is_host_only_and_planned(lib):
     # batch 2 never splits below K = 32768
     assert size(5120, 13824, 2) == 0 and size(1024, 16384, 2) == 0
     # batch 3-8: long rows (K >= 8192) on layers where the rows kernel would
-    # run fewer than 192 blocks split K; 4096 rows (256 blocks) do not
+    # run fewer than 192 blocks split K; 4096 rows (256 blocks) only at batch 8
     for batch in (3, 4, 8):
         assert size(5120, 13824, batch) == _split_workspace(5120, 13824) == 4587520
         assert size(2048, 8192, batch) == _split_workspace(2048, 8192) > 0
-        assert size(4096, 11008, batch) == 0 and size(5120, 5120, batch) == 0
+        assert size(5120, 5120, batch) == 0
+    for batch in (3, 4, 7):
+        assert size(4096, 11008, batch) == 0 and size(8208, 8192, batch) == 0
+    assert size(4096, 11008, 8) == _split_workspace(4096, 11008) > 0
+    assert size(8208, 8192, 8) == 0  # 257 blocks
     # batch 9-16: K >= 5120 on at most 512 tiles
     for batch in (9, 16):
         for rows, cols in ((5120, 5120), (4096, 11008), (8192, 8192), (4096, 28672)):
