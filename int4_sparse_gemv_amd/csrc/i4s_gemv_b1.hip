@@ -90,6 +90,55 @@ __device__ inline float unit_dot_b1(const UnitRegs<NK> &u, const uint32_t (&xr)[
   return g;
 }
 
+// unit_dot_b1 in two steps, for 2:4 and 1:4: the activations each kept
+// weight multiplies (they depend on the codes and x only, so they can be
+// picked while the unit's vals are still on their way), then the products
+// (the same dot2 operations in the same order: the same bits).
+template <int NK>
+constexpr int kPicked = NK == 2 ? 16 : 8;  // activation pairs per unit
+template <int NK>
+__device__ inline void unit_pick_b1(const UnitRegs<NK> &u, const uint32_t (&xr)[32], const uint32_t *lut,
+                                    uint32_t (&xp)[kPicked<NK>]) {
+  if constexpr (NK == 2) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t me = (u.c[c] << 2) & 0x3C3C3C3Cu;
+      uint32_t mo = (u.c[c] >> 2) & 0x3C3C3C3Cu;
+      opaque(me);
+      opaque(mo);
+#pragma unroll
+      for (int gi = 0; gi < 8; ++gi) {
+        const uint32_t m = (gi & 1) ? mo : me;
+        const uint32_t sel = lut_read(lut, (m >> (8 * (gi >> 1))) & 0xFFu);
+        const int grp = 8 * c + gi;
+        xp[grp] = __builtin_amdgcn_perm(xr[2 * grp + 1], xr[2 * grp], sel);
+      }
+    }
+  } else {
+    const uint32_t me = (u.c[0] << 3) & 0x78787878u;
+    const uint32_t mo = (u.c[0] >> 1) & 0x78787878u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t m = (k & 1) ? mo : me;
+      const u32x2_lut_t sel = lut_read2(lut, (m >> (8 * (k >> 1))) & 0xFFu);
+      xp[k] = __builtin_amdgcn_perm(xr[4 * k + 1], xr[4 * k], sel.x) |
+              __builtin_amdgcn_perm(xr[4 * k + 3], xr[4 * k + 2], sel.y);
+    }
+  }
+}
+template <int NK>
+__device__ inline float unit_products_b1(const UnitRegs<NK> &u, const uint32_t (&xp)[kPicked<NK>]) {
+  float g = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kPicked<NK> / 4; ++j) {  // vals word j: activation pairs 4j..4j+3
+    h2_t q[4];
+    dequant_word(u.v[j], q);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) g = __builtin_amdgcn_fdot2(q[p], as_h2(xp[4 * j + p]), g, false);
+  }
+  return g;
+}
+
 // The 64 activations of unit u from the block's LDS copy (eight 16-byte reads).
 __device__ inline void lds_unit_x(const uint16_t *xs, int u, uint32_t (&xr)[32]) {
   const uint4 *xv = reinterpret_cast<const uint4 *>(xs + __umul24((uint32_t)u, kStrideB1));
@@ -268,16 +317,38 @@ __device__ __forceinline__ void b1_direct_body(
     srow[r] = (uint32_t)rr * ngroups;
   }
   // In the order the decode consumes them: unit by unit, the rows of a unit
-  // together.
+  // together.  With one row per wave (2:4 and 1:4), every unit's codes go
+  // first: the activations a unit's weights multiply are then picked while
+  // its vals are still streaming in, and what is left after the last vals
+  // arrive is the dequantization and the dot products.  (Per-wave clock
+  // stamps on a 4096x4096 2:4 layer: the decode after the weights' arrival
+  // took 0.56 us at the median, the last 0.7 us of the launch.)
+  constexpr bool kCodesFirst = RPW == 1 && NK != 4;
   UnitRegs<NK> wr[UPL][RPW];
+  if constexpr (kCodesFirst) {
 #pragma unroll
-  for (int k = 0; k < UPL; ++k) {
-    const int u = min(lane + 64 * k, units - 1);  // lanes past the row re-read its last unit
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-      load_unit_nt<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
-                       srow[r] + ((uint32_t)u >> sg_shift));
+    for (int k = 0; k < UPL; ++k) {
+      const int u = min(lane + 64 * k, units - 1);  // lanes past the row re-read its last unit
+      load_codes_nt<NK>(wr[k][0], codes, rstart[0] + (uint32_t)u * 16 * NK);
+    }
     issue_fence();
+#pragma unroll
+    for (int k = 0; k < UPL; ++k) {
+      const int u = min(lane + 64 * k, units - 1);
+      load_vals_scale_nt<NK>(wr[k][0], vals, scales, rstart[0] + (uint32_t)u * 16 * NK,
+                             srow[0] + ((uint32_t)u >> sg_shift));
+      issue_fence();
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < UPL; ++k) {
+      const int u = min(lane + 64 * k, units - 1);  // lanes past the row re-read its last unit
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        load_unit_nt<NK>(wr[k][r], vals, codes, scales, rstart[r] + (uint32_t)u * 16 * NK,
+                         srow[r] + ((uint32_t)u >> sg_shift));
+      issue_fence();
+    }
   }
   // row_ptr: a vector load, issued last and needed only after decoding.  (A
   // scalar load would share its counter with LDS and, returning out of
@@ -313,10 +384,23 @@ __device__ __forceinline__ void b1_direct_body(
   // moved the dense weight loads down into the decode block, after the
   // barrier).  Two or more rows keep the branch: without it their register
   // count rose from ~75 to ~120, too many for three blocks per CU.
+  uint32_t xp[kCodesFirst ? kPicked<NK> : 1];
+  if constexpr (kCodesFirst) {
+    unit_pick_b1<NK>(wr[0][0], xr0, lut, xp);  // waits for the codes only
+    __builtin_amdgcn_sched_barrier(0);          // every pick before the first wait for vals
+  }
 #pragma unroll
   for (int k = 0; k < UPL; ++k) {
     const int u = lane + 64 * k;
-    if constexpr (RPW == 1) {
+    if constexpr (kCodesFirst) {
+      const float a = fmaf(fp16_bits_to_float(wr[k][0].s), unit_products_b1<NK>(wr[k][0], xp), acc[0]);
+      acc[0] = u < units ? a : acc[0];
+      if (k + 1 < UPL) {  // the next unit's picks, while its vals arrive
+        uint32_t xr[32];
+        lds_unit_x(xs, min(u + 64, units - 1), xr);
+        unit_pick_b1<NK>(wr[k + 1][0], xr, lut, xp);
+      }
+    } else if constexpr (RPW == 1) {
       uint32_t xr[32];
       if (k == 0) {
 #pragma unroll

@@ -227,6 +227,32 @@ __device__ inline void lds_barrier() {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// The two halves of load_unit_nt, for kernels that issue every unit's codes
+// before any unit's vals (the codes of 2:4 and 1:4 only).
+template <int NK>
+__device__ inline void load_codes_nt(UnitRegs<NK> &r, const uint16_t *__restrict__ codes, uint32_t elem0) {
+  if constexpr (NK == 1) {
+    r.c[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(codes + (elem0 >> 3)));
+  } else if constexpr (NK == 2) {
+    const u32x2_t c = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(codes + (elem0 >> 3)));
+    r.c[0] = c.x; r.c[1] = c.y;
+  }
+}
+template <int NK>
+__device__ inline void load_vals_scale_nt(UnitRegs<NK> &r, const uint8_t *__restrict__ vals,
+                                          const uint16_t *__restrict__ scales, uint32_t elem0, uint32_t scale_idx) {
+  const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(vals + (elem0 >> 1));
+  if constexpr (NK == 1) {
+    const u32x2_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(vp));
+    r.v[0] = a.x; r.v[1] = a.y;
+  } else {
+    const u32x4_t a = __builtin_nontemporal_load(vp);
+    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+  }
+  r.s = __builtin_nontemporal_load(
+      reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(scales) + 2u * scale_idx));
+}
+
 template <int NK>
 __device__ inline void load_unit_nt(UnitRegs<NK> &r, const uint8_t *__restrict__ vals,
                                     const uint16_t *__restrict__ codes,
