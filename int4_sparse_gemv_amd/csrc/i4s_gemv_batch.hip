@@ -470,9 +470,12 @@ __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
 
 // Geometry of a chunk of U units (16 or 8) in a wave's LDS area for one
 // tile: vals [16 rows][U + 1] (the extra column spreads the banks), codes
-// [16 rows][U + 1], scales
-// [U units][16 rows].  One load instruction covers 64 / U rows of U units
-// (4 rows x 256 bytes or 8 rows x 128 bytes of vals).
+// [16 rows][U + 1], scales [U units][kScaleStride] (16 rows and 4 halfs of
+// padding: the 64 lanes' 2-byte writes of one load, unit lu of rows
+// 4k..4k+3, then fall in distinct banks -- with 16 halfs per unit units lu
+// and lu + 8 shared banks, 28 % of the LDS cycles in conflict -- and the
+// 8-byte reads of 4 rows stay aligned).  One load instruction covers 64 / U
+// rows of U units (4 rows x 256 bytes or 8 rows x 128 bytes of vals).
 // A dense unit-row: 64 nibbles, 32 bytes.
 struct DenseVals {
   u32x4_t lo, hi;
@@ -484,7 +487,8 @@ struct RowsGeom {
   // vals per unit-row: 16 bytes (2:4), 8 (1:4: the 2:4 layout, half used), 32 (dense)
   static constexpr int kValsBytes = 16 * kStride * (NK == 4 ? 32 : 16);
   static constexpr int kCodesBytes = NK == 4 ? 0 : 16 * kStride * 8;
-  static constexpr int kTileLds = kValsBytes + kCodesBytes + U * 16 * 2;  // 2:4 and 1:4: 7040 / 3712 bytes
+  static constexpr int kScaleStride = 20;
+  static constexpr int kTileLds = kValsBytes + kCodesBytes + U * kScaleStride * 2;  // 2:4 and 1:4: 7168 / 3776 bytes
   static constexpr int kRowsPerLoad = 64 / U;
   static constexpr int kLoads = 16 / kRowsPerLoad;  // load instructions per tile and chunk
   static constexpr int kBlocks = U / 4;             // 4-unit blocks per chunk
@@ -556,7 +560,7 @@ __device__ __forceinline__ void rows_body(
   uint8_t *wl = lds + wave * TPW * Geo::kTileLds;  // the wave's areas, one per tile
   auto lv_of = [&](int t) { return reinterpret_cast<vals_t *>(wl + t * Geo::kTileLds); };  // [16 rows][ST]
   auto lc_of = [&](int t) { return reinterpret_cast<codes_t *>(wl + t * Geo::kTileLds + Geo::kValsBytes); };
-  auto lsc_of = [&](int t) {                                                                // [U units][16 rows]
+  auto lsc_of = [&](int t) {                                                     // [U units][Geo::kScaleStride]
     return reinterpret_cast<uint16_t *>(wl + t * Geo::kTileLds + Geo::kValsBytes + Geo::kCodesBytes);
   };
 
@@ -657,7 +661,7 @@ __device__ __forceinline__ void rows_body(
         for (int k = 0; k < NL; ++k) {
           lv[(RL * k + lr) * ST + lu] = wv[t][k];
           if constexpr (NK != 4) lc[(RL * k + lr) * ST + lu] = wc[t][k];
-          lsc[lu * 16 + RL * k + lr] = unit_ok ? wsc[t][k] : (uint16_t)0;
+          lsc[lu * Geo::kScaleStride + RL * k + lr] = unit_ok ? wsc[t][k] : (uint16_t)0;
         }
       }
       wave_lds_sync();
@@ -701,7 +705,7 @@ __device__ __forceinline__ void rows_body(
           u32x2_t sv[4 / SG];
 #pragma unroll
           for (int g = 0; g < 4 / SG; ++g)
-            sv[g] = *reinterpret_cast<const u32x2_t *>(&lsc[(4 * bb + SG * g + SG - 1) * 16 + 4 * lq]);
+            sv[g] = *reinterpret_cast<const u32x2_t *>(&lsc[(4 * bb + SG * g + SG - 1) * Geo::kScaleStride + 4 * lq]);
           f4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
@@ -1347,7 +1351,7 @@ hipError_t launch_smfmac(const i4s_packed &w, const uint16_t *x, int32_t batch, 
 template <int SG, int TW, int RN>
 hipError_t launch_slice_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y,
                           const SplitPlan &pl, f4_t *partial, hipStream_t stream) {
-  const size_t lds = (size_t)batch * kKXStride * 2 + kKWaves * RowsGeom<kKUnits>::kTileLds;  // <= 61,184 bytes
+  const size_t lds = (size_t)batch * kKXStride * 2 + kKWaves * RowsGeom<kKUnits>::kTileLds;  // <= 61,952 bytes
   const int sg_shift = SG == 1 ? 0 : (SG == 2 ? 1 : 2);
   hipLaunchKernelGGL((gemv_smfmac_slice_kernel<SG, TW, RN>), dim3((unsigned)pl.ksplit, (unsigned)pl.row_groups),
                      dim3(64 * kKWaves), lds, stream, w.rows, w.cols / kSegCols, sg_shift, w.row_ptr, w.vals,

@@ -115,7 +115,12 @@ hipError_t launch_gemv(const i4s_packed &w, const uint16_t *x, int32_t batch,
 // plan of a call (i4s_plan.cpp).
 constexpr int kKWaves = 4;                       // K-split kernel: waves per block
 constexpr int kKUnits = 16;                      // K-split kernel: units per slice
-constexpr int kKXStride = kKUnits * kSegCols + 8;  // K-split kernel: halfs per staged vector
+// K-split kernel: halfs per staged vector, 16 halfs of padding: 520 dwords,
+// 8 banks on per vector, so the B reads of 8 vectors x 2 column quarters in
+// one LDS pass fall in distinct banks (8 halfs of padding put vector v + 1
+// of quarter q on the banks of vector v of quarter q + 1: 24-36 % of the LDS
+// cycles in conflict at batch 4-8)
+constexpr int kKXStride = kKUnits * kSegCols + 16;
 constexpr int kKPartialTileBytes = 64 * 16;      // one fp32 16x16 partial tile (64 lanes x 4 floats)
 constexpr int kRUnits = 16;                      // rows kernel: units per chunk (the wide form)
 constexpr int kRMaxWaves = 8;                    // rows kernel: waves per block (the wide form)
