@@ -607,12 +607,26 @@ def kernel_label(m, batch):
         return f"gemv_b1_kernel<{m.n_keep},{rpw},8>"
     if batch == 2 and m.rows <= 8192 and units <= 64:
         return f"gemv_bv_direct_kernel<{m.n_keep},2,{(units + 63) // 64}>"
-    long_split = units > 256 and batch > 8 and m.rows <= 4096
-    if units <= 512 and not (m.n_keep == 2 and long_split):
+    if m.n_keep == 2 and _split_wanted(m.rows, units, batch):
+        return "gemv_smfmac_slice_kernel + gemv_slice_reduce_kernel"
+    if units <= 512:
         return f"gemv_smfmac_rows_kernel<{m.n_keep},...>"
-    if m.n_keep == 2:
-        return "gemv_smfmac_split_kernel + gemv_split_reduce_kernel"
     return f"gemv_kernel<{m.n_keep},BT>=" + str(batch)
+
+
+def _split_wanted(rows, units, batch):
+    """The library's rule for the 2:4 K split at batch >= 2 (i4s_plan.cpp,
+    restated for the label; the workspace size the library reports is the
+    authority)."""
+    tiles = (rows + 15) // 16
+    if units > 512:
+        return True
+    if 3 <= batch <= 8:
+        rows_blocks = (tiles + 1) // 2 if tiles >= 300 else tiles
+        return units >= 128 and (rows_blocks < 192 or (batch == 8 and rows_blocks <= 256))
+    if batch > 8:
+        return units >= 80 and tiles <= 512
+    return False
 
 
 def run_suite(R, args, floor_shape):

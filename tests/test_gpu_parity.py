@@ -543,7 +543,10 @@ def test_run_on_side_stream():
     # batch 2 on the VALU kernel (each unit decoded once for both vectors)
     (2, 2, 37, 5120), (1, 2, 37, 5120), (4, 2, 37, 5120),
     # more than 8192 rows: two rows per wave at batch 1
-    (2, 1, 8200, 1024), (1, 1, 8200, 1024), (4, 1, 8200, 2048)])
+    (2, 1, 8200, 1024), (1, 1, 8200, 1024), (4, 1, 8200, 2048),
+    # layers whose workspace path splits K (batch 3-8 with long rows on few
+    # rows, batch 16, K > 32768): the split kernel's per-lane recompute
+    (2, 8, 300, 8192), (2, 16, 37, 13824), (2, 4, 40, 40960)])
 def test_row_ptr_is_honoured(n_keep, batch, rows, cols):
     """Rows stored in reverse order, described only by row_ptr, give the same y
     (bit for bit on the VALU kernels, within the tolerance on the matrix cores)."""
@@ -583,7 +586,10 @@ def test_row_ptr_is_honoured(n_keep, batch, rows, cols):
     (6000, 2048, 6, 128), (5000, 3072, 3, 64),
     # K > 16384: four chunks per wave at batch <= 8; the workspace path splits
     # K across blocks at batch > 8 on few rows and for any batch beyond 32768
-    (96, 20480, 5, 64), (300, 24576, 16, 128), (40, 32768, 9, 256), (64, 40960, 4, 128)])
+    (96, 20480, 5, 64), (300, 24576, 16, 128), (40, 32768, 9, 256), (64, 40960, 4, 128),
+    # K split with two tiles per wave, a partial last tile and a partial last
+    # row group (and at 13824 columns a half-width last slice)
+    (5000, 13824, 8, 256), (8100, 7168, 16, 64)])
 def test_batch_paths_with_and_without_workspace(rows, cols, batch, g):
     """i4s_run (no workspace) and i4s_run_ws (K split across blocks where the
     layer's plan uses it) both meet the tolerance for every group size; the
