@@ -468,32 +468,11 @@ __global__ __launch_bounds__(64 * kMWaves) void gemv_smfmac_kernel(
 // the bytes are half.
 
 
-// Geometry of a chunk of U units (16 or 8) in a wave's LDS area for one
-// tile: vals [16 rows][U + 1] (the extra column spreads the banks), codes
-// [16 rows][U + 1], scales [U units][kScaleStride] (16 rows and 4 halfs of
-// padding: the 64 lanes' 2-byte writes of one load, unit lu of rows
-// 4k..4k+3, then fall in distinct banks -- with 16 halfs per unit units lu
-// and lu + 8 shared banks, 28 % of the LDS cycles in conflict -- and the
-// 8-byte reads of 4 rows stay aligned).  One load instruction covers 64 / U
-// rows of U units (4 rows x 256 bytes or 8 rows x 128 bytes of vals).
 // A dense unit-row: 64 nibbles, 32 bytes.
 struct DenseVals {
   u32x4_t lo, hi;
 };
 
-template <int U, int NK = 2>
-struct RowsGeom {
-  static constexpr int kStride = U + 1;
-  // vals per unit-row: 16 bytes (2:4), 8 (1:4: the 2:4 layout, half used), 32 (dense)
-  static constexpr int kValsBytes = 16 * kStride * (NK == 4 ? 32 : 16);
-  static constexpr int kCodesBytes = NK == 4 ? 0 : 16 * kStride * 8;
-  static constexpr int kScaleStride = 20;
-  static constexpr int kTileLds = kValsBytes + kCodesBytes + U * kScaleStride * 2;  // 2:4 and 1:4: 7168 / 3776 bytes
-  static constexpr int kRowsPerLoad = 64 / U;
-  static constexpr int kLoads = 16 / kRowsPerLoad;  // load instructions per tile and chunk
-  static constexpr int kBlocks = U / 4;             // 4-unit blocks per chunk
-  static constexpr int kMaxWaves = U == 8 ? 16 : 8;
-};
 constexpr int kRStride = kRUnits + 1;        // LDS row stride in elements (the wide form)
 constexpr int kRValsBytes = RowsGeom<16>::kValsBytes;
 constexpr int kRCodesBytes = RowsGeom<16>::kCodesBytes;
@@ -1178,52 +1157,6 @@ bool rows_kernel_fits(const i4s_packed &w) {
 // Measured on MI355X: two tiles win from 320 tiles up (5120 rows: 7.7 / 8.0 /
 // 8.8 us against 7.8 / 9.0 / 12.3 at batch 4 / 8 / 16), one tile wins at 256
 // (4096 rows, 1:4: 5.2 / 5.5 / 6.7 against 6.9 / 7.1 / 7.9).
-struct RowsShape {
-  int u, cpw, waves, tpw;
-  size_t lds;
-};
-
-// Chunk width: 16 units (4 rows x 256 bytes per load) by default; 8 units
-// (8 rows x 128 bytes, twice the waves per block, half the work each) when
-// two-tile blocks are fewer than the compute units and the batch is at most
-// 8.  Measured: 5120x5120 at batch 4 / 8 / 16: 7.45 / 7.76 / 8.90 us with 16,
-// 6.63 / 7.32 / 9.01 with 8; 13824x5120 (432 blocks): 10.8 / 11.5 / 14.4 with
-// 16, 11.6 / 12.9 / 16.5 with 8.
-// want_u (8 or 16) fixes the chunk width; 0 chooses it.
-RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want_u = 0) {
-  RowsShape r;
-  // Four tiles per wave (8-unit chunks, one per wave) for batches above 8
-  // on tall layers: each B fragment then feeds four tiles, halving the
-  // activation reads through L2 against two tiles.  Cold, us at b16:
-  // 13824x5120 15.4 -> 13.2, 11008x4096 12.0 -> 10.9; at b8 and below, and
-  // with fewer than ~160 four-tile blocks, two tiles per wave are as fast or
-  // faster (5120x5120 at b16: 9.1 against 12.0).  The block's LDS (waves x
-  // 4 x 3.7 KB) caps K at 5632.
-  const int tile8 = n_keep == 1 ? RowsGeom<8, 1>::kTileLds : RowsGeom<8>::kTileLds;
-  const bool four = n_keep != 4 && batch > 8 && total_tiles >= 640 && want_u != 16 &&
-                    (size_t)((units + 7) / 8) * 4 * tile8 <= 160 * 1024;
-  r.tpw = four ? 4 : (total_tiles >= 300 ? 2 : 1);
-  r.u = ((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) || r.tpw == 4) ? 8 : 16;
-  if (want_u) r.u = want_u;
-  // 8-unit chunks only with one chunk per wave (K <= 8192): two chunks per
-  // wave of the 16-wave form would not fit its 128 registers
-  if ((units + 7) / 8 > RowsGeom<8>::kMaxWaves) r.u = 16;
-  const int maxw = r.u == 8 ? RowsGeom<8>::kMaxWaves : RowsGeom<16>::kMaxWaves;
-  const int chunks = (units + r.u - 1) / r.u;
-  r.cpw = chunks > 2 * maxw ? 4 : (chunks > maxw ? 2 : 1);
-  // dense rows are twice the bytes: two chunks of two tiles would spill; four
-  // chunks per wave (K > 16384) always take one tile per wave
-  if ((n_keep == 4 && r.cpw == 2) || r.cpw == 4) r.tpw = 1;
-  // four tiles per wave: the 8-unit one-chunk form of 2:4 and 1:4 only (LDS)
-  if (r.tpw == 4 && (r.u != 8 || r.cpw != 1 || n_keep == 4)) r.tpw = 2;
-  r.waves = (chunks + r.cpw - 1) / r.cpw;
-  const int tile_lds = n_keep == 4 ? (r.u == 8 ? RowsGeom<8, 4>::kTileLds : RowsGeom<16, 4>::kTileLds)
-                                    : (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);
-  if (r.tpw == 4 && (size_t)r.waves * 4 * tile_lds > 160 * 1024) r.tpw = 2;  // LDS per workgroup
-  r.lds = (size_t)r.waves * r.tpw * tile_lds;
-  return r;
-}
-
 // Dynamic LDS above 64 KB needs the kernel's limit raised (once per kernel
 // and device; gfx950 allows 160 KB per workgroup).  Setting it again is
 // harmless, so concurrent first calls need no lock.
@@ -1268,26 +1201,35 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
 }
 
 // Call FN<NK, cpw, SG, tpw, U>(args...) for the shape's run-time values.
+// Every combination rows_shape can return is listed; anything else (and a
+// group size other than 64, 128 or 256) is refused rather than run on an
+// instantiation built for another shape.
 #define I4S_ROWS_SG(FN, C, T, U, ...)                                                    \
   do {                                                                                   \
     if (sg_shift == 0) return FN<NK, C, 1, T, U>(__VA_ARGS__);                           \
     if (sg_shift == 1) return FN<NK, C, 2, T, U>(__VA_ARGS__);                           \
-    return FN<NK, C, 4, T, U>(__VA_ARGS__);                                              \
+    if (sg_shift == 2) return FN<NK, C, 4, T, U>(__VA_ARGS__);                           \
+    return hipErrorNotSupported;                                                         \
   } while (0)
 #define I4S_ROWS_DISPATCH(FN, ...)                                                       \
   do {                                                                                   \
     if (r.u == 16) {                                                                     \
-      if (r.cpw == 4) I4S_ROWS_SG(FN, 4, 1, 16, __VA_ARGS__);                           \
+      if (r.cpw == 4 && r.tpw == 1) I4S_ROWS_SG(FN, 4, 1, 16, __VA_ARGS__);             \
       if (r.cpw == 1 && r.tpw == 1) I4S_ROWS_SG(FN, 1, 1, 16, __VA_ARGS__);             \
-      if (r.cpw == 1) I4S_ROWS_SG(FN, 1, 2, 16, __VA_ARGS__);                           \
-      if (r.tpw == 1 || NK == 4) I4S_ROWS_SG(FN, 2, 1, 16, __VA_ARGS__);  /* dense: 1 */ \
-      if constexpr (NK != 4) I4S_ROWS_SG(FN, 2, 2, 16, __VA_ARGS__);                    \
+      if (r.cpw == 1 && r.tpw == 2) I4S_ROWS_SG(FN, 1, 2, 16, __VA_ARGS__);             \
+      if (r.cpw == 2 && r.tpw == 1) I4S_ROWS_SG(FN, 2, 1, 16, __VA_ARGS__);             \
+      if constexpr (NK != 4) {                                                           \
+        if (r.cpw == 2 && r.tpw == 2) I4S_ROWS_SG(FN, 2, 2, 16, __VA_ARGS__);           \
+      }                                                                                  \
     }                                                                                    \
-    if (r.tpw == 1) I4S_ROWS_SG(FN, 1, 1, 8, __VA_ARGS__);                              \
-    if constexpr (NK != 4) {                                                             \
-      if (r.tpw == 4) I4S_ROWS_SG(FN, 1, 4, 8, __VA_ARGS__);                            \
+    if (r.u == 8 && r.cpw == 1) {                                                        \
+      if (r.tpw == 1) I4S_ROWS_SG(FN, 1, 1, 8, __VA_ARGS__);                            \
+      if (r.tpw == 2) I4S_ROWS_SG(FN, 1, 2, 8, __VA_ARGS__);                            \
+      if constexpr (NK != 4) {                                                           \
+        if (r.tpw == 4) I4S_ROWS_SG(FN, 1, 4, 8, __VA_ARGS__);                          \
+      }                                                                                  \
     }                                                                                    \
-    I4S_ROWS_SG(FN, 1, 2, 8, __VA_ARGS__);                                              \
+    return hipErrorNotSupported;                                                         \
   } while (0)
 
 template <int NK>

@@ -125,6 +125,40 @@ constexpr int kKPartialTileBytes = 64 * 16;      // one fp32 16x16 partial tile 
 constexpr int kRUnits = 16;                      // rows kernel: units per chunk (the wide form)
 constexpr int kRMaxWaves = 8;                    // rows kernel: waves per block (the wide form)
 
+// Geometry of a chunk of U units (16 or 8) in a wave's LDS area for one
+// tile: vals [16 rows][U + 1] (the extra column spreads the banks), codes
+// [16 rows][U + 1], scales [U units][kScaleStride] (16 rows and 4 halfs of
+// padding: the 64 lanes' 2-byte writes of one load, unit lu of rows
+// 4k..4k+3, then fall in distinct banks -- with 16 halfs per unit units lu
+// and lu + 8 shared banks, 28 % of the LDS cycles in conflict -- and the
+// 8-byte reads of 4 rows stay aligned).  One load instruction covers 64 / U
+// rows of U units (4 rows x 256 bytes or 8 rows x 128 bytes of vals).
+template <int U, int NK = 2>
+struct RowsGeom {
+  static constexpr int kStride = U + 1;
+  // vals per unit-row: 16 bytes (2:4), 8 (1:4: the 2:4 layout, half used), 32 (dense)
+  static constexpr int kValsBytes = 16 * kStride * (NK == 4 ? 32 : 16);
+  static constexpr int kCodesBytes = NK == 4 ? 0 : 16 * kStride * 8;
+  static constexpr int kScaleStride = 20;
+  static constexpr int kTileLds = kValsBytes + kCodesBytes + U * kScaleStride * 2;  // 2:4 and 1:4: 7168 / 3776 bytes
+  static constexpr int kRowsPerLoad = 64 / U;
+  static constexpr int kLoads = 16 / kRowsPerLoad;  // load instructions per tile and chunk
+  static constexpr int kBlocks = U / 4;             // 4-unit blocks per chunk
+  static constexpr int kMaxWaves = U == 8 ? 16 : 8;
+};
+
+// Launch shape of the rows kernel for one layer: chunk width u (8 or 16
+// units), chunks per wave cpw, waves per block, 16-row tiles per wave tpw and
+// the block's dynamic LDS.  rows_shape only returns combinations that the
+// batch kernels instantiate: u 16 with (cpw, tpw) in {(1, 1), (1, 2), (2, 1),
+// (2, 2) but not dense, (4, 1)}; u 8 with cpw 1 and tpw in {1, 2, 4 but not
+// dense}.  units must satisfy the rows kernel's limit (K <= 32768).
+struct RowsShape {
+  int u = 0, cpw = 0, waves = 0, tpw = 0;
+  size_t lds = 0;
+};
+RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want_u = 0);
+
 struct SplitPlan {
   int row_groups = 0, ksplit = 0, tw = 0;
   size_t partial_bytes = 0, workspace_bytes = 0;

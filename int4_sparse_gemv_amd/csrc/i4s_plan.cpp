@@ -52,4 +52,45 @@ SplitPlan split_plan(const i4s_packed &w, int32_t batch) {
   return pl;
 }
 
+// Chunk width: 16 units (4 rows x 256 bytes per load) by default; 8 units
+// (8 rows x 128 bytes, twice the waves per block, half the work each) when
+// two-tile blocks are fewer than the compute units and the batch is at most
+// 8.  Measured: 5120x5120 at batch 4 / 8 / 16: 7.45 / 7.76 / 8.90 us with 16,
+// 6.63 / 7.32 / 9.01 with 8; 13824x5120 (432 blocks): 10.8 / 11.5 / 14.4 with
+// 16, 11.6 / 12.9 / 16.5 with 8.
+// want_u (8 or 16) fixes the chunk width; 0 chooses it.
+RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want_u) {
+  RowsShape r;
+  // Four tiles per wave (8-unit chunks, one per wave) for batches above 8
+  // on tall layers: each B fragment then feeds four tiles, halving the
+  // activation reads through L2 against two tiles.  Cold, us at b16:
+  // 13824x5120 15.4 -> 13.2, 11008x4096 12.0 -> 10.9; at b8 and below, and
+  // with fewer than ~160 four-tile blocks, two tiles per wave are as fast or
+  // faster (5120x5120 at b16: 9.1 against 12.0).  The block's LDS (waves x
+  // 4 x 3.7 KB) caps K at 5632.
+  const int tile8 = n_keep == 1 ? RowsGeom<8, 1>::kTileLds : RowsGeom<8>::kTileLds;
+  const bool four = n_keep != 4 && batch > 8 && total_tiles >= 640 && want_u != 16 &&
+                    (size_t)((units + 7) / 8) * 4 * tile8 <= 160 * 1024;
+  r.tpw = four ? 4 : (total_tiles >= 300 ? 2 : 1);
+  r.u = ((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) || r.tpw == 4) ? 8 : 16;
+  if (want_u) r.u = want_u;
+  // 8-unit chunks only with one chunk per wave (K <= 8192): two chunks per
+  // wave of the 16-wave form would not fit its 128 registers
+  if ((units + 7) / 8 > RowsGeom<8>::kMaxWaves) r.u = 16;
+  const int maxw = r.u == 8 ? RowsGeom<8>::kMaxWaves : RowsGeom<16>::kMaxWaves;
+  const int chunks = (units + r.u - 1) / r.u;
+  r.cpw = chunks > 2 * maxw ? 4 : (chunks > maxw ? 2 : 1);
+  // dense rows are twice the bytes: two chunks of two tiles would spill; four
+  // chunks per wave (K > 16384) always take one tile per wave
+  if ((n_keep == 4 && r.cpw == 2) || r.cpw == 4) r.tpw = 1;
+  // four tiles per wave: the 8-unit one-chunk form of 2:4 and 1:4 only (LDS)
+  if (r.tpw == 4 && (r.u != 8 || r.cpw != 1 || n_keep == 4)) r.tpw = 2;
+  r.waves = (chunks + r.cpw - 1) / r.cpw;
+  const int tile_lds = n_keep == 4 ? (r.u == 8 ? RowsGeom<8, 4>::kTileLds : RowsGeom<16, 4>::kTileLds)
+                                    : (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);
+  if (r.tpw == 4 && (size_t)r.waves * 4 * tile_lds > 160 * 1024) r.tpw = 2;  // LDS per workgroup
+  r.lds = (size_t)r.waves * r.tpw * tile_lds;
+  return r;
+}
+
 }  // namespace i4s

@@ -4,7 +4,9 @@
 // through its C ABI: the argument checks of each (every error comes back as
 // the documented status before anything is launched), the adaptive group
 // size decision on the SSE totals the analysis leaves behind, the K-split
-// workspace plan, the no-allocation entry point's scratch limit, the device
+// workspace plan, the rows kernel's launch shapes (every shape the plan can
+// return has a kernel instantiation, fits the block size and the LDS), the
+// no-allocation entry point's scratch limit, the device
 // check (a device that reports another architecture gives
 // I4S_ERR_UNSUPPORTED), and the status texts.  Prints "ok <n> checks" and
 // exits 0 when every check holds.  Test infrastructure only.
@@ -17,6 +19,7 @@
 
 #include "i4s.h"
 #include "i4s_hip_stub.h"
+#include "i4s_internal.h"
 
 namespace {
 
@@ -357,6 +360,37 @@ void test_multi() {
   CHECK(i4s_stub_launches() == before);
 }
 
+// rows_shape over every K the rows kernel takes (up to 512 units), tile
+// counts around each of its thresholds, batch 2..16 and N = 1, 2, 4: the
+// (chunk width, chunks per wave, tiles per wave) triple is one of the
+// instantiated kernels, the waves cover the chunks exactly once, the block
+// fits the kernel's work-group limit and the LDS fits 160 KB.
+void test_rows_shapes() {
+  const int tiles_set[] = {1, 2, 7, 16, 100, 159, 160, 161, 255, 256, 257, 299, 300, 301, 320,
+                           511, 512, 513, 639, 640, 641, 700, 864, 1000, 2000, 5000};
+  long bad = 0;
+  char first[160] = "";
+  for (int nk : {1, 2, 4})
+    for (int units = 1; units <= 512; ++units)
+      for (int t : tiles_set)
+        for (int b = 2; b <= 16; ++b) {
+          const i4s::RowsShape r = i4s::rows_shape(units, t, b, nk);
+          const bool inst =
+              (r.u == 16 && ((r.cpw == 1 && (r.tpw == 1 || r.tpw == 2)) ||
+                             (r.cpw == 2 && (r.tpw == 1 || (r.tpw == 2 && nk != 4))) || (r.cpw == 4 && r.tpw == 1))) ||
+              (r.u == 8 && r.cpw == 1 && (r.tpw == 1 || r.tpw == 2 || (r.tpw == 4 && nk != 4)));
+          const int chunks = inst ? (units + r.u - 1) / r.u : 0;
+          const int maxw = r.tpw == 4 ? 12 : (r.u == 8 ? 16 : 8);
+          const bool ok = inst && r.waves >= 1 && r.waves * r.cpw >= chunks && (r.waves - 1) * r.cpw < chunks &&
+                          r.waves <= maxw && r.lds > 0 && r.lds <= 160 * 1024;
+          if (!ok && bad++ == 0)
+            std::snprintf(first, sizeof first, "units %d tiles %d batch %d N %d -> u %d cpw %d tpw %d waves %d lds %zu",
+                          units, t, b, nk, r.u, r.cpw, r.tpw, r.waves, r.lds);
+        }
+  if (bad) std::fprintf(stderr, "rows_shape: %ld bad shapes, first: %s\n", bad, first);
+  CHECK(bad == 0);
+}
+
 void test_status() {
   const i4s_status all[] = {I4S_OK, I4S_ERR_INVALID_ARGUMENT, I4S_ERR_UNSUPPORTED, I4S_ERR_NONFINITE_WEIGHT,
                             I4S_ERR_WORKSPACE_TOO_SMALL, I4S_ERR_DEVICE};
@@ -379,6 +413,7 @@ int main(int argc, char **argv) {
     test_run();
     test_workspace_and_noalloc();
     test_multi();
+    test_rows_shapes();
     test_status();
   }
   if (g_fails) {
