@@ -15,9 +15,11 @@
 // lanes therefore read adjacent 16-byte pieces of a row (dwordx4 for 2:4),
 // and one unit never straddles a quantization group.  The RPW rows of a wave
 // share the same columns, so each activation fetch from LDS feeds RPW rows.
-// For 2:4 and 1:4 the v_perm_b32 selectors come from a 16-entry table in
-// LDS and v_dot2_f32_f16 multiplies and accumulates in fp32; the group scale
-// is applied once per unit.
+// For 2:4 and 1:4 v_perm_b32 picks the activations: with one row per wave
+// the 2:4 selectors are computed from the code nibbles (a multiply and a
+// mask), otherwise they come from a 16-entry table in LDS.  v_dot2_f32_f16
+// multiplies and accumulates in fp32; the group scale is applied once per
+// unit.
 //
 // Row starts: the kernels read row_ptr, but issue the weight loads of a row
 // at the offset the format prescribes (row * K * N / 4) without waiting for
