@@ -1104,10 +1104,10 @@ __global__ __launch_bounds__(64 * kKWaves) void gemv_smfmac_slice_kernel(
 // One thread per (row group, tile, lane); lanes of vectors past `batch` idle.
 // tpg = tiles per row group (4 or 8: bpg = tpg / 4 blocks of 256 threads per
 // group).  A row group's slices ran on one XCD (the slice kernel's block
-// order), and their partials are still in that XCD's L2 when this launch
-// starts, so block b takes row group 8 * (b / (8 * bpg)) + b % 8 -- the same
-// XCD under the round-robin placement of blocks -- and part (b / 8) % bpg of
-// it; the groups past the last multiple of 8 take the rest in the same way.
+// order), and block b takes row group 8 * (b / (8 * bpg)) + b % 8 -- the
+// same XCD under the round-robin placement of blocks, whose L2 may still hold
+// the group's partials -- and part (b / 8) % bpg of it; the groups past the
+// last multiple of 8 take the rest in the same way.
 // (Measured on MI355X, 5120x13824 at batch 4 / 8 / 16: 14.23 / 14.14 / 15.96
 // -> 13.90 / 13.66 / 14.59 us per call for both launches, against blocks in
 // row-group order.)  The placement only affects speed: the blocks cover the
