@@ -588,8 +588,10 @@ def test_row_ptr_is_honoured(n_keep, batch, rows, cols):
     # K across blocks at batch > 8 on few rows and for any batch beyond 32768
     (96, 20480, 5, 64), (300, 24576, 16, 128), (40, 32768, 9, 256), (64, 40960, 4, 128),
     # K split with two tiles per wave, a partial last tile and a partial last
-    # row group (and at 13824 columns a half-width last slice)
-    (5000, 13824, 8, 256), (8100, 7168, 16, 64)])
+    # row group (and at 13824 columns a half-width last slice); 4500 rows: 36
+    # row groups, so the sum's blocks past the last multiple of 8 groups take
+    # the remaining 4 groups (two blocks each)
+    (5000, 13824, 8, 256), (8100, 7168, 16, 64), (4500, 13824, 16, 128)])
 def test_batch_paths_with_and_without_workspace(rows, cols, batch, g):
     """i4s_run (no workspace) and i4s_run_ws (K split across blocks where the
     layer's plan uses it) both meet the tolerance for every group size; the
