@@ -159,6 +159,49 @@ __device__ inline void lds_unit_x(const uint16_t *xs, int u, uint32_t (&xr)[32])
   }
 }
 
+// Dense INT4 in the one-launch batch-1 kernel: the offsets are removed once
+// per unit instead of once per element.  The nibbles enter v_dot2 as the raw
+// magic-number halves, 1024 + u for the low nibble of each byte and
+// 1024 + 16u for the high one (elements 2, 3, 6, 7 of every 8), and the
+// block stages the activations of those columns divided by 16 (exact for
+// normal values), so each product is (1024 + u) x or (64 + u) x.  The unit's
+// offset term, D = 1032 * sum(x, low columns) + 1152 * sum(x / 16, high
+// columns), is subtracted after the unit's dot products: sum((u - 8) x).  D
+// is summed while x is staged: a 16-byte piece's share with four v_dot2
+// (1032 and 1152 are exact in fp16), the unit's eight pieces -- eight
+// consecutive lanes -- with three DPP additions (quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror).  The sums are of terms ~1000x larger
+// than the result, in fp32: the error stays ~1e-4 of the tolerance's
+// sum |w x|.  32 fewer VALU per unit-row than the exact per-element form.
+__device__ inline void dense_stage_piece(u32x4_t &v, float *dsum, int xi_raw, int nvec) {
+  const h2_t s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  v.y = __builtin_bit_cast(uint32_t, as_h2(v.y) * s16);  // columns 2, 3 of the piece
+  v.w = __builtin_bit_cast(uint32_t, as_h2(v.w) * s16);  // columns 6, 7
+  const h2_t klo = {(_Float16)1032.0f, (_Float16)1032.0f}, khi = {(_Float16)1152.0f, (_Float16)1152.0f};
+  float p = __builtin_amdgcn_fdot2(as_h2(v.x), klo, 0.0f, false);
+  p = __builtin_amdgcn_fdot2(as_h2(v.y), khi, p, false);
+  p = __builtin_amdgcn_fdot2(as_h2(v.z), klo, p, false);
+  p = __builtin_amdgcn_fdot2(as_h2(v.w), khi, p, false);
+  p = dpp_rot_add<0xB1>(p);
+  p = dpp_rot_add<0x4E>(p);
+  p = dpp_rot_add<0x141>(p);
+  if ((xi_raw & 7) == 0 && xi_raw < nvec) dsum[xi_raw >> 3] = p;
+}
+
+__device__ inline float unit_dot_dense_raw(const UnitRegs<4> &u, const uint32_t (&xr)[32], float d) {
+  const uint32_t magic = 0x64006400u;
+  float g = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // vals word j: columns 8j..8j+7
+    const uint32_t w = u.v[j], t = w >> 8;
+    g = __builtin_amdgcn_fdot2(as_h2(and_or(w, 0x000F000Fu, magic)), as_h2(xr[4 * j]), g, false);
+    g = __builtin_amdgcn_fdot2(as_h2(and_or(w, 0x00F000F0u, magic)), as_h2(xr[4 * j + 1]), g, false);
+    g = __builtin_amdgcn_fdot2(as_h2(and_or(t, 0x000F000Fu, magic)), as_h2(xr[4 * j + 2]), g, false);
+    g = __builtin_amdgcn_fdot2(as_h2(and_or(t, 0x00F000F0u, magic)), as_h2(xr[4 * j + 3]), g, false);
+  }
+  return g - d;
+}
+
 template <int NK, int RPW, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemv_b1_kernel(
     int rows, int cols, int group_size, const int32_t *__restrict__ row_ptr,
@@ -373,12 +416,23 @@ __device__ __forceinline__ void b1_direct_body(
 
   // 3. stage x in LDS (threads with a clamped index write the same piece
   // to the same place again)
+  // dense: the per-unit offset terms follow the activations in LDS
+  float *dsum = reinterpret_cast<float *>(xs + units * kStrideB1);
 #pragma unroll
-  for (int j = 0; j < XP; ++j)
-    *reinterpret_cast<u32x4_t *>(xs + __umul24(xi[j] >> 3, kStrideB1) + 8 * (xi[j] & 7)) = xg[j];
+  for (int j = 0; j < XP; ++j) {
+    u32x4_t v = xg[j];
+    if constexpr (NK == 4) dense_stage_piece(v, dsum, (int)threadIdx.x + j * 64 * WAVES, nvec);
+    *reinterpret_cast<u32x4_t *>(xs + __umul24(xi[j] >> 3, kStrideB1) + 8 * (xi[j] & 7)) = v;
+  }
   init_tables<NK>(lut);
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
+
+  // one unit-row's dot product (u: the unit whose activations xr holds)
+  auto dot_unit = [&](const UnitRegs<NK> &t, const uint32_t (&xr)[32], int u) -> float {
+    if constexpr (NK == 4) return unit_dot_dense_raw(t, xr, dsum[u]);
+    else return unit_dot_b1<NK>(t, xr, lut);
+  };
 
   // 4. decode and accumulate.  The activations of the lane's first unit are
   // read from LDS before the first wait for weights, so those reads overlap
@@ -418,7 +472,7 @@ __device__ __forceinline__ void b1_direct_body(
       } else {
         lds_unit_x(xs, min(u, units - 1), xr);
       }
-      const float a = fmaf(fp16_bits_to_float(wr[k][0].s), unit_dot_b1<NK>(wr[k][0], xr, lut), acc[0]);
+      const float a = fmaf(fp16_bits_to_float(wr[k][0].s), dot_unit(wr[k][0], xr, min(u, units - 1)), acc[0]);
       acc[0] = u < units ? a : acc[0];
     } else {
       auto decode = [&]() {
@@ -431,7 +485,7 @@ __device__ __forceinline__ void b1_direct_body(
         }
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-          const float gsum = unit_dot_b1<NK>(wr[k][r], xr, lut);
+          const float gsum = dot_unit(wr[k][r], xr, u);
           acc[r] = fmaf(fp16_bits_to_float(wr[k][r].s), gsum, acc[r]);
         }
       };
@@ -460,7 +514,7 @@ __device__ __forceinline__ void b1_direct_body(
         if (lane + 64 * k < units) {
           uint32_t xr[32];
           lds_unit_x(xs, u, xr);
-          acc[r] = fmaf(fp16_bits_to_float(t.s), unit_dot_b1<NK>(t, xr, lut), acc[r]);
+          acc[r] = fmaf(fp16_bits_to_float(t.s), dot_unit(t, xr, u), acc[r]);
         }
       }
     }
@@ -514,7 +568,7 @@ constexpr int kB1Waves = 8;
 template <int NK, int RPW, int UPL>
 hipError_t launch_b1_direct(const i4s_packed &w, const uint16_t *x, uint16_t *y, hipStream_t stream) {
   const int units = w.cols / kSegCols;
-  const size_t lds = (size_t)units * kStrideB1 * 2;
+  const size_t lds = (size_t)units * kStrideB1 * 2 + (NK == 4 ? (size_t)units * 4 : 0);  // + dense offset terms
   const int rows_per_block = kB1Waves * RPW;
   const dim3 grid((unsigned)((w.rows + rows_per_block - 1) / rows_per_block)), block(64 * kB1Waves);
   const int sg_shift = w.group_size == 64 ? 0 : (w.group_size == 128 ? 1 : 2);
@@ -527,7 +581,7 @@ template <int NK, int RPW, int UPL>
 hipError_t launch_b1_direct_multi(const i4s_packed *w, int32_t n, const uint16_t *x, uint16_t *const *y,
                                   hipStream_t stream) {
   const int units = w[0].cols / kSegCols;
-  const size_t lds = (size_t)units * kStrideB1 * 2;
+  const size_t lds = (size_t)units * kStrideB1 * 2 + (NK == 4 ? (size_t)units * 4 : 0);  // + dense offset terms
   const int rows_per_block = kB1Waves * RPW;
   MultiDesc d = {};
   d.n = n;
