@@ -513,12 +513,19 @@ __device__ inline f4_t smfmac_step_14(uint32_t wd, uint32_t cb, uint32_t sh, con
 // or 4), so where a group ends inside a block of 4 units is known at compile
 // time.
 // `blk` is the block's index within its layer: it covers the TPW 16-row
-// tiles from row 16 * TPW * blk.  lds is the block's dynamic LDS
-// ([waves][TPW][RowsGeom<U>::kTileLds]).  Each B fragment a wave loads feeds the matrix
-// steps of its TPW tiles (measured on the 13824x5120 layer: the B-fragment
-// loads from L2, not the weight stream, bound the one-tile form; two tiles
-// per wave take 14.8 -> 10.6 us at batch 4 and 23.4 -> 14.6 us at batch 16).
-template <int NK, int CPW, int SG, int TPW, int U>
+// tiles from row 16 * TPW * blk.  lds is the block's dynamic LDS (per wave:
+// [TPW][RowsGeom<U>::kTileLds], then kRowsBcBytes when BV = 4).  Each B
+// fragment a wave loads feeds the matrix steps of its TPW tiles (measured on
+// the 13824x5120 layer: the B-fragment loads from L2, not the weight stream,
+// bound the one-tile form; two tiles per wave take 14.8 -> 10.6 us at batch
+// 4 and 23.4 -> 14.6 us at batch 16).
+// BV = 4 (at most four vectors): a wave reads each 4-unit block's
+// activations once, two 16-byte loads per lane, and spreads them to the
+// matrix layout through kRowsBcBytes of its LDS area; BV = 16: every lane
+// loads its own B fragment (at batch 4 three quarters of those bytes repeat
+// the last vector, and all of them share the CU's vector memory path with
+// the weight stream).
+template <int NK, int CPW, int SG, int TPW, int U, int BV>
 __device__ __forceinline__ void rows_body(
     int blk, int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
     const uint8_t *__restrict__ vals, const uint16_t *__restrict__ codes,
@@ -536,7 +543,10 @@ __device__ __forceinline__ void rows_body(
   typedef typename std::conditional<NK == 4, DenseVals,
                                     typename std::conditional<NK == 2, u32x4_t, u32x2_t>::type>::type vals_t;
   typedef typename std::conditional<NK == 2, u32x2_t, uint32_t>::type codes_t;
-  uint8_t *wl = lds + wave * TPW * Geo::kTileLds;  // the wave's areas, one per tile
+  static_assert(BV == 4 || BV == 16, "B fragments: compact (batch <= 4) or per lane");
+  constexpr int kWaveLds = TPW * Geo::kTileLds + (BV == 4 ? kRowsBcBytes : 0);
+  uint8_t *wl = lds + wave * kWaveLds;  // the wave's areas: one per tile, then the activations' (BV = 4)
+  uint8_t *wbc = wl + TPW * Geo::kTileLds;
   auto lv_of = [&](int t) { return reinterpret_cast<vals_t *>(wl + t * Geo::kTileLds); };  // [16 rows][ST]
   auto lc_of = [&](int t) { return reinterpret_cast<codes_t *>(wl + t * Geo::kTileLds + Geo::kValsBytes); };
   auto lsc_of = [&](int t) {                                                     // [U units][Geo::kScaleStride]
@@ -564,9 +574,43 @@ __device__ __forceinline__ void rows_body(
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int k = 0; k < NL; ++k) wrow[t][k] = min(row0 + 16 * t + RL * k + lr, rows - 1);
-  u32x4_t bq[2][8];
-  load_b(bq[0], 0);
-  load_b(bq[1], 1);
+  // BV = 4: lane L loads piece (L % 8) ^ f(P) of the 128-byte activation row
+  // of pair P = 8i + L / 8 (vector P % 4, unit P / 4 of the block), i = 0, 1,
+  // so every 8 lanes read one whole 128-byte row.  The wave writes the two
+  // loads to its area in lane order (pair P, position p: piece p ^ f(P)), and
+  // lane (vector li, quarter lq) reads pieces lq and 4 + lq of pair
+  // 4s + min(li, 3) for unit s.  f(P) = 4 for vectors 2 and 3 moves their
+  // pieces to the other half of the 128 bytes, so the 16 distinct 16-byte
+  // reads of one LDS instruction (four vectors x four quarters) fall in
+  // distinct banks.
+  auto load_bc = [&](u32x4_t (&bc)[2], int n) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int P = 8 * i + lane / 8, v = P % 4, s = P / 4;
+      const int q = (lane % 8) ^ (4 * ((P >> 1) & 1));
+      const int u = min(unit_of(n, s), units - 1);
+      bc[i] = *reinterpret_cast<const u32x4_t *>(x + (int64_t)min(v, batch - 1) * cols + u * kSegCols + 8 * q);
+    }
+  };
+  auto read_bc = [&](u32x4_t (&bx)[8]) {
+    const int v = min(li, 3);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int P = 4 * s + v, f = 4 * ((P >> 1) & 1);
+      const u32x4_t *a = reinterpret_cast<const u32x4_t *>(wbc) + P * 8;
+      bx[2 * s] = a[lq ^ f];
+      bx[2 * s + 1] = a[(4 + lq) ^ f];
+    }
+  };
+  u32x4_t bq[2][8];   // BV = 16: the B fragments of blocks n and n + 1
+  u32x4_t bqc[2][2];  // BV = 4: the compact loads of blocks n and n + 1
+  if constexpr (BV == 4) {
+    load_bc(bqc[0], 0);
+    load_bc(bqc[1], 1);
+  } else {
+    load_b(bq[0], 0);
+    load_b(bq[1], 1);
+  }
   vals_t wv[TPW][NL];  // one chunk; the next chunk reuses them once it is staged
   codes_t wc[TPW][NL];
   uint16_t wsc[TPW][NL];
@@ -652,7 +696,17 @@ __device__ __forceinline__ void rows_body(
 #pragma unroll
       for (int bb = 0; bb < NBK; ++bb) {
         const int n = NBK * c + bb;
-        u32x4_t (&bx)[8] = bq[n % 2];
+        // BV = 4: block n's activations into the wave's area (once the
+        // previous block's reads are done) and back in the matrix layout
+        u32x4_t bxl[8];
+        if constexpr (BV == 4) {
+          if (n > 0) wave_lds_sync();
+          reinterpret_cast<u32x4_t *>(wbc)[lane] = bqc[n % 2][0];
+          reinterpret_cast<u32x4_t *>(wbc)[64 + lane] = bqc[n % 2][1];
+          wave_lds_sync();
+          read_bc(bxl);
+        }
+        u32x4_t (&bx)[8] = BV == 4 ? bxl : bq[n % 2];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
           const vals_t *lv = lv_of(t);
@@ -728,7 +782,10 @@ __device__ __forceinline__ void rows_body(
         // the buffer just used takes block n + 2; the scheduling barriers keep
         // the loads here, so only two buffers are ever live
         __builtin_amdgcn_sched_barrier(0);
-        if (n + 2 < NBK * CPW) load_b(bx, n + 2);
+        if (n + 2 < NBK * CPW) {
+          if constexpr (BV == 4) load_bc(bqc[n % 2], n + 2);
+          else load_b(bx, n + 2);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -786,7 +843,7 @@ __device__ __forceinline__ void rows_body(
     for (int t = 0; t < TPW; ++t) {
       f4_t sum = acc[t];
       for (int w = 1; w < nwaves; ++w)
-        sum += reinterpret_cast<const f4_t *>(lds + w * TPW * Geo::kTileLds)[64 * t + lane];
+        sum += reinterpret_cast<const f4_t *>(lds + w * kWaveLds)[64 * t + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + 16 * t + 4 * lq + r;
@@ -804,7 +861,7 @@ constexpr int rows_min_waves() {
   return (NK == 2 && CPW == 1 && TPW == 2 && U == 16) ? 4 : 1;
 }
 
-template <int NK, int CPW, int SG, int TPW, int U>
+template <int NK, int CPW, int SG, int TPW, int U, int BV>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 64 * (TPW == 4 ? 12 : RowsGeom<U>::kMaxWaves)),
                           amdgpu_waves_per_eu(rows_min_waves<NK, CPW, TPW, U>())))
 void gemv_smfmac_rows_kernel(
@@ -813,13 +870,14 @@ void gemv_smfmac_rows_kernel(
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, int batch,
     uint16_t *__restrict__ y) {
   extern __shared__ __align__(16) uint8_t lds[];  // [waves][TPW][RowsGeom<U>::kTileLds]
-  rows_body<NK, CPW, SG, TPW, U>(blockIdx.x, rows, units, sg_shift, row_ptr, vals, codes, scales, x, batch, y, lds);
+  rows_body<NK, CPW, SG, TPW, U, BV>(blockIdx.x, rows, units, sg_shift, row_ptr, vals, codes, scales, x, batch, y,
+                                     lds);
 }
 
 // Several layers that share x (and N, G and K) in one launch: each block
 // finds its layer from the cumulative block counts and runs the single-layer
 // body on it.
-template <int NK, int CPW, int SG, int TPW, int U>
+template <int NK, int CPW, int SG, int TPW, int U, int BV>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 64 * (TPW == 4 ? 12 : RowsGeom<U>::kMaxWaves)),
                           amdgpu_waves_per_eu(rows_min_waves<NK, CPW, TPW, U>())))
 void gemv_smfmac_rows_multi_kernel(
@@ -829,7 +887,7 @@ void gemv_smfmac_rows_multi_kernel(
 #pragma unroll
   for (int i = 1; i < kMaxMulti; ++i) m += (i < d.n && (int)blockIdx.x >= d.block_end[i - 1]) ? 1 : 0;
   const int first = m == 0 ? 0 : d.block_end[m - 1];
-  rows_body<NK, CPW, SG, TPW, U>((int)blockIdx.x - first, d.rows[m], units, d.sg_shift[m], d.row_ptr[m],
+  rows_body<NK, CPW, SG, TPW, U, BV>((int)blockIdx.x - first, d.rows[m], units, d.sg_shift[m], d.row_ptr[m],
                                  d.vals[m], d.codes[m], d.scales[m], x, batch, d.y[m], lds);
 }
 
@@ -1192,59 +1250,65 @@ hipError_t allow_lds(const void *kernel, size_t bytes) {
   if (e == hipSuccess && g) g->store(bytes, std::memory_order_relaxed);
   return e;
 }
-template <int NK, int C, int G, int T, int U> struct RowsTag {};
-template <int NK, int C, int G, int T, int U> struct RowsMultiTag {};
+template <int NK, int C, int G, int T, int U, int BV> struct RowsTag {};
+template <int NK, int C, int G, int T, int U, int BV> struct RowsMultiTag {};
 
-template <int NK, int C, int G, int T, int U>
+template <int NK, int C, int G, int T, int U, int BV>
 hipError_t launch_rows_t(const i4s_packed &w, const uint16_t *x, int32_t batch, uint16_t *y, const RowsShape &r,
                          int sg_shift, hipStream_t stream) {
-  const void *k = reinterpret_cast<const void *>(&gemv_smfmac_rows_kernel<NK, C, G, T, U>);
-  hipError_t e = allow_lds<RowsTag<NK, C, G, T, U>>(k, r.lds);
+  const void *k = reinterpret_cast<const void *>(&gemv_smfmac_rows_kernel<NK, C, G, T, U, BV>);
+  hipError_t e = allow_lds<RowsTag<NK, C, G, T, U, BV>>(k, r.lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((w.rows + 16 * T - 1) / (16 * T))), block(64 * r.waves);
-  hipLaunchKernelGGL((gemv_smfmac_rows_kernel<NK, C, G, T, U>), grid, block, r.lds, stream, w.rows,
+  hipLaunchKernelGGL((gemv_smfmac_rows_kernel<NK, C, G, T, U, BV>), grid, block, r.lds, stream, w.rows,
                      w.cols / kSegCols, sg_shift, w.row_ptr, w.vals, w.codes, w.scales, x, batch, y);
   return hipGetLastError();
 }
 
-template <int NK, int C, int G, int T, int U>
+template <int NK, int C, int G, int T, int U, int BV>
 hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, const MultiDesc &d, int blocks,
                                const RowsShape &r, hipStream_t stream) {
-  const void *k = reinterpret_cast<const void *>(&gemv_smfmac_rows_multi_kernel<NK, C, G, T, U>);
-  hipError_t e = allow_lds<RowsMultiTag<NK, C, G, T, U>>(k, r.lds);
+  const void *k = reinterpret_cast<const void *>(&gemv_smfmac_rows_multi_kernel<NK, C, G, T, U, BV>);
+  hipError_t e = allow_lds<RowsMultiTag<NK, C, G, T, U, BV>>(k, r.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemv_smfmac_rows_multi_kernel<NK, C, G, T, U>), dim3((unsigned)blocks), dim3(64 * r.waves),
-                     r.lds, stream, units, x, batch, d);
+  hipLaunchKernelGGL((gemv_smfmac_rows_multi_kernel<NK, C, G, T, U, BV>), dim3((unsigned)blocks),
+                     dim3(64 * r.waves), r.lds, stream, units, x, batch, d);
   return hipGetLastError();
 }
 
-// Call FN<NK, cpw, SG, tpw, U>(args...) for the shape's run-time values.
+// Call FN<NK, cpw, SG, tpw, U, bv>(args...) for the shape's run-time values.
 // Every combination rows_shape can return is listed; anything else (and a
 // group size other than 64, 128 or 256) is refused rather than run on an
 // instantiation built for another shape.
-#define I4S_ROWS_SG(FN, C, T, U, ...)                                                    \
+#define I4S_ROWS_SG(FN, C, T, U, BV, ...)                                                \
   do {                                                                                   \
-    if (sg_shift == 0) return FN<NK, C, 1, T, U>(__VA_ARGS__);                           \
-    if (sg_shift == 1) return FN<NK, C, 2, T, U>(__VA_ARGS__);                           \
-    if (sg_shift == 2) return FN<NK, C, 4, T, U>(__VA_ARGS__);                           \
+    if (sg_shift == 0) return FN<NK, C, 1, T, U, BV>(__VA_ARGS__);                       \
+    if (sg_shift == 1) return FN<NK, C, 2, T, U, BV>(__VA_ARGS__);                       \
+    if (sg_shift == 2) return FN<NK, C, 4, T, U, BV>(__VA_ARGS__);                       \
+    return hipErrorNotSupported;                                                         \
+  } while (0)
+#define I4S_ROWS_BV(FN, C, T, U, ...)                                                    \
+  do {                                                                                   \
+    if (r.bv == 4) I4S_ROWS_SG(FN, C, T, U, 4, __VA_ARGS__);                             \
+    if (r.bv == 16) I4S_ROWS_SG(FN, C, T, U, 16, __VA_ARGS__);                           \
     return hipErrorNotSupported;                                                         \
   } while (0)
 #define I4S_ROWS_DISPATCH(FN, ...)                                                       \
   do {                                                                                   \
     if (r.u == 16) {                                                                     \
-      if (r.cpw == 4 && r.tpw == 1) I4S_ROWS_SG(FN, 4, 1, 16, __VA_ARGS__);             \
-      if (r.cpw == 1 && r.tpw == 1) I4S_ROWS_SG(FN, 1, 1, 16, __VA_ARGS__);             \
-      if (r.cpw == 1 && r.tpw == 2) I4S_ROWS_SG(FN, 1, 2, 16, __VA_ARGS__);             \
-      if (r.cpw == 2 && r.tpw == 1) I4S_ROWS_SG(FN, 2, 1, 16, __VA_ARGS__);             \
+      if (r.cpw == 4 && r.tpw == 1) I4S_ROWS_BV(FN, 4, 1, 16, __VA_ARGS__);             \
+      if (r.cpw == 1 && r.tpw == 1) I4S_ROWS_BV(FN, 1, 1, 16, __VA_ARGS__);             \
+      if (r.cpw == 1 && r.tpw == 2) I4S_ROWS_BV(FN, 1, 2, 16, __VA_ARGS__);             \
+      if (r.cpw == 2 && r.tpw == 1) I4S_ROWS_BV(FN, 2, 1, 16, __VA_ARGS__);             \
       if constexpr (NK != 4) {                                                           \
-        if (r.cpw == 2 && r.tpw == 2) I4S_ROWS_SG(FN, 2, 2, 16, __VA_ARGS__);           \
+        if (r.cpw == 2 && r.tpw == 2) I4S_ROWS_BV(FN, 2, 2, 16, __VA_ARGS__);           \
       }                                                                                  \
     }                                                                                    \
     if (r.u == 8 && r.cpw == 1) {                                                        \
-      if (r.tpw == 1) I4S_ROWS_SG(FN, 1, 1, 8, __VA_ARGS__);                            \
-      if (r.tpw == 2) I4S_ROWS_SG(FN, 1, 2, 8, __VA_ARGS__);                            \
+      if (r.tpw == 1) I4S_ROWS_BV(FN, 1, 1, 8, __VA_ARGS__);                            \
+      if (r.tpw == 2) I4S_ROWS_BV(FN, 1, 2, 8, __VA_ARGS__);                            \
       if constexpr (NK != 4) {                                                           \
-        if (r.tpw == 4) I4S_ROWS_SG(FN, 1, 4, 8, __VA_ARGS__);                          \
+        if (r.tpw == 4 && r.bv == 16) I4S_ROWS_SG(FN, 1, 4, 8, 16, __VA_ARGS__);       \
       }                                                                                  \
     }                                                                                    \
     return hipErrorNotSupported;                                                         \

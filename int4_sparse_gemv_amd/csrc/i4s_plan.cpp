@@ -90,6 +90,19 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
                                     : (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);
   if (r.tpw == 4 && (size_t)r.waves * 4 * tile_lds > 160 * 1024) r.tpw = 2;  // LDS per workgroup
   r.lds = (size_t)r.waves * r.tpw * tile_lds;
+  // At most four vectors: each wave reads a 4-unit block's activations once
+  // (two 16-byte loads per lane instead of eight, three quarters of which
+  // repeat the last vector) and spreads them through its LDS area; measured
+  // on 13824x5120 at b4, 11.4 -> 10.5 us cold.  Not where the extra LDS would
+  // exceed the workgroup limit or leave fewer blocks per CU.
+  if (batch <= 4 && r.tpw <= 2) {
+    const size_t lds4 = r.lds + (size_t)r.waves * kRowsBcBytes;
+    const size_t cu = 160 * 1024;
+    if (lds4 <= cu && cu / lds4 == cu / r.lds) {
+      r.bv = 4;
+      r.lds = lds4;
+    }
+  }
   return r;
 }
 

@@ -364,7 +364,9 @@ void test_multi() {
 // counts around each of its thresholds, batch 2..16 and N = 1, 2, 4: the
 // (chunk width, chunks per wave, tiles per wave) triple is one of the
 // instantiated kernels, the waves cover the chunks exactly once, the block
-// fits the kernel's work-group limit and the LDS fits 160 KB.
+// fits the kernel's work-group limit, the LDS is what the kernel addresses
+// and fits 160 KB, and the compact B fragments (bv 4) are chosen only at
+// batch <= 4 and only where they leave as many blocks per CU.
 void test_rows_shapes() {
   const int tiles_set[] = {1, 2, 7, 16, 100, 159, 160, 161, 255, 256, 257, 299, 300, 301, 320,
                            511, 512, 513, 639, 640, 641, 700, 864, 1000, 2000, 5000};
@@ -381,11 +383,22 @@ void test_rows_shapes() {
               (r.u == 8 && r.cpw == 1 && (r.tpw == 1 || r.tpw == 2 || (r.tpw == 4 && nk != 4)));
           const int chunks = inst ? (units + r.u - 1) / r.u : 0;
           const int maxw = r.tpw == 4 ? 12 : (r.u == 8 ? 16 : 8);
-          const bool ok = inst && r.waves >= 1 && r.waves * r.cpw >= chunks && (r.waves - 1) * r.cpw < chunks &&
-                          r.waves <= maxw && r.lds > 0 && r.lds <= 160 * 1024;
+          // the LDS is the waves' tile areas plus, with compact B fragments
+          // (at most four vectors, one or two tiles), the activations' area
+          const size_t tile = nk == 4 ? (r.u == 8 ? i4s::RowsGeom<8, 4>::kTileLds : i4s::RowsGeom<16, 4>::kTileLds)
+                              : nk == 1 ? (r.u == 8 ? i4s::RowsGeom<8, 1>::kTileLds : i4s::RowsGeom<16, 1>::kTileLds)
+                                        : (r.u == 8 ? i4s::RowsGeom<8>::kTileLds : i4s::RowsGeom<16>::kTileLds);
+          const size_t base = (size_t)r.waves * r.tpw * tile;
+          const bool bv_ok = (r.bv == 16 && r.lds == base) ||
+                             (r.bv == 4 && b <= 4 && r.tpw <= 2 &&
+                              r.lds == base + (size_t)r.waves * i4s::kRowsBcBytes &&
+                              (160 * 1024) / r.lds == (160 * 1024) / base);
+          const bool ok = inst && bv_ok && r.waves >= 1 && r.waves * r.cpw >= chunks &&
+                          (r.waves - 1) * r.cpw < chunks && r.waves <= maxw && r.lds > 0 && r.lds <= 160 * 1024;
           if (!ok && bad++ == 0)
-            std::snprintf(first, sizeof first, "units %d tiles %d batch %d N %d -> u %d cpw %d tpw %d waves %d lds %zu",
-                          units, t, b, nk, r.u, r.cpw, r.tpw, r.waves, r.lds);
+            std::snprintf(first, sizeof first,
+                          "units %d tiles %d batch %d N %d -> u %d cpw %d tpw %d waves %d bv %d lds %zu", units, t, b,
+                          nk, r.u, r.cpw, r.tpw, r.waves, r.bv, r.lds);
         }
   if (bad) std::fprintf(stderr, "rows_shape: %ld bad shapes, first: %s\n", bad, first);
   CHECK(bad == 0);
