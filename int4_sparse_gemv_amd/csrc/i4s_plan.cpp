@@ -93,12 +93,15 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
   // At most four vectors: each wave reads a 4-unit block's activations once
   // (two 16-byte loads per lane instead of eight, three quarters of which
   // repeat the last vector) and spreads them through its LDS area; measured
-  // on 13824x5120 at b4, 11.4 -> 10.5 us cold.  Not where the extra LDS would
-  // exceed the workgroup limit or leave fewer blocks per CU.
+  // cold, 13824x5120 at b4 11.4 -> 10.5 us, 5120x5120 at b2 / b3 / b4 6.60 /
+  // 6.70 / 6.86 -> 6.29 / 6.38 / 6.43.  Not where the extra LDS would exceed
+  // the workgroup limit, nor where it would leave fewer blocks per CU on a
+  // layer with more blocks than the 256 CUs.
   if (batch <= 4 && r.tpw <= 2) {
     const size_t lds4 = r.lds + (size_t)r.waves * kRowsBcBytes;
     const size_t cu = 160 * 1024;
-    if (lds4 <= cu && cu / lds4 == cu / r.lds) {
+    const int blocks = (total_tiles + r.tpw - 1) / r.tpw;
+    if (lds4 <= cu && (cu / lds4 == cu / r.lds || blocks <= 256)) {
       r.bv = 4;
       r.lds = lds4;
     }
