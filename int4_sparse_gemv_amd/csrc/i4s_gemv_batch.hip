@@ -514,17 +514,17 @@ __device__ inline f4_t smfmac_step_14(uint32_t wd, uint32_t cb, uint32_t sh, con
 // time.
 // `blk` is the block's index within its layer: it covers the TPW 16-row
 // tiles from row 16 * TPW * blk.  lds is the block's dynamic LDS (per wave:
-// [TPW][RowsGeom<U>::kTileLds], then kRowsBcBytes when BV = 4).  Each B
+// [TPW][RowsGeom<U>::kTileLds], then kRowsBcBytes when BV < 16).  Each B
 // fragment a wave loads feeds the matrix steps of its TPW tiles (measured on
 // the 13824x5120 layer: the B-fragment loads from L2, not the weight stream,
 // bound the one-tile form; two tiles per wave take 14.8 -> 10.6 us at batch
 // 4 and 23.4 -> 14.6 us at batch 16).
-// BV = 4 (at most four vectors): a wave reads each 4-unit block's
-// activations once, two 16-byte loads per lane, and spreads them to the
-// matrix layout through kRowsBcBytes of its LDS area; BV = 16: every lane
-// loads its own B fragment (at batch 4 three quarters of those bytes repeat
-// the last vector, and all of them share the CU's vector memory path with
-// the weight stream).
+// BV = 4 or 8 (at most that many vectors): a wave reads each 4-unit block's
+// activations once, BV / 2 16-byte loads per lane, and spreads them to the
+// matrix layout through kRowsBcBytes of its LDS area (in BV / 4 passes);
+// BV = 16: every lane loads its own B fragment (at batch 4 three quarters of
+// those bytes repeat the last vector, and all of them share the CU's vector
+// memory path with the weight stream).
 template <int NK, int CPW, int SG, int TPW, int U, int BV>
 __device__ __forceinline__ void rows_body(
     int blk, int rows, int units, int sg_shift, const int32_t *__restrict__ row_ptr,
@@ -543,8 +543,11 @@ __device__ __forceinline__ void rows_body(
   typedef typename std::conditional<NK == 4, DenseVals,
                                     typename std::conditional<NK == 2, u32x4_t, u32x2_t>::type>::type vals_t;
   typedef typename std::conditional<NK == 2, u32x2_t, uint32_t>::type codes_t;
-  static_assert(BV == 4 || BV == 16, "B fragments: compact (batch <= 4) or per lane");
-  constexpr int kWaveLds = TPW * Geo::kTileLds + (BV == 4 ? kRowsBcBytes : 0);
+  static_assert(BV == 4 || BV == 8 || BV == 16, "B fragments: compact (batch <= 4 or 8) or per lane");
+  constexpr bool kCompact = BV < 16;
+  constexpr int NI = kCompact ? BV / 2 : 1;  // compact loads per lane and 4-unit block
+  constexpr int NP = kCompact ? BV / 4 : 1;  // passes through the LDS area per block
+  constexpr int kWaveLds = TPW * Geo::kTileLds + (kCompact ? kRowsBcBytes : 0);
   uint8_t *wl = lds + wave * kWaveLds;  // the wave's areas: one per tile, then the activations' (BV = 4)
   uint8_t *wbc = wl + TPW * Geo::kTileLds;
   auto lv_of = [&](int t) { return reinterpret_cast<vals_t *>(wl + t * Geo::kTileLds); };  // [16 rows][ST]
@@ -574,37 +577,39 @@ __device__ __forceinline__ void rows_body(
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int k = 0; k < NL; ++k) wrow[t][k] = min(row0 + 16 * t + RL * k + lr, rows - 1);
-  // BV = 4: lane L loads piece (L % 8) ^ f(P) of the 128-byte activation row
-  // of pair P = 8i + L / 8 (vector P % 4, unit P / 4 of the block), i = 0, 1,
-  // so every 8 lanes read one whole 128-byte row.  The wave writes the two
-  // loads to its area in lane order (pair P, position p: piece p ^ f(P)), and
-  // lane (vector li, quarter lq) reads pieces lq and 4 + lq of pair
-  // 4s + min(li, 3) for unit s.  f(P) = 4 for vectors 2 and 3 moves their
-  // pieces to the other half of the 128 bytes, so the 16 distinct 16-byte
-  // reads of one LDS instruction (four vectors x four quarters) fall in
-  // distinct banks.
-  auto load_bc = [&](u32x4_t (&bc)[2], int n) {
+  // BV = 4 or 8: load i of lane L takes piece (L % 8) ^ g(v) of the 128-byte
+  // activation row of pair P = 8i + L / 8 (vector v = P % BV, unit P / BV of
+  // the block), so every 8 lanes read one whole row.  A pass through the
+  // wave's 2 KB area writes two loads in lane order (16 pairs: four units of
+  // four vectors, or two units of eight) and reads them back: lane (vector
+  // li, quarter lq) takes pieces lq and 4 + lq of vector min(li, BV - 1) for
+  // each unit of the pass.  g(v) = 4 for vectors 2, 3 (6, 7) moves their
+  // pieces to the other half of the 128 bytes, so the distinct 16-byte reads
+  // of one LDS instruction fall in distinct banks (BV = 4) or at most two to
+  // a bank (BV = 8).
+  auto swz = [](int v) { return 4 * ((v >> 1) & 1); };
+  auto load_bc = [&](u32x4_t (&bc)[NI], int n) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int P = 8 * i + lane / 8, v = P % 4, s = P / 4;
-      const int q = (lane % 8) ^ (4 * ((P >> 1) & 1));
+    for (int i = 0; i < NI; ++i) {
+      const int P = 8 * i + lane / 8, v = P % BV, s = P / BV;
+      const int q = (lane % 8) ^ swz(v);
       const int u = min(unit_of(n, s), units - 1);
       bc[i] = *reinterpret_cast<const u32x4_t *>(x + (int64_t)min(v, batch - 1) * cols + u * kSegCols + 8 * q);
     }
   };
-  auto read_bc = [&](u32x4_t (&bx)[8]) {
-    const int v = min(li, 3);
+  // the B fragments of the pass's units (4 / NP of them, from unit s0) out of the area
+  auto read_bc = [&](u32x4_t (&bx)[8], int s0) {
+    const int v = min(li, BV - 1), f = swz(v);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int P = 4 * s + v, f = 4 * ((P >> 1) & 1);
-      const u32x4_t *a = reinterpret_cast<const u32x4_t *>(wbc) + P * 8;
-      bx[2 * s] = a[lq ^ f];
-      bx[2 * s + 1] = a[(4 + lq) ^ f];
+    for (int s = 0; s < 4 / NP; ++s) {
+      const u32x4_t *a = reinterpret_cast<const u32x4_t *>(wbc) + (s * BV + v) * 8;
+      bx[2 * (s0 + s)] = a[lq ^ f];
+      bx[2 * (s0 + s) + 1] = a[(4 + lq) ^ f];
     }
   };
   u32x4_t bq[2][8];   // BV = 16: the B fragments of blocks n and n + 1
-  u32x4_t bqc[2][2];  // BV = 4: the compact loads of blocks n and n + 1
-  if constexpr (BV == 4) {
+  u32x4_t bqc[2][NI];  // BV < 16: the compact loads of blocks n and n + 1
+  if constexpr (kCompact) {
     load_bc(bqc[0], 0);
     load_bc(bqc[1], 1);
   } else {
@@ -696,17 +701,20 @@ __device__ __forceinline__ void rows_body(
 #pragma unroll
       for (int bb = 0; bb < NBK; ++bb) {
         const int n = NBK * c + bb;
-        // BV = 4: block n's activations into the wave's area (once the
-        // previous block's reads are done) and back in the matrix layout
+        // BV < 16: block n's activations through the wave's area, NP passes
+        // of two loads (each written once the previous pass's reads are done)
         u32x4_t bxl[8];
-        if constexpr (BV == 4) {
-          if (n > 0) wave_lds_sync();
-          reinterpret_cast<u32x4_t *>(wbc)[lane] = bqc[n % 2][0];
-          reinterpret_cast<u32x4_t *>(wbc)[64 + lane] = bqc[n % 2][1];
-          wave_lds_sync();
-          read_bc(bxl);
+        if constexpr (kCompact) {
+#pragma unroll
+          for (int j = 0; j < NP; ++j) {
+            if (n > 0 || j > 0) wave_lds_sync();
+            reinterpret_cast<u32x4_t *>(wbc)[lane] = bqc[n % 2][2 * j];
+            reinterpret_cast<u32x4_t *>(wbc)[64 + lane] = bqc[n % 2][2 * j + 1];
+            wave_lds_sync();
+            read_bc(bxl, j * (4 / NP));
+          }
         }
-        u32x4_t (&bx)[8] = BV == 4 ? bxl : bq[n % 2];
+        u32x4_t (&bx)[8] = kCompact ? bxl : bq[n % 2];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
           const vals_t *lv = lv_of(t);
@@ -783,7 +791,7 @@ __device__ __forceinline__ void rows_body(
         // the loads here, so only two buffers are ever live
         __builtin_amdgcn_sched_barrier(0);
         if (n + 2 < NBK * CPW) {
-          if constexpr (BV == 4) load_bc(bqc[n % 2], n + 2);
+          if constexpr (kCompact) load_bc(bqc[n % 2], n + 2);
           else load_b(bx, n + 2);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1287,9 +1295,16 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
     if (sg_shift == 2) return FN<NK, C, 4, T, U, BV>(__VA_ARGS__);                       \
     return hipErrorNotSupported;                                                         \
   } while (0)
+// bv 4 and 8 (2:4 and dense only; 8 not with two tiles of 16-unit chunks,
+// which would spill) or 16
 #define I4S_ROWS_BV(FN, C, T, U, ...)                                                    \
   do {                                                                                   \
-    if (r.bv == 4) I4S_ROWS_SG(FN, C, T, U, 4, __VA_ARGS__);                             \
+    if constexpr (NK != 1) {                                                             \
+      if (r.bv == 4) I4S_ROWS_SG(FN, C, T, U, 4, __VA_ARGS__);                           \
+      if constexpr (!(T == 2 && U == 16)) {                                              \
+        if (r.bv == 8) I4S_ROWS_SG(FN, C, T, U, 8, __VA_ARGS__);                         \
+      }                                                                                  \
+    }                                                                                    \
     if (r.bv == 16) I4S_ROWS_SG(FN, C, T, U, 16, __VA_ARGS__);                           \
     return hipErrorNotSupported;                                                         \
   } while (0)

@@ -90,19 +90,27 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
                                     : (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);
   if (r.tpw == 4 && (size_t)r.waves * 4 * tile_lds > 160 * 1024) r.tpw = 2;  // LDS per workgroup
   r.lds = (size_t)r.waves * r.tpw * tile_lds;
-  // At most four vectors: each wave reads a 4-unit block's activations once
-  // (two 16-byte loads per lane instead of eight, three quarters of which
-  // repeat the last vector) and spreads them through its LDS area; measured
-  // cold, 13824x5120 at b4 11.4 -> 10.5 us, 5120x5120 at b2 / b3 / b4 6.60 /
-  // 6.70 / 6.86 -> 6.29 / 6.38 / 6.43.  Not where the extra LDS would exceed
-  // the workgroup limit, nor where it would leave fewer blocks per CU on a
-  // layer with more blocks than the 256 CUs.
-  if (batch <= 4 && r.tpw <= 2) {
+  // At most four vectors (2:4 and dense): each wave reads a 4-unit block's
+  // activations once (two 16-byte loads per lane instead of eight, three
+  // quarters of which repeat the last vector) and spreads them through its
+  // LDS area; measured cold, 13824x5120 at b4 11.4 -> 10.5 us, 5120x5120 at
+  // b2 / b3 / b4 6.60 / 6.70 / 6.86 -> 6.29 / 6.38 / 6.43.  Not where the
+  // extra LDS would exceed the workgroup limit, nor where it would leave
+  // fewer blocks per CU on a layer with more blocks than the 256 CUs.
+  // Five to eight vectors: four loads per lane and block, two passes through
+  // the same area; only where the blocks fit the CUs once (on 13824x5120 at
+  // b8 the two-tile 16-unit form spills at its 128-register cap: 12.4 ->
+  // 12.7 us): 5120x5120 at b8 7.59 -> 6.96 us, 4096x4096 at b4 / b8 4.87 /
+  // 5.49 -> 4.58 / 4.95, 4096x11008 (G64) at b4 10.69 -> 9.53.  Not for 1:4,
+  // whose half-size weights left the activations' share of the traffic
+  // larger and still came out 1-2 % slower (4096x4096 1:4 at b4 / b8 4.75 /
+  // 5.15 -> 4.80 / 5.27).
+  const int blocks = (total_tiles + r.tpw - 1) / r.tpw;
+  if (n_keep != 1 && batch <= 8 && r.tpw <= 2 && !(batch > 4 && r.tpw == 2 && r.u == 16)) {
     const size_t lds4 = r.lds + (size_t)r.waves * kRowsBcBytes;
     const size_t cu = 160 * 1024;
-    const int blocks = (total_tiles + r.tpw - 1) / r.tpw;
-    if (lds4 <= cu && (cu / lds4 == cu / r.lds || blocks <= 256)) {
-      r.bv = 4;
+    if (lds4 <= cu && (batch <= 4 ? (cu / lds4 == cu / r.lds || blocks <= 256) : blocks <= 256)) {
+      r.bv = batch <= 4 ? 4 : 8;
       r.lds = lds4;
     }
   }
