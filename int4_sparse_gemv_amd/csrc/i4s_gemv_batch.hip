@@ -1295,11 +1295,11 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
     if (sg_shift == 2) return FN<NK, C, 4, T, U, BV>(__VA_ARGS__);                       \
     return hipErrorNotSupported;                                                         \
   } while (0)
-// bv 4 and 8 (2:4 and dense only; 8 not with two tiles of 16-unit chunks,
-// which would spill) or 16
+// bv 4 and 8 (1:4 only in one-tile blocks of one 8-unit chunk; 8 not with
+// two tiles of 16-unit chunks, which would spill) or 16
 #define I4S_ROWS_BV(FN, C, T, U, ...)                                                    \
   do {                                                                                   \
-    if constexpr (NK != 1) {                                                             \
+    if constexpr (NK != 1 || (C == 1 && T == 1 && U == 8)) {                             \
       if (r.bv == 4) I4S_ROWS_SG(FN, C, T, U, 4, __VA_ARGS__);                           \
       if constexpr (!(T == 2 && U == 16)) {                                              \
         if (r.bv == 8) I4S_ROWS_SG(FN, C, T, U, 8, __VA_ARGS__);                         \

@@ -73,6 +73,10 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
                     (size_t)((units + 7) / 8) * 4 * tile8 <= 160 * 1024;
   r.tpw = four ? 4 : (total_tiles >= 300 ? 2 : 1);
   r.u = ((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) || r.tpw == 4) ? 8 : 16;
+  // 1:4 in one-tile blocks at batch <= 8: 8-unit chunks, twice the waves
+  // (with the compact B fragments below; 4096x4096 1:4 at b4 / b8 4.74 /
+  // 5.15 -> 4.52 / 4.96 us; with per-lane fragments 4.87 / 5.42)
+  if (n_keep == 1 && r.tpw == 1 && batch <= 8) r.u = 8;
   if (want_u) r.u = want_u;
   // 8-unit chunks only with one chunk per wave (K <= 8192): two chunks per
   // wave of the 16-wave form would not fit its 128 registers
@@ -101,12 +105,12 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
   // the same area; only where the blocks fit the CUs once (on 13824x5120 at
   // b8 the two-tile 16-unit form spills at its 128-register cap: 12.4 ->
   // 12.7 us): 5120x5120 at b8 7.59 -> 6.96 us, 4096x4096 at b4 / b8 4.87 /
-  // 5.49 -> 4.58 / 4.95, 4096x11008 (G64) at b4 10.69 -> 9.53.  Not for 1:4,
-  // whose half-size weights left the activations' share of the traffic
-  // larger and still came out 1-2 % slower (4096x4096 1:4 at b4 / b8 4.75 /
-  // 5.15 -> 4.80 / 5.27).
+  // 5.49 -> 4.58 / 4.95, 4096x11008 (G64) at b4 10.69 -> 9.53.  1:4 only in
+  // one-tile blocks of 8-unit chunks: with 16-unit chunks it came out 1-2 %
+  // slower (4096x4096 1:4 at b4 / b8 4.75 / 5.15 -> 4.80 / 5.27).
   const int blocks = (total_tiles + r.tpw - 1) / r.tpw;
-  if (n_keep != 1 && batch <= 8 && r.tpw <= 2 && !(batch > 4 && r.tpw == 2 && r.u == 16)) {
+  const bool compact_ok = n_keep != 1 || (r.tpw == 1 && r.u == 8 && r.cpw == 1);
+  if (compact_ok && batch <= 8 && r.tpw <= 2 && !(batch > 4 && r.tpw == 2 && r.u == 16)) {
     const size_t lds4 = r.lds + (size_t)r.waves * kRowsBcBytes;
     const size_t cu = 160 * 1024;
     if (lds4 <= cu && (batch <= 4 ? (cu / lds4 == cu / r.lds || blocks <= 256) : blocks <= 256)) {
