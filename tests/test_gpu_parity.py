@@ -415,8 +415,11 @@ def test_batch_rows_match_single_calls(n_keep):
     """Row b of a batch call matches the batch-1 call on x_b (within the
     tolerance: batch 1, batch 2 and batch >= 3 run different kernels here),
     and a row does not depend on the other vectors of its batch: bit-identical
-    across every batch size that runs the same kernel (batch >= 3, with or
-    without a workspace: at this K the workspace path runs the same kernel)."""
+    across every batch size that runs the same kernel shape (batch 3-8 and
+    batch 9-16: this layer's one-tile blocks take 8-unit chunks up to 8
+    vectors and 16-unit chunks above, which groups the partial sums
+    differently; with or without a workspace: at this K the workspace path
+    runs the same kernel)."""
     rng = np.random.default_rng(78)
     rows, cols = 64, 2048
     w = rand16(rng, (rows, cols))
@@ -439,7 +442,10 @@ def test_batch_rows_match_single_calls(n_keep):
     for b in range(2):
         y_ref, a_ref = O.gemv(w_hat, x[b:b + 1])
         assert_gemv_close(y2[b][None], y_ref, a_ref, f"batch-2 row {b}")
-    for nb in range(3, 16):
+    plain8 = gpu_run(p, x[:8], use_workspace=False)
+    for nb in range(3, 8):
+        np.testing.assert_array_equal(gpu_run(p, x[:nb], use_workspace=False), plain8[:nb])
+    for nb in range(9, 16):
         np.testing.assert_array_equal(gpu_run(p, x[:nb], use_workspace=False), plain16[:nb])
     for nb in range(9, 16):
         np.testing.assert_array_equal(gpu_run(p, x[:nb]), y16[:nb])
