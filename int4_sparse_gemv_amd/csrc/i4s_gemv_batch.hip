@@ -608,10 +608,15 @@ __device__ __forceinline__ void rows_body(
     }
   };
   u32x4_t bq[2][8];   // BV = 16: the B fragments of blocks n and n + 1
-  u32x4_t bqc[2][NI];  // BV < 16: the compact loads of blocks n and n + 1
+  // BV < 16: the compact loads of blocks n and n + 1 (NBUF = 2), or of block
+  // n alone, reloaded as soon as it sits in LDS (NBUF = 1: eight vectors on
+  // two tiles of 16-unit chunks, whose two buffers would spill at the
+  // 128-register cap)
+  constexpr int NBUF = (BV == 8 && TPW == 2 && U == 16) ? 1 : 2;
+  u32x4_t bqc[NBUF][NI];
   if constexpr (kCompact) {
     load_bc(bqc[0], 0);
-    load_bc(bqc[1], 1);
+    if constexpr (NBUF == 2) load_bc(bqc[1], 1);
   } else {
     load_b(bq[0], 0);
     load_b(bq[1], 1);
@@ -708,10 +713,15 @@ __device__ __forceinline__ void rows_body(
 #pragma unroll
           for (int j = 0; j < NP; ++j) {
             if (n > 0 || j > 0) wave_lds_sync();
-            reinterpret_cast<u32x4_t *>(wbc)[lane] = bqc[n % 2][2 * j];
-            reinterpret_cast<u32x4_t *>(wbc)[64 + lane] = bqc[n % 2][2 * j + 1];
+            reinterpret_cast<u32x4_t *>(wbc)[lane] = bqc[n % NBUF][2 * j];
+            reinterpret_cast<u32x4_t *>(wbc)[64 + lane] = bqc[n % NBUF][2 * j + 1];
             wave_lds_sync();
             read_bc(bxl, j * (4 / NP));
+          }
+          if constexpr (NBUF == 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (n + 1 < NBK * CPW) load_bc(bqc[0], n + 1);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         u32x4_t (&bx)[8] = kCompact ? bxl : bq[n % 2];
@@ -791,8 +801,11 @@ __device__ __forceinline__ void rows_body(
         // the loads here, so only two buffers are ever live
         __builtin_amdgcn_sched_barrier(0);
         if (n + 2 < NBK * CPW) {
-          if constexpr (kCompact) load_bc(bqc[n % 2], n + 2);
-          else load_b(bx, n + 2);
+          if constexpr (kCompact) {
+            if constexpr (NBUF == 2) load_bc(bqc[n % 2], n + 2);
+          } else {
+            load_b(bx, n + 2);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1295,15 +1308,12 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
     if (sg_shift == 2) return FN<NK, C, 4, T, U, BV>(__VA_ARGS__);                       \
     return hipErrorNotSupported;                                                         \
   } while (0)
-// bv 4 and 8 (1:4 only in one-tile blocks of one 8-unit chunk; 8 not with
-// two tiles of 16-unit chunks, which would spill) or 16
+// bv 4 and 8 (1:4 only in one-tile blocks of one 8-unit chunk) or 16
 #define I4S_ROWS_BV(FN, C, T, U, ...)                                                    \
   do {                                                                                   \
     if constexpr (NK != 1 || (C == 1 && T == 1 && U == 8)) {                             \
       if (r.bv == 4) I4S_ROWS_SG(FN, C, T, U, 4, __VA_ARGS__);                           \
-      if constexpr (!(T == 2 && U == 16)) {                                              \
-        if (r.bv == 8) I4S_ROWS_SG(FN, C, T, U, 8, __VA_ARGS__);                         \
-      }                                                                                  \
+      if (r.bv == 8) I4S_ROWS_SG(FN, C, T, U, 8, __VA_ARGS__);                           \
     }                                                                                    \
     if (r.bv == 16) I4S_ROWS_SG(FN, C, T, U, 16, __VA_ARGS__);                           \
     return hipErrorNotSupported;                                                         \

@@ -103,18 +103,18 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
   // extra LDS would exceed the workgroup limit, nor where it would leave
   // fewer blocks per CU on a layer with more blocks than the 256 CUs.
   // Five to eight vectors: four loads per lane and block, two passes through
-  // the same area; only where the blocks fit the CUs once (on 13824x5120 at
-  // b8 the two-tile 16-unit form spills at its 128-register cap: 12.4 ->
-  // 12.7 us): 5120x5120 at b8 7.59 -> 6.96 us, 4096x4096 at b4 / b8 4.87 /
-  // 5.49 -> 4.58 / 4.95, 4096x11008 (G64) at b4 10.69 -> 9.53.  1:4 only in
+  // the same area (two tiles of 16-unit chunks keep one block's loads in
+  // flight instead of two, within their 128 registers): 5120x5120 at b8
+  // 7.59 -> 6.96 us, 13824x5120 at b8 12.4 -> 11.9, 4096x4096 at b4 / b8
+  // 4.87 / 5.49 -> 4.58 / 4.95, 4096x11008 (G64) at b4 10.69 -> 9.53.  1:4 only in
   // one-tile blocks of 8-unit chunks: with 16-unit chunks it came out 1-2 %
   // slower (4096x4096 1:4 at b4 / b8 4.75 / 5.15 -> 4.80 / 5.27).
   const int blocks = (total_tiles + r.tpw - 1) / r.tpw;
   const bool compact_ok = n_keep != 1 || (r.tpw == 1 && r.u == 8 && r.cpw == 1);
-  if (compact_ok && batch <= 8 && r.tpw <= 2 && !(batch > 4 && r.tpw == 2 && r.u == 16)) {
+  if (compact_ok && batch <= 8 && r.tpw <= 2) {
     const size_t lds4 = r.lds + (size_t)r.waves * kRowsBcBytes;
     const size_t cu = 160 * 1024;
-    if (lds4 <= cu && (batch <= 4 ? (cu / lds4 == cu / r.lds || blocks <= 256) : blocks <= 256)) {
+    if (lds4 <= cu && (cu / lds4 == cu / r.lds || blocks <= 256)) {
       r.bv = batch <= 4 ? 4 : 8;
       r.lds = lds4;
     }

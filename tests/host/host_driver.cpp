@@ -397,8 +397,8 @@ void test_rows_shapes() {
                               r.lds == base + (size_t)r.waves * i4s::kRowsBcBytes &&
                               ((160 * 1024) / r.lds == (160 * 1024) / base || (t + r.tpw - 1) / r.tpw <= 256)) ||
                              (r.bv == 8 && (nk != 1 || (r.tpw == 1 && r.u == 8 && r.cpw == 1)) && b > 4 && b <= 8 &&
-                              r.tpw <= 2 && !(r.tpw == 2 && r.u == 16) &&
-                              r.lds == base + (size_t)r.waves * i4s::kRowsBcBytes && (t + r.tpw - 1) / r.tpw <= 256);
+                              r.tpw <= 2 && r.lds == base + (size_t)r.waves * i4s::kRowsBcBytes &&
+                              ((160 * 1024) / r.lds == (160 * 1024) / base || (t + r.tpw - 1) / r.tpw <= 256));
           const bool ok = inst && bv_ok && r.waves >= 1 && r.waves * r.cpw >= chunks &&
                           (r.waves - 1) * r.cpw < chunks && r.waves <= maxw && r.lds > 0 && r.lds <= 160 * 1024;
           if (!ok && bad++ == 0)
