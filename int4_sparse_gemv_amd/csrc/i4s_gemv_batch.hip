@@ -1191,6 +1191,7 @@ __global__ __launch_bounds__(64 * kKWaves) void gemv_smfmac_slice_kernel(
 // -> 13.90 / 13.66 / 14.59 us per call for both launches, against blocks in
 // row-group order.)  The placement only affects speed: the blocks cover the
 // groups exactly once under any placement.
+template <int RL>
 __global__ __launch_bounds__(256) void gemv_slice_reduce_kernel(
     int rows, int batch, int ngrp, int tpg, int ksplit, const f4_t *__restrict__ partial,
     uint16_t *__restrict__ y) {
@@ -1208,14 +1209,19 @@ __global__ __launch_bounds__(256) void gemv_slice_reduce_kernel(
   const int lane = gid % 64, tile = (gid / 64) % tpg, rg = gid / (64 * tpg);
   const int li = lane % 16, lq = lane / 16;
   if (li >= batch) return;
+  // RL (8 or 16, at least the slice count up to 16) loads in flight: every
+  // slice of K <= 16384 in one round trip, summed in slice order.  (With the
+  // compiler free to interleave the sums, the loads past the eighth were
+  // issued only after the first had returned.)
   f4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = 0; k0 < ksplit; k0 += 8) {  // up to 8 loads in flight, summed in slice order
-    f4_t part[8];
+  for (int k0 = 0; k0 < ksplit; k0 += RL) {
+    f4_t part[RL];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < RL; ++k)
       part[k] = partial[slice_tile(min(k0 + k, ksplit - 1), ngrp, rg, tpg, tile) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first sum waits
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < RL; ++k)
       if (k0 + k < ksplit) sum += part[k];
   }
 #pragma unroll
@@ -1409,8 +1415,12 @@ hipError_t launch_slice_t(const i4s_packed &w, const uint16_t *x, int32_t batch,
   if (e != hipSuccess || pl.ksplit == 1) return e;
   const int tpg = kKWaves * TW;
   const unsigned threads = (unsigned)pl.row_groups * (unsigned)tpg * 64u;  // a multiple of 256
-  hipLaunchKernelGGL(gemv_slice_reduce_kernel, dim3(threads / 256), dim3(256), 0, stream, w.rows, batch,
-                     pl.row_groups, tpg, pl.ksplit, partial, y);
+  if (pl.ksplit <= 8)
+    hipLaunchKernelGGL(gemv_slice_reduce_kernel<8>, dim3(threads / 256), dim3(256), 0, stream, w.rows, batch,
+                       pl.row_groups, tpg, pl.ksplit, partial, y);
+  else
+    hipLaunchKernelGGL(gemv_slice_reduce_kernel<16>, dim3(threads / 256), dim3(256), 0, stream, w.rows, batch,
+                       pl.row_groups, tpg, pl.ksplit, partial, y);
   return hipGetLastError();
 }
 
