@@ -514,16 +514,17 @@ __device__ inline f4_t smfmac_step_14(uint32_t wd, uint32_t cb, uint32_t sh, con
 // time.
 // `blk` is the block's index within its layer: it covers the TPW 16-row
 // tiles from row 16 * TPW * blk.  lds is the block's dynamic LDS (per wave:
-// [TPW][RowsGeom<U>::kTileLds], then kRowsBcBytes when BV < 16).  Each B
+// [TPW][RowsGeom<U>::kTileLds], then kRowsBcBytes when BV > 0).  Each B
 // fragment a wave loads feeds the matrix steps of its TPW tiles (measured on
 // the 13824x5120 layer: the B-fragment loads from L2, not the weight stream,
 // bound the one-tile form; two tiles per wave take 14.8 -> 10.6 us at batch
 // 4 and 23.4 -> 14.6 us at batch 16).
-// BV = 4 or 8 (at most that many vectors): a wave reads each 4-unit block's
-// activations once, BV / 2 16-byte loads per lane, and spreads them to the
-// matrix layout through kRowsBcBytes of its LDS area (in BV / 4 passes);
-// BV = 16: every lane loads its own B fragment (at batch 4 three quarters of
-// those bytes repeat the last vector, and all of them share the CU's vector
+// BV = 4, 8 or 16 (at most that many vectors): a wave reads each 4-unit
+// block's activations once, BV / 2 16-byte loads per lane in whole 128-byte
+// rows, and spreads them to the matrix layout through kRowsBcBytes of its
+// LDS area (in BV / 4 passes); BV = 0: every lane loads its own B fragment,
+// 16 bytes from each of two half rows (at batch 4 three quarters of those
+// bytes repeat the last vector, and all of them share the CU's vector
 // memory path with the weight stream).
 template <int NK, int CPW, int SG, int TPW, int U, int BV>
 __device__ __forceinline__ void rows_body(
@@ -543,12 +544,12 @@ __device__ __forceinline__ void rows_body(
   typedef typename std::conditional<NK == 4, DenseVals,
                                     typename std::conditional<NK == 2, u32x4_t, u32x2_t>::type>::type vals_t;
   typedef typename std::conditional<NK == 2, u32x2_t, uint32_t>::type codes_t;
-  static_assert(BV == 4 || BV == 8 || BV == 16, "B fragments: compact (batch <= 4 or 8) or per lane");
-  constexpr bool kCompact = BV < 16;
+  static_assert(BV == 0 || BV == 4 || BV == 8 || BV == 16, "B fragments: compact (4, 8, 16 vectors) or per lane");
+  constexpr bool kCompact = BV > 0;
   constexpr int NI = kCompact ? BV / 2 : 1;  // compact loads per lane and 4-unit block
   constexpr int NP = kCompact ? BV / 4 : 1;  // passes through the LDS area per block
   constexpr int kWaveLds = TPW * Geo::kTileLds + (kCompact ? kRowsBcBytes : 0);
-  uint8_t *wl = lds + wave * kWaveLds;  // the wave's areas: one per tile, then the activations' (BV = 4)
+  uint8_t *wl = lds + wave * kWaveLds;  // the wave's areas: one per tile, then the activations' (BV > 0)
   uint8_t *wbc = wl + TPW * Geo::kTileLds;
   auto lv_of = [&](int t) { return reinterpret_cast<vals_t *>(wl + t * Geo::kTileLds); };  // [16 rows][ST]
   auto lc_of = [&](int t) { return reinterpret_cast<codes_t *>(wl + t * Geo::kTileLds + Geo::kValsBytes); };
@@ -577,21 +578,22 @@ __device__ __forceinline__ void rows_body(
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int k = 0; k < NL; ++k) wrow[t][k] = min(row0 + 16 * t + RL * k + lr, rows - 1);
-  // BV = 4 or 8: load i of lane L takes piece (L % 8) ^ g(v) of the 128-byte
+  // BV > 0: load i of lane L takes piece (L % 8) ^ g(v) of the 128-byte
   // activation row of pair P = 8i + L / 8 (vector v = P % BV, unit P / BV of
   // the block), so every 8 lanes read one whole row.  A pass through the
   // wave's 2 KB area writes two loads in lane order (16 pairs: four units of
-  // four vectors, or two units of eight) and reads them back: lane (vector
+  // four vectors, two of eight or one of sixteen) and reads them back: lane (vector
   // li, quarter lq) takes pieces lq and 4 + lq of vector min(li, BV - 1) for
   // each unit of the pass.  g(v) = 4 for vectors 2, 3 (6, 7) moves their
   // pieces to the other half of the 128 bytes, so the distinct 16-byte reads
   // of one LDS instruction fall in distinct banks (BV = 4) or at most two to
   // a bank (BV = 8).
+  constexpr int BVS = kCompact ? BV : 1;  // (the lambdas below are not called when BV = 0)
   auto swz = [](int v) { return 4 * ((v >> 1) & 1); };
   auto load_bc = [&](u32x4_t (&bc)[NI], int n) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int P = 8 * i + lane / 8, v = P % BV, s = P / BV;
+      const int P = 8 * i + lane / 8, v = P % BVS, s = P / BVS;
       const int q = (lane % 8) ^ swz(v);
       const int u = min(unit_of(n, s), units - 1);
       bc[i] = *reinterpret_cast<const u32x4_t *>(x + (int64_t)min(v, batch - 1) * cols + u * kSegCols + 8 * q);
@@ -599,20 +601,20 @@ __device__ __forceinline__ void rows_body(
   };
   // the B fragments of the pass's units (4 / NP of them, from unit s0) out of the area
   auto read_bc = [&](u32x4_t (&bx)[8], int s0) {
-    const int v = min(li, BV - 1), f = swz(v);
+    const int v = min(li, BVS - 1), f = swz(v);
 #pragma unroll
     for (int s = 0; s < 4 / NP; ++s) {
-      const u32x4_t *a = reinterpret_cast<const u32x4_t *>(wbc) + (s * BV + v) * 8;
+      const u32x4_t *a = reinterpret_cast<const u32x4_t *>(wbc) + (s * BVS + v) * 8;
       bx[2 * (s0 + s)] = a[lq ^ f];
       bx[2 * (s0 + s) + 1] = a[(4 + lq) ^ f];
     }
   };
-  u32x4_t bq[2][8];   // BV = 16: the B fragments of blocks n and n + 1
-  // BV < 16: the compact loads of blocks n and n + 1 (NBUF = 2), or of block
-  // n alone, reloaded as soon as it sits in LDS (NBUF = 1: eight vectors on
-  // two tiles of 16-unit chunks, whose two buffers would spill at the
-  // 128-register cap)
-  constexpr int NBUF = (BV == 8 && TPW == 2 && U == 16) ? 1 : 2;
+  u32x4_t bq[2][8];   // BV = 0: the B fragments of blocks n and n + 1
+  // BV > 0: the compact loads of blocks n and n + 1 (NBUF = 2), or of block
+  // n alone, reloaded as soon as it sits in LDS (NBUF = 1: sixteen vectors,
+  // and eight on two tiles of 16-unit chunks, whose two buffers would spill
+  // at the 128-register cap)
+  constexpr int NBUF = (BV == 16 || (BV == 8 && TPW == 2 && U == 16)) ? 1 : 2;
   u32x4_t bqc[NBUF][NI];
   if constexpr (kCompact) {
     load_bc(bqc[0], 0);
@@ -706,7 +708,7 @@ __device__ __forceinline__ void rows_body(
 #pragma unroll
       for (int bb = 0; bb < NBK; ++bb) {
         const int n = NBK * c + bb;
-        // BV < 16: block n's activations through the wave's area, NP passes
+        // BV > 0: block n's activations through the wave's area, NP passes
         // of two loads (each written once the previous pass's reads are done)
         u32x4_t bxl[8];
         if constexpr (kCompact) {
@@ -1314,14 +1316,18 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
     if (sg_shift == 2) return FN<NK, C, 4, T, U, BV>(__VA_ARGS__);                       \
     return hipErrorNotSupported;                                                         \
   } while (0)
-// bv 4 and 8 (1:4 only in one-tile blocks of one 8-unit chunk) or 16
+// bv 4 and 8 (1:4 only in one-tile blocks of one 8-unit chunk), 16 (one
+// tile per wave) or 0
 #define I4S_ROWS_BV(FN, C, T, U, ...)                                                    \
   do {                                                                                   \
     if constexpr (NK != 1 || (C == 1 && T == 1 && U == 8)) {                             \
       if (r.bv == 4) I4S_ROWS_SG(FN, C, T, U, 4, __VA_ARGS__);                           \
       if (r.bv == 8) I4S_ROWS_SG(FN, C, T, U, 8, __VA_ARGS__);                           \
     }                                                                                    \
-    if (r.bv == 16) I4S_ROWS_SG(FN, C, T, U, 16, __VA_ARGS__);                           \
+    if constexpr (T == 1) {                                                              \
+      if (r.bv == 16) I4S_ROWS_SG(FN, C, T, U, 16, __VA_ARGS__);                         \
+    }                                                                                    \
+    if (r.bv == 0) I4S_ROWS_SG(FN, C, T, U, 0, __VA_ARGS__);                             \
     return hipErrorNotSupported;                                                         \
   } while (0)
 #define I4S_ROWS_DISPATCH(FN, ...)                                                       \
@@ -1339,7 +1345,7 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
       if (r.tpw == 1) I4S_ROWS_BV(FN, 1, 1, 8, __VA_ARGS__);                            \
       if (r.tpw == 2) I4S_ROWS_BV(FN, 1, 2, 8, __VA_ARGS__);                            \
       if constexpr (NK != 4) {                                                           \
-        if (r.tpw == 4 && r.bv == 16) I4S_ROWS_SG(FN, 1, 4, 8, 16, __VA_ARGS__);       \
+        if (r.tpw == 4 && r.bv == 0) I4S_ROWS_SG(FN, 1, 4, 8, 0, __VA_ARGS__);         \
       }                                                                                  \
     }                                                                                    \
     return hipErrorNotSupported;                                                         \

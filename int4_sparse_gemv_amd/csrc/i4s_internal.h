@@ -147,24 +147,25 @@ struct RowsGeom {
   static constexpr int kMaxWaves = U == 8 ? 16 : 8;
 };
 
-// Rows kernel at batch <= 8: the activations of a 4-unit block pass through
-// this much of the wave's LDS area (4 vectors x 4 units x 128 bytes at once,
-// or 8 vectors x 2 units twice).
+// Rows kernel with compact B fragments: the activations of a 4-unit block
+// pass through this much of the wave's LDS area (4 vectors x 4 units x 128
+// bytes at once, 8 vectors x 2 units twice, or 16 vectors x 1 unit four
+// times).
 constexpr int kRowsBcBytes = 2048;
 
 // Launch shape of the rows kernel for one layer: chunk width u (8 or 16
 // units), chunks per wave cpw, waves per block, 16-row tiles per wave tpw,
-// how the B fragments are read (bv = 4 or 8: at most that many vectors, read
-// once and spread through the wave's LDS area; bv = 16: each lane reads its
-// own) and
+// how the B fragments are read (bv = 4, 8 or 16: at most that many vectors,
+// read once and spread through the wave's LDS area; bv = 0: each lane reads
+// its own) and
 // the block's dynamic LDS.  rows_shape only returns combinations that the
 // batch kernels instantiate: u 16 with (cpw, tpw) in {(1, 1), (1, 2), (2, 1),
 // (2, 2) but not dense, (4, 1)}; u 8 with cpw 1 and tpw in {1, 2, 4 but not
-// dense}; bv 4 or 8 only with tpw 1 or 2 (8 not with tpw 2 and u 16; for
-// 1:4 only with u 8, cpw 1 and tpw 1).  units must satisfy the rows kernel's
+// dense}; bv 4 or 8 only with tpw 1 or 2 (for 1:4 only with u 8, cpw 1 and
+// tpw 1), bv 16 only with tpw 1.  units must satisfy the rows kernel's
 // limit (K <= 32768).
 struct RowsShape {
-  int u = 0, cpw = 0, waves = 0, tpw = 0, bv = 16;
+  int u = 0, cpw = 0, waves = 0, tpw = 0, bv = 0;
   size_t lds = 0;
 };
 RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want_u = 0);

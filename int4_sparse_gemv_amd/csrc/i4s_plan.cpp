@@ -109,14 +109,21 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
   // 4.87 / 5.49 -> 4.58 / 4.95, 4096x11008 (G64) at b4 10.69 -> 9.53.  1:4 only in
   // one-tile blocks of 8-unit chunks: with 16-unit chunks it came out 1-2 %
   // slower (4096x4096 1:4 at b4 / b8 4.75 / 5.15 -> 4.80 / 5.27).
+  // Nine to sixteen vectors, one tile per wave: eight whole-row loads per
+  // lane and block, four passes, one block ahead; at b12 / b16 on 4096x4096
+  // 2:4 6.07 / 6.68 -> 5.53 / 5.54 us, dense 6.88 / 7.51 -> 6.61 / 6.64, 1:4
+  // 5.74 / 6.31 -> 5.79 / 5.81 (with per-lane fragments each lane reads 16
+  // bytes from each of two half rows).
   const int blocks = (total_tiles + r.tpw - 1) / r.tpw;
-  const bool compact_ok = n_keep != 1 || (r.tpw == 1 && r.u == 8 && r.cpw == 1);
-  if (compact_ok && batch <= 8 && r.tpw <= 2) {
-    const size_t lds4 = r.lds + (size_t)r.waves * kRowsBcBytes;
+  const int want = batch <= 4 ? 4 : (batch <= 8 ? 8 : 16);
+  const bool compact_ok = want == 16 ? r.tpw == 1
+                                     : (r.tpw <= 2 && (n_keep != 1 || (r.tpw == 1 && r.u == 8 && r.cpw == 1)));
+  if (compact_ok) {
+    const size_t ldsc = r.lds + (size_t)r.waves * kRowsBcBytes;
     const size_t cu = 160 * 1024;
-    if (lds4 <= cu && (cu / lds4 == cu / r.lds || blocks <= 256)) {
-      r.bv = batch <= 4 ? 4 : 8;
-      r.lds = lds4;
+    if (ldsc <= cu && (cu / ldsc == cu / r.lds || blocks <= 256)) {
+      r.bv = want;
+      r.lds = ldsc;
     }
   }
   return r;

@@ -365,10 +365,11 @@ void test_multi() {
 // (chunk width, chunks per wave, tiles per wave) triple is one of the
 // instantiated kernels, the waves cover the chunks exactly once, the block
 // fits the kernel's work-group limit, the LDS is what the kernel addresses
-// and fits 160 KB, and the compact B fragments are chosen only for 2:4 and
-// dense (1:4: one-tile blocks of one 8-unit chunk), at batch <= 4 (bv 4:
-// where they leave as many blocks per CU or the blocks fit the 256 CUs once)
-// and 5..8 (bv 8: where the blocks fit the CUs once).
+// and fits 160 KB, and the compact B fragments (bv 4 / 8 / 16 at batch <=
+// 4 / <= 8 / above) are chosen only in the shapes instantiated for them
+// (1:4 at batch <= 8 only in one-tile blocks of one 8-unit chunk, 16 only
+// with one tile per wave) and only where they leave as many blocks per CU
+// or the blocks fit the 256 CUs once.
 void test_rows_shapes() {
   const int tiles_set[] = {1, 2, 7, 16, 100, 159, 160, 161, 255, 256, 257, 299, 300, 301, 320,
                            511, 512, 513, 639, 640, 641, 700, 864, 1000, 2000, 5000};
@@ -391,13 +392,12 @@ void test_rows_shapes() {
                               : nk == 1 ? (r.u == 8 ? i4s::RowsGeom<8, 1>::kTileLds : i4s::RowsGeom<16, 1>::kTileLds)
                                         : (r.u == 8 ? i4s::RowsGeom<8>::kTileLds : i4s::RowsGeom<16>::kTileLds);
           const size_t base = (size_t)r.waves * r.tpw * tile;
-          const bool bv_ok = (r.bv == 16 && r.lds == base) ||
-                             (r.bv == 4 && (nk != 1 || (r.tpw == 1 && r.u == 8 && r.cpw == 1)) && b <= 4 &&
-                              r.tpw <= 2 &&
+          const bool compact_shape = r.bv == 16 ? (b > 8 && r.tpw == 1)
+                                   : (r.bv == 8 ? b > 4 && b <= 8 : b <= 4) && r.tpw <= 2 &&
+                                         (nk != 1 || (r.tpw == 1 && r.u == 8 && r.cpw == 1));
+          const bool bv_ok = (r.bv == 0 && r.lds == base) ||
+                             ((r.bv == 4 || r.bv == 8 || r.bv == 16) && compact_shape &&
                               r.lds == base + (size_t)r.waves * i4s::kRowsBcBytes &&
-                              ((160 * 1024) / r.lds == (160 * 1024) / base || (t + r.tpw - 1) / r.tpw <= 256)) ||
-                             (r.bv == 8 && (nk != 1 || (r.tpw == 1 && r.u == 8 && r.cpw == 1)) && b > 4 && b <= 8 &&
-                              r.tpw <= 2 && r.lds == base + (size_t)r.waves * i4s::kRowsBcBytes &&
                               ((160 * 1024) / r.lds == (160 * 1024) / base || (t + r.tpw - 1) / r.tpw <= 256));
           const bool ok = inst && bv_ok && r.waves >= 1 && r.waves * r.cpw >= chunks &&
                           (r.waves - 1) * r.cpw < chunks && r.waves <= maxw && r.lds > 0 && r.lds <= 160 * 1024;
