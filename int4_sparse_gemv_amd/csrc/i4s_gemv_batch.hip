@@ -1316,11 +1316,11 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
     if (sg_shift == 2) return FN<NK, C, 4, T, U, BV>(__VA_ARGS__);                       \
     return hipErrorNotSupported;                                                         \
   } while (0)
-// bv 4 and 8 (1:4 only in one-tile blocks of one 8-unit chunk), 16 (one
-// tile per wave) or 0
+// bv 4 and 8 (1:4 only with one 8-unit chunk per wave), 16 (one tile per
+// wave) or 0
 #define I4S_ROWS_BV(FN, C, T, U, ...)                                                    \
   do {                                                                                   \
-    if constexpr (NK != 1 || (C == 1 && T == 1 && U == 8)) {                             \
+    if constexpr (NK != 1 || (C == 1 && U == 8)) {                                       \
       if (r.bv == 4) I4S_ROWS_SG(FN, C, T, U, 4, __VA_ARGS__);                           \
       if (r.bv == 8) I4S_ROWS_SG(FN, C, T, U, 8, __VA_ARGS__);                           \
     }                                                                                    \

@@ -73,11 +73,13 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
                     (size_t)((units + 7) / 8) * 4 * tile8 <= 160 * 1024;
   r.tpw = four ? 4 : (total_tiles >= 300 ? 2 : 1);
   r.u = ((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) || r.tpw == 4) ? 8 : 16;
-  // One-tile blocks at batch <= 8: 8-unit chunks, twice the waves (with the
-  // compact B fragments below), cold us at b4 / b8: 4096x4096 1:4 4.74 /
-  // 5.15 -> 4.52 / 4.96 (per-lane fragments: 4.87 / 5.42), 2:4 4.58 / 4.96
-  // -> 4.45 / 4.89, dense 5.56 / 6.00 -> 5.49 / 5.67
-  if (r.tpw == 1 && batch <= 8) r.u = 8;
+  // One-tile blocks, and 1:4 in two-tile blocks, at batch <= 8: 8-unit
+  // chunks, twice the waves (with the compact B fragments below), cold us at
+  // b4 / b8: 4096x4096 1:4 4.74 / 5.15 -> 4.52 / 4.96 (per-lane fragments:
+  // 4.87 / 5.42), 2:4 4.58 / 4.96 -> 4.45 / 4.89, dense 5.56 / 6.00 -> 5.49 /
+  // 5.67; 11008x4096 1:4 10.07 / 10.90 -> 9.59 / 10.17 (per-lane fragments:
+  // 10.10 / 10.92)
+  if ((r.tpw == 1 || n_keep == 1) && r.tpw <= 2 && batch <= 8) r.u = 8;
   if (want_u) r.u = want_u;
   // 8-unit chunks only with one chunk per wave (K <= 8192): two chunks per
   // wave of the 16-wave form would not fit its 128 registers
@@ -106,8 +108,8 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
   // the same area (two tiles of 16-unit chunks keep one block's loads in
   // flight instead of two, within their 128 registers): 5120x5120 at b8
   // 7.59 -> 6.96 us, 13824x5120 at b8 12.4 -> 11.9, 4096x4096 at b4 / b8
-  // 4.87 / 5.49 -> 4.58 / 4.95, 4096x11008 (G64) at b4 10.69 -> 9.53.  1:4 only in
-  // one-tile blocks of 8-unit chunks: with 16-unit chunks it came out 1-2 %
+  // 4.87 / 5.49 -> 4.58 / 4.95, 4096x11008 (G64) at b4 10.69 -> 9.53.  1:4 only
+  // with one 8-unit chunk per wave: with 16-unit chunks it came out 1-2 %
   // slower (4096x4096 1:4 at b4 / b8 4.75 / 5.15 -> 4.80 / 5.27).
   // Nine to sixteen vectors, one tile per wave: eight whole-row loads per
   // lane and block, four passes, one block ahead; at b12 / b16 on 4096x4096
@@ -117,7 +119,7 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
   const int blocks = (total_tiles + r.tpw - 1) / r.tpw;
   const int want = batch <= 4 ? 4 : (batch <= 8 ? 8 : 16);
   const bool compact_ok = want == 16 ? r.tpw == 1
-                                     : (r.tpw <= 2 && (n_keep != 1 || (r.tpw == 1 && r.u == 8 && r.cpw == 1)));
+                                     : (r.tpw <= 2 && (n_keep != 1 || (r.u == 8 && r.cpw == 1)));
   if (compact_ok) {
     const size_t ldsc = r.lds + (size_t)r.waves * kRowsBcBytes;
     const size_t cu = 160 * 1024;

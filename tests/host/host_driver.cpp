@@ -367,8 +367,8 @@ void test_multi() {
 // fits the kernel's work-group limit, the LDS is what the kernel addresses
 // and fits 160 KB, and the compact B fragments (bv 4 / 8 / 16 at batch <=
 // 4 / <= 8 / above) are chosen only in the shapes instantiated for them
-// (1:4 at batch <= 8 only in one-tile blocks of one 8-unit chunk, 16 only
-// with one tile per wave) and only where they leave as many blocks per CU
+// (1:4 at batch <= 8 only with one 8-unit chunk per wave, 16 only with one
+// tile per wave) and only where they leave as many blocks per CU
 // or the blocks fit the 256 CUs once.
 void test_rows_shapes() {
   const int tiles_set[] = {1, 2, 7, 16, 100, 159, 160, 161, 255, 256, 257, 299, 300, 301, 320,
@@ -394,7 +394,7 @@ void test_rows_shapes() {
           const size_t base = (size_t)r.waves * r.tpw * tile;
           const bool compact_shape = r.bv == 16 ? (b > 8 && r.tpw == 1)
                                    : (r.bv == 8 ? b > 4 && b <= 8 : b <= 4) && r.tpw <= 2 &&
-                                         (nk != 1 || (r.tpw == 1 && r.u == 8 && r.cpw == 1));
+                                         (nk != 1 || (r.u == 8 && r.cpw == 1));
           const bool bv_ok = (r.bv == 0 && r.lds == base) ||
                              ((r.bv == 4 || r.bv == 8 || r.bv == 16) && compact_shape &&
                               r.lds == base + (size_t)r.waves * i4s::kRowsBcBytes &&
