@@ -73,13 +73,15 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
                     (size_t)((units + 7) / 8) * 4 * tile8 <= 160 * 1024;
   r.tpw = four ? 4 : (total_tiles >= 300 ? 2 : 1);
   r.u = ((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) || r.tpw == 4) ? 8 : 16;
-  // One-tile blocks, and 1:4 in two-tile blocks, at batch <= 8: 8-unit
-  // chunks, twice the waves (with the compact B fragments below), cold us at
-  // b4 / b8: 4096x4096 1:4 4.74 / 5.15 -> 4.52 / 4.96 (per-lane fragments:
-  // 4.87 / 5.42), 2:4 4.58 / 4.96 -> 4.45 / 4.89, dense 5.56 / 6.00 -> 5.49 /
-  // 5.67; 11008x4096 1:4 10.07 / 10.90 -> 9.59 / 10.17 (per-lane fragments:
-  // 10.10 / 10.92)
-  if ((r.tpw == 1 || n_keep == 1) && r.tpw <= 2 && batch <= 8) r.u = 8;
+  // One-tile blocks, 1:4 in two-tile blocks, and two-tile blocks of rows of
+  // at most 4096 columns, at batch <= 8: 8-unit chunks, twice the waves
+  // (with the compact B fragments below where they fit), cold us at b4 / b8:
+  // 4096x4096 1:4 4.74 / 5.15 -> 4.52 / 4.96 (per-lane fragments: 4.87 /
+  // 5.42), 2:4 4.58 / 4.96 -> 4.45 / 4.89, dense 5.56 / 6.00 -> 5.49 / 5.67;
+  // 11008x4096 1:4 10.07 / 10.90 -> 9.59 / 10.17 (per-lane fragments: 10.10
+  // / 10.92), 2:4 9.09 / 9.90 -> 8.77 / 9.48, dense 12.96 / 13.59 -> 11.53 /
+  // 13.05
+  if ((r.tpw == 1 || n_keep == 1 || units <= 64) && r.tpw <= 2 && batch <= 8) r.u = 8;
   if (want_u) r.u = want_u;
   // 8-unit chunks only with one chunk per wave (K <= 8192): two chunks per
   // wave of the 16-wave form would not fit its 128 registers
