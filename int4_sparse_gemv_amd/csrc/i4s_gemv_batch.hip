@@ -1317,7 +1317,7 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
     return hipErrorNotSupported;                                                         \
   } while (0)
 // bv 4 and 8 (1:4 only with one 8-unit chunk per wave), 16 (one tile per
-// wave) or 0
+// wave; four tiles of 2:4 below) or 0
 #define I4S_ROWS_BV(FN, C, T, U, ...)                                                    \
   do {                                                                                   \
     if constexpr (NK != 1 || (C == 1 && U == 8)) {                                       \
@@ -1344,6 +1344,9 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
     if (r.u == 8 && r.cpw == 1) {                                                        \
       if (r.tpw == 1) I4S_ROWS_BV(FN, 1, 1, 8, __VA_ARGS__);                            \
       if (r.tpw == 2) I4S_ROWS_BV(FN, 1, 2, 8, __VA_ARGS__);                            \
+      if constexpr (NK == 2) {                                                           \
+        if (r.tpw == 4 && r.bv == 16) I4S_ROWS_SG(FN, 1, 4, 8, 16, __VA_ARGS__);       \
+      }                                                                                  \
       if constexpr (NK != 4) {                                                           \
         if (r.tpw == 4 && r.bv == 0) I4S_ROWS_SG(FN, 1, 4, 8, 0, __VA_ARGS__);         \
       }                                                                                  \

@@ -117,10 +117,12 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
   // lane and block, four passes, one block ahead; at b12 / b16 on 4096x4096
   // 2:4 6.07 / 6.68 -> 5.53 / 5.54 us, dense 6.88 / 7.51 -> 6.61 / 6.64, 1:4
   // 5.74 / 6.31 -> 5.79 / 5.81 (with per-lane fragments each lane reads 16
-  // bytes from each of two half rows).
+  // bytes from each of two half rows).  The same on four-tile 2:4 blocks
+  // where the LDS fits: 11008x4096 at b12 / b16 11.59 / 12.17 -> 11.36 /
+  // 11.45; 1:4 there 12.36 / 12.83 -> 12.71 / 12.79, so not for 1:4.
   const int blocks = (total_tiles + r.tpw - 1) / r.tpw;
   const int want = batch <= 4 ? 4 : (batch <= 8 ? 8 : 16);
-  const bool compact_ok = want == 16 ? r.tpw == 1
+  const bool compact_ok = want == 16 ? (r.tpw == 1 || (r.tpw == 4 && n_keep == 2))
                                      : (r.tpw <= 2 && (n_keep != 1 || (r.u == 8 && r.cpw == 1)));
   if (compact_ok) {
     const size_t ldsc = r.lds + (size_t)r.waves * kRowsBcBytes;

@@ -368,7 +368,7 @@ void test_multi() {
 // and fits 160 KB, and the compact B fragments (bv 4 / 8 / 16 at batch <=
 // 4 / <= 8 / above) are chosen only in the shapes instantiated for them
 // (1:4 at batch <= 8 only with one 8-unit chunk per wave, 16 only with one
-// tile per wave) and only where they leave as many blocks per CU
+// tile per wave or four 2:4 tiles) and only where they leave as many blocks per CU
 // or the blocks fit the 256 CUs once.
 void test_rows_shapes() {
   const int tiles_set[] = {1, 2, 7, 16, 100, 159, 160, 161, 255, 256, 257, 299, 300, 301, 320,
@@ -386,13 +386,13 @@ void test_rows_shapes() {
               (r.u == 8 && r.cpw == 1 && (r.tpw == 1 || r.tpw == 2 || (r.tpw == 4 && nk != 4)));
           const int chunks = inst ? (units + r.u - 1) / r.u : 0;
           const int maxw = r.tpw == 4 ? 12 : (r.u == 8 ? 16 : 8);
-          // the LDS is the waves' tile areas plus, with compact B fragments
-          // (at most four vectors, one or two tiles), the activations' area
+          // the LDS is the waves' tile areas plus, with compact B fragments,
+          // the activations' area
           const size_t tile = nk == 4 ? (r.u == 8 ? i4s::RowsGeom<8, 4>::kTileLds : i4s::RowsGeom<16, 4>::kTileLds)
                               : nk == 1 ? (r.u == 8 ? i4s::RowsGeom<8, 1>::kTileLds : i4s::RowsGeom<16, 1>::kTileLds)
                                         : (r.u == 8 ? i4s::RowsGeom<8>::kTileLds : i4s::RowsGeom<16>::kTileLds);
           const size_t base = (size_t)r.waves * r.tpw * tile;
-          const bool compact_shape = r.bv == 16 ? (b > 8 && r.tpw == 1)
+          const bool compact_shape = r.bv == 16 ? (b > 8 && (r.tpw == 1 || (r.tpw == 4 && nk == 2)))
                                    : (r.bv == 8 ? b > 4 && b <= 8 : b <= 4) && r.tpw <= 2 &&
                                          (nk != 1 || (r.u == 8 && r.cpw == 1));
           const bool bv_ok = (r.bv == 0 && r.lds == base) ||
