@@ -1346,8 +1346,6 @@ hipError_t launch_rows_multi_t(int units, const uint16_t *x, int32_t batch, cons
       if (r.tpw == 2) I4S_ROWS_BV(FN, 1, 2, 8, __VA_ARGS__);                            \
       if constexpr (NK == 2) {                                                           \
         if (r.tpw == 4 && r.bv == 16) I4S_ROWS_SG(FN, 1, 4, 8, 16, __VA_ARGS__);       \
-      }                                                                                  \
-      if constexpr (NK != 4) {                                                           \
         if (r.tpw == 4 && r.bv == 0) I4S_ROWS_SG(FN, 1, 4, 8, 0, __VA_ARGS__);         \
       }                                                                                  \
     }                                                                                    \

@@ -160,8 +160,8 @@ constexpr int kRowsBcBytes = 2048;
 // its own) and
 // the block's dynamic LDS.  rows_shape only returns combinations that the
 // batch kernels instantiate: u 16 with (cpw, tpw) in {(1, 1), (1, 2), (2, 1),
-// (2, 2) but not dense, (4, 1)}; u 8 with cpw 1 and tpw in {1, 2, 4 but not
-// dense}; bv 4 or 8 only with tpw 1 or 2 (for 1:4 only with u 8 and cpw 1),
+// (2, 2) but not dense, (4, 1)}; u 8 with cpw 1 and tpw in {1, 2, 4 for 2:4
+// only}; bv 4 or 8 only with tpw 1 or 2 (for 1:4 only with u 8 and cpw 1),
 // bv 16 only with tpw 1, or tpw 4 for 2:4.  units must satisfy the rows kernel's
 // limit (K <= 32768).
 struct RowsShape {

@@ -67,9 +67,11 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
   // 13824x5120 15.4 -> 13.2, 11008x4096 12.0 -> 10.9; at b8 and below, and
   // with fewer than ~160 four-tile blocks, two tiles per wave are as fast or
   // faster (5120x5120 at b16: 9.1 against 12.0).  The block's LDS (waves x
-  // 4 x 3.7 KB) caps K at 5632.
-  const int tile8 = n_keep == 1 ? RowsGeom<8, 1>::kTileLds : RowsGeom<8>::kTileLds;
-  const bool four = n_keep != 4 && batch > 8 && total_tiles >= 640 && want_u != 16 &&
+  // 4 x 3.7 KB) caps K at 5632.  2:4 only: 1:4 on 11008x4096 at b12 / b16
+  // took 12.37 / 12.83 us on four tiles, 11.46 / 12.18 on two tiles of
+  // 16-unit chunks.
+  const int tile8 = RowsGeom<8>::kTileLds;
+  const bool four = n_keep == 2 && batch > 8 && total_tiles >= 640 && want_u != 16 &&
                     (size_t)((units + 7) / 8) * 4 * tile8 <= 160 * 1024;
   r.tpw = four ? 4 : (total_tiles >= 300 ? 2 : 1);
   r.u = ((r.tpw == 2 && total_tiles / 2 < 256 && batch <= 8) || r.tpw == 4) ? 8 : 16;
@@ -92,8 +94,8 @@ RowsShape rows_shape(int units, int total_tiles, int batch, int n_keep, int want
   // dense rows are twice the bytes: two chunks of two tiles would spill; four
   // chunks per wave (K > 16384) always take one tile per wave
   if ((n_keep == 4 && r.cpw == 2) || r.cpw == 4) r.tpw = 1;
-  // four tiles per wave: the 8-unit one-chunk form of 2:4 and 1:4 only (LDS)
-  if (r.tpw == 4 && (r.u != 8 || r.cpw != 1 || n_keep == 4)) r.tpw = 2;
+  // four tiles per wave: the 8-unit one-chunk form of 2:4 only (LDS)
+  if (r.tpw == 4 && (r.u != 8 || r.cpw != 1 || n_keep != 2)) r.tpw = 2;
   r.waves = (chunks + r.cpw - 1) / r.cpw;
   const int tile_lds = n_keep == 4 ? (r.u == 8 ? RowsGeom<8, 4>::kTileLds : RowsGeom<16, 4>::kTileLds)
                                     : (r.u == 8 ? RowsGeom<8>::kTileLds : RowsGeom<16>::kTileLds);

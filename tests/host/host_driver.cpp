@@ -383,7 +383,7 @@ void test_rows_shapes() {
           const bool inst =
               (r.u == 16 && ((r.cpw == 1 && (r.tpw == 1 || r.tpw == 2)) ||
                              (r.cpw == 2 && (r.tpw == 1 || (r.tpw == 2 && nk != 4))) || (r.cpw == 4 && r.tpw == 1))) ||
-              (r.u == 8 && r.cpw == 1 && (r.tpw == 1 || r.tpw == 2 || (r.tpw == 4 && nk != 4)));
+              (r.u == 8 && r.cpw == 1 && (r.tpw == 1 || r.tpw == 2 || (r.tpw == 4 && nk == 2)));
           const int chunks = inst ? (units + r.u - 1) / r.u : 0;
           const int maxw = r.tpw == 4 ? 12 : (r.u == 8 ? 16 : 8);
           // the LDS is the waves' tile areas plus, with compact B fragments,

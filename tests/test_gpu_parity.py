@@ -292,8 +292,9 @@ def test_config_pack_and_gemv(name, m):
     (4900, 2048, 4, 64), (40, 13824, 4, 128),
     # K > 16384 on the matrix cores: four chunks per wave
     (24, 20480, 4, 128), (17, 32768, 4, 64), (33, 32768, 1, 256),
-    # four tiles per wave at batch > 8 (>= 640 tiles, K <= 5632), ragged; at
-    # K = 4096 the 2:4 form also reads its B fragments compactly
+    # four tiles per wave at batch > 8 (2:4, >= 640 tiles, K <= 5632), ragged;
+    # at K = 4096 it also reads its B fragments compactly; 1:4 of that height
+    # takes two tiles of 16-unit chunks there
     (10241, 5632, 2, 256), (10241, 2048, 1, 64), (10241, 4096, 2, 128)])
 def test_gemv_shapes_and_all_batches(rows, cols, n_keep, g):
     rng = np.random.default_rng(rows + cols)
