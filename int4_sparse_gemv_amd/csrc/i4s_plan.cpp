@@ -41,10 +41,11 @@ SplitPlan split_plan(const i4s_packed &w, int32_t batch) {
   if (!split_wanted(w.rows, units, batch)) return pl;
   const int tiles = (w.rows + 15) / 16;
   pl.ksplit = (units + kKUnits - 1) / kKUnits;
-  // two tiles per wave where that still leaves >= I4S_SPLIT_TW2_MIN_BLOCKS
-  // blocks, else one
+  // two tiles per wave above batch 8 where that still leaves >=
+  // I4S_SPLIT_TW2_MIN_BLOCKS blocks, else one.  5120x13824, cold us, one /
+  // two tiles: b4 12.24 / 13.25, b8 12.60 / 12.99, b16 14.75 / 14.28.
   const int groups2 = (tiles + 2 * kKWaves - 1) / (2 * kKWaves);
-  pl.tw = (int64_t)pl.ksplit * groups2 >= I4S_SPLIT_TW2_MIN_BLOCKS ? 2 : 1;
+  pl.tw = batch > 8 && (int64_t)pl.ksplit * groups2 >= I4S_SPLIT_TW2_MIN_BLOCKS ? 2 : 1;
   pl.row_groups = (tiles + kKWaves * pl.tw - 1) / (kKWaves * pl.tw);
   if (pl.ksplit > 1)
     pl.partial_bytes = (size_t)pl.ksplit * pl.row_groups * kKWaves * pl.tw * kKPartialTileBytes;
